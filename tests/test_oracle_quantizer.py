@@ -1,0 +1,196 @@
+"""Pins for the oracle's codebook, quantiser, bit-pack and stage-1 round trip
+(CPU only).
+
+References other than the oracle itself: Max (1960)'s printed Gaussian
+Lloyd-Max table, numerical integration with scipy (for the optimality
+conditions, the distortion and the expected stage-1 MSE of a rotated unit
+vector), brute-force nearest-centroid search, hand-worked packed bytes and the
+row size printed on the pages (RotaryQuant §3.2 Step 4).
+"""
+
+import math
+
+import numpy as np
+import pytest
+from scipy import integrate
+from scipy.special import gammaln
+from scipy.stats import norm
+
+import oracle as O
+from compressed_space_attention_isoquant_amd import inputs
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lloyd_max_matches_max_1960(golden, bits):
+    g = golden("lloyd_max_gaussian_max1960.json")
+    c = O.lloyd_max_gaussian(bits)
+    n = 1 << bits
+    positive = c[n // 2:]
+    table = np.array(g["levels"][str(bits)])
+    # the table prints 4 significant digits
+    assert np.max(np.abs(positive - table) / np.maximum(1.0, table)) < 6e-4
+    # symmetric and strictly ascending
+    assert np.max(np.abs(c + c[::-1])) < 1e-14
+    assert np.all(np.diff(c) > 0)
+    if bits == 3:
+        t = O.thresholds(c)[n // 2 - 1:]
+        assert np.max(np.abs(t - np.array(g["thresholds"]["3"]))) < 6e-4
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lloyd_max_optimality_by_quadrature(golden, bits):
+    """Centroid condition and distortion checked by direct numerical
+    integration of the Gaussian density (independent of the oracle's closed
+    form)."""
+    g = golden("lloyd_max_gaussian_max1960.json")
+    c = O.lloyd_max_gaussian(bits)
+    t = np.concatenate(([-np.inf], O.thresholds(c), [np.inf]))
+    dist = 0.0
+    for k in range(len(c)):
+        a, b = t[k], t[k + 1]
+        mass = integrate.quad(norm.pdf, a, b, epsabs=1e-14, epsrel=1e-13)[0]
+        first = integrate.quad(lambda x: x * norm.pdf(x), a, b, epsabs=1e-14, epsrel=1e-13)[0]
+        assert abs(first / mass - c[k]) < 1e-9
+        dist += integrate.quad(lambda x: (x - c[k]) ** 2 * norm.pdf(x), a, b, epsabs=1e-14, epsrel=1e-13)[0]
+    assert abs(dist - g["distortion"][str(bits)]) / g["distortion"][str(bits)] < 2e-3
+
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_codebook_scaling(d):
+    for bits in (2, 3, 4):
+        c = O.codebook(bits, d)
+        assert c.dtype == np.float32
+        ref = O.lloyd_max_gaussian(bits) / math.sqrt(d)
+        assert np.max(np.abs(c.astype(np.float64) - ref) / np.abs(ref)) < 2 ** -24
+        # fp32 rounding keeps the codebook exactly symmetric: middle threshold 0
+        assert np.array_equal(c, -c[::-1])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_threshold_count_is_nearest_centroid(bits):
+    c = O.codebook(bits, 128)
+    vals = np.random.default_rng(bits).standard_normal(200000) * 0.2
+    t = O.thresholds(c)
+    codes = np.sum(vals[:, None] > t[None, :], axis=1)
+    brute = np.argmin(np.abs(vals[:, None] - c.astype(np.float64)[None, :]), axis=1)
+    assert np.array_equal(codes, brute)
+
+
+def test_pack_worked_examples(golden):
+    for case in golden("pack_worked_examples.json")["cases"]:
+        got = O.pack(np.array(case["codes"]), case["bits"]).tobytes().hex()
+        assert got == case["bytes_hex"], case
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_pack_round_trip_and_size(golden, bits, d):
+    g = golden("pages_closed_forms.json")
+    codes = np.random.default_rng(d * bits).integers(0, 1 << bits, size=(7, d))
+    rows = O.pack(codes, bits)
+    assert rows.shape == (7, d * bits // 8) and rows.dtype == np.uint8
+    assert np.array_equal(O.unpack(rows, bits, d), codes)
+    if (d, bits) == (128, 3):
+        assert rows.shape[-1] == O.row_bytes(d, bits) == g["packed_bytes_d128_b3"]["value"]
+        ratio = g["fp16_bytes_d128"]["value"] / g["packed_bytes_d128_b3"]["value"]
+        assert abs(ratio - g["compression_ratio"]["value"]) < 0.05
+
+
+def test_bit_flip_changes_one_code():
+    codes = np.random.default_rng(0).integers(0, 8, size=128)
+    rows = O.pack(codes, 3)
+    for bit in (0, 5, 200, 383):
+        r = rows.copy()
+        r[bit // 8] ^= 1 << (bit % 8)
+        diff = np.nonzero(O.unpack(r, 3, 128) != codes)[0]
+        assert list(diff) == [bit // 3]
+
+
+def test_zero_vector():
+    q = inputs.quaternions(1, 128)[0]
+    c = O.codebook(3, 128)
+    r = O.quantize(np.zeros((1, 128), np.float32), q, c, O.FULL)
+    assert np.all(r["codes"] == 3) and r["norm16"][0] == 0
+    x = O.dequantize(O.pack(r["codes"], 3), r["norm16"], q, c, 3, O.FULL, 128)
+    assert np.array_equal(x, np.zeros((1, 128)))
+
+
+def test_norm_is_fp16_round_to_nearest_even():
+    s = np.array([1.0, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 65504.0, 0.0, 23.4567])
+    bits, near = O.norm_fp16(s)
+    vals = bits.view(np.float16).astype(np.float64)
+    # 1 + 2^-11 is halfway between 1 and 1 + 2^-10: ties go to the even mantissa (1.0)
+    assert vals[1] == 1.0 and near[1]
+    assert vals[2] == 1.0 + 2 * 2 ** -10 and near[2]
+    assert vals[3] == 65504.0 and not near[0] and not near[5]
+    assert abs(vals[5] - 23.4567) <= 2 ** -7
+
+
+def quant_mse_closed_form(d, c):
+    """E ||x - x'||^2 for a unit vector x, any fixed orthogonal R: each rotated
+    coordinate has the sphere marginal f_d(u) ~ (1 - u^2)^((d-3)/2)."""
+    logk = gammaln(d / 2) - 0.5 * math.log(math.pi) - gammaln((d - 1) / 2)
+    f = lambda u: math.exp(logk + 0.5 * (d - 3) * math.log1p(-u * u))
+    c = c.astype(np.float64)
+    t = np.concatenate(([-1.0], O.thresholds(c), [1.0]))
+    total = 0.0
+    for k in range(len(c)):
+        total += integrate.quad(lambda u: (u - c[k]) ** 2 * f(u), t[k], t[k + 1],
+                                epsabs=1e-15, epsrel=1e-12, limit=200)[0]
+    return d * total
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("variant", [O.FULL, O.FAST])
+def test_stage1_mse_matches_closed_form(d, bits, variant):
+    n = 4096
+    q = inputs.quaternions(1, d)[0]
+    c = O.codebook(bits, d)
+    x = inputs.unit_vectors(n, d, np.float32, seed=100 + d + bits)
+    r = O.quantize(x, q, c, variant)
+    xr = O.dequantize(O.pack(r["codes"], bits), r["norm16"], q, c, bits, variant, d)
+    err = np.sum((x.astype(np.float64) - xr) ** 2, axis=-1)
+    expect = quant_mse_closed_form(d, c)
+    se = np.std(err) / math.sqrt(n)
+    assert abs(np.mean(err) - expect) < 4 * se, (np.mean(err), expect, se)
+
+
+def test_closed_form_mse_values():
+    """The integral itself against the values it should give (d=128): about
+    0.1160 / 0.03398 / 0.009325 for b = 2 / 3 / 4, close to the Gaussian D
+    of Max's table (the sphere marginal is nearly Gaussian at d = 128)."""
+    vals = [quant_mse_closed_form(128, O.codebook(b, 128)) for b in (2, 3, 4)]
+    assert abs(vals[0] - 0.11601) < 2e-4
+    assert abs(vals[1] - 0.033979) < 1e-4
+    assert abs(vals[2] - 0.009325) < 3e-5
+
+
+def test_dequantize_is_scaled_inverse_rotation():
+    d, bits = 128, 3
+    q = inputs.quaternions(1, d)[0]
+    c = O.codebook(bits, d)
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((32, d)) * 7).astype(np.float16)
+    r = O.quantize(x, q, c, O.FULL)
+    xr = O.dequantize(O.pack(r["codes"], bits), r["norm16"], q, c, bits, O.FULL, d)
+    s16 = r["norm16"].view(np.float16).astype(np.float64)
+    # x' = s16 R^T c[codes]; check R x' / s16 is exactly the centroid vector
+    back = O.rotate(xr / s16[:, None], q, O.FULL)
+    assert np.max(np.abs(back - c.astype(np.float64)[r["codes"]])) < 1e-12
+    # no renormalisation: ||x'|| = s16 ||c[codes]||
+    assert np.allclose(np.linalg.norm(xr, axis=-1),
+                       s16 * np.linalg.norm(c.astype(np.float64)[r["codes"]], axis=-1), rtol=1e-12)
+
+
+def test_boundary_flags():
+    d, bits = 128, 3
+    q = inputs.quaternions(1, d)[0]
+    c = O.codebook(bits, d)
+    x = inputs.unit_vectors(2000, d, np.float32, seed=5)
+    r = O.quantize(x, q, c, O.FULL)
+    t = O.thresholds(c)
+    margin = np.min(np.abs(r["rotated"][..., None] - t), axis=-1)
+    assert np.array_equal(r["flags"], margin < O.BOUNDARY_BAND)
+    # about 2 * 1e-6 * density * (2^b - 1) per element: rare
+    assert r["flags"].mean() < 1e-3

@@ -1,0 +1,229 @@
+"""Pins for the oracle's rotation R = R_SO(4) o H_d (CPU only).
+
+Each check compares the oracle with something other than itself: the explicit
+Sylvester matrix, scipy's Hadamard routine, the quaternion multiplication
+table, textbook left/right multiplication matrices, group identities, and the
+operation counts printed on the pages (RotaryQuant §3.2, IsoQuant abstract).
+"""
+
+import math
+
+import numpy as np
+import pytest
+from scipy.linalg import hadamard
+
+import oracle as O
+from compressed_space_attention_isoquant_amd import inputs
+
+DIMS = [4, 8, 16, 32, 64, 128, 256, 512]
+
+
+def sylvester(d):
+    """Explicit normalised Hadamard matrix, entry (-1)^popcount(i & j) / sqrt(d)."""
+    H = np.empty((d, d))
+    for i in range(d):
+        for j in range(d):
+            H[i, j] = -1.0 if bin(i & j).count("1") % 2 else 1.0
+    return H / math.sqrt(d)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_wht_equals_explicit_matrix(d):
+    H = sylvester(d)
+    # columns of wht(I) are H e_j; H is symmetric
+    assert np.max(np.abs(O.wht(np.eye(d)) - H)) < 1e-13
+    assert np.max(np.abs(H - hadamard(d) / math.sqrt(d))) == 0.0
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_wht_orthogonal_and_involution(d):
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((16, d))
+    y = O.wht(x)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13, atol=0)
+    assert np.max(np.abs(O.wht(y) - x)) < 1e-12
+    e0 = np.zeros(d)
+    e0[0] = 1.0
+    assert np.max(np.abs(O.wht(e0) - 1.0 / math.sqrt(d))) < 1e-15
+
+
+def test_wht_op_count_matches_pages(golden):
+    g = golden("pages_closed_forms.json")
+    x = np.random.default_rng(0).standard_normal(128)
+    q = inputs.quaternions(1, 128)[0]
+    _, counts = O.rotate_scalar(x, q, O.FULL)
+    assert counts["wht_addsub"] == g["wht_ops_d128"]["value"] == 128 * 7
+
+
+# ---------------------------------------------------------------------------
+# Quaternions and SO(4)
+# ---------------------------------------------------------------------------
+
+ONE = np.array([1.0, 0, 0, 0])
+I = np.array([0, 1.0, 0, 0])
+J = np.array([0, 0, 1.0, 0])
+K = np.array([0, 0, 0, 1.0])
+
+
+def test_hamilton_multiplication_table():
+    # i^2 = j^2 = k^2 = ijk = -1, ij = k, jk = i, ki = j, ji = -k
+    for u in (I, J, K):
+        assert np.array_equal(O.qmul(u, u), -ONE)
+    assert np.array_equal(O.qmul(O.qmul(I, J), K), -ONE)
+    assert np.array_equal(O.qmul(I, J), K)
+    assert np.array_equal(O.qmul(J, K), I)
+    assert np.array_equal(O.qmul(K, I), J)
+    assert np.array_equal(O.qmul(J, I), -K)
+    assert np.array_equal(O.qmul(ONE, J), J)
+
+
+def test_quaternion_norm_is_multiplicative():
+    rng = np.random.default_rng(3)
+    p = rng.standard_normal((100, 4))
+    q = rng.standard_normal((100, 4))
+    lhs = np.linalg.norm(O.qmul(p, q), axis=-1)
+    rhs = np.linalg.norm(p, axis=-1) * np.linalg.norm(q, axis=-1)
+    assert np.allclose(lhs, rhs, rtol=1e-13)
+
+
+def left_matrix(q):
+    """Textbook matrix of v -> q v."""
+    a, b, c, d = q
+    return np.array([[a, -b, -c, -d], [b, a, -d, c], [c, d, a, -b], [d, -c, b, a]])
+
+
+def right_matrix(p):
+    """Textbook matrix of v -> v p."""
+    a, b, c, d = p
+    return np.array([[a, -b, -c, -d], [b, a, d, -c], [c, -d, a, b], [d, c, -b, a]])
+
+
+def block_matrix(quats, variant):
+    """4x4 matrix of the oracle's forward map on one block, from basis images."""
+    return np.stack([O.so4_forward(e, quats, variant) for e in np.eye(4)], axis=1)
+
+
+def random_pairs(n, seed):
+    g = np.random.default_rng(seed).standard_normal((n, 2, 4))
+    return g / np.linalg.norm(g, axis=-1, keepdims=True)
+
+
+def test_so4_matches_matrix_form_and_is_special_orthogonal():
+    for qp in random_pairs(50, 11):
+        qL, qR = qp
+        M = block_matrix(qp[None], O.FULL)
+        ref = left_matrix(qL) @ right_matrix(O.qconj(qR))
+        assert np.max(np.abs(M - ref)) < 1e-14
+        assert np.max(np.abs(M.T @ M - np.eye(4))) < 1e-12
+        assert abs(np.linalg.det(M) - 1.0) < 1e-12
+        # left and right multiplications commute
+        assert np.max(np.abs(left_matrix(qL) @ right_matrix(qR) - right_matrix(qR) @ left_matrix(qL))) < 1e-14
+        # trace of q_L v conj(q_R) is 4 Re(q_L) Re(q_R)
+        assert abs(np.trace(M) - 4 * qL[0] * qR[0]) < 1e-12
+        Mf = block_matrix(qp[None], O.FAST)
+        assert np.max(np.abs(Mf - left_matrix(qL))) < 1e-14
+        assert abs(np.linalg.det(Mf) - 1.0) < 1e-12
+
+
+def test_fast_is_isoclinic():
+    # <v, q v> = Re(q) |v|^2 for every v: every plane turns by the same angle
+    rng = np.random.default_rng(5)
+    for qp in random_pairs(20, 12):
+        v = rng.standard_normal((10, 4))
+        w = O.so4_forward(v, qp[None], O.FAST)
+        assert np.allclose(np.sum(v * w, axis=-1), qp[0][0] * np.sum(v * v, axis=-1), rtol=1e-12, atol=1e-14)
+
+
+def test_single_quaternion_conjugation_fixes_real_axis():
+    # RotaryQuant Appendix B: v -> q v conj(q) keeps Re(v) and rotates Im(v)
+    rng = np.random.default_rng(6)
+    for qp in random_pairs(20, 13):
+        same = np.stack([qp[0], qp[0]])[None]
+        v = rng.standard_normal(4)
+        w = O.so4_forward(v, same, O.FULL)
+        assert abs(w[0] - v[0]) < 1e-13
+        assert abs(np.linalg.norm(w[1:]) - np.linalg.norm(v[1:])) < 1e-13
+        M = block_matrix(same, O.FULL)
+        assert np.max(np.abs(M[0] - np.array([1.0, 0, 0, 0]))) < 1e-13
+
+
+def test_identity_quaternions_and_known_rotation():
+    ident = np.zeros((1, 2, 4))
+    ident[0, :, 0] = 1.0
+    v = np.random.default_rng(7).standard_normal(4)
+    for variant in (O.FULL, O.FAST):
+        assert np.max(np.abs(O.so4_forward(v, ident, variant) - v)) < 1e-15
+    th = 0.3
+    rot = np.zeros((1, 2, 4))
+    rot[0, 0] = [math.cos(th), math.sin(th), 0, 0]
+    rot[0, 1] = [1, 0, 0, 0]
+    # left multiplication by cos + i sin turns the (1, i) and (j, k) planes by th
+    assert np.allclose(O.so4_forward(ONE, rot, O.FAST), [math.cos(th), math.sin(th), 0, 0], atol=1e-15)
+    assert np.allclose(O.so4_forward(J, rot, O.FAST), [0, 0, math.cos(th), math.sin(th)], atol=1e-15)
+
+
+@pytest.mark.parametrize("variant", [O.FULL, O.FAST])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_rotation_inverse_and_inner_products(variant, d):
+    q = inputs.quaternions(1, d)[0]
+    rng = np.random.default_rng(d + variant)
+    x = rng.standard_normal((64, d))
+    y = rng.standard_normal((64, d))
+    rx = O.rotate(x, q, variant)
+    ry = O.rotate(y, q, variant)
+    assert np.max(np.abs(O.rotate_inverse(rx, q, variant) - x)) < 1e-12
+    assert np.max(np.abs(O.so4_inverse(O.so4_forward(x, q, variant), q, variant) - x)) < 1e-12
+    # RotaryQuant Appendix A: <Rq, Rk> = <q, k>
+    assert np.allclose(np.sum(rx * ry, axis=-1), np.sum(x * y, axis=-1), rtol=0, atol=1e-12 * d)
+    assert np.allclose(np.linalg.norm(rx, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+
+
+def test_rotation_as_explicit_dense_matrix():
+    """R equals the product of the block-diagonal 4x4 matrices and the explicit
+    Hadamard matrix, built without the oracle's butterfly."""
+    d = 32
+    q = inputs.quaternions(1, d, seed=9)[0].astype(np.float64)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    B = np.zeros((d, d))
+    for i in range(d // 4):
+        B[4 * i:4 * i + 4, 4 * i:4 * i + 4] = left_matrix(q[i, 0]) @ right_matrix(O.qconj(q[i, 1]))
+    R = B @ sylvester(d)
+    x = np.random.default_rng(1).standard_normal((8, d))
+    assert np.max(np.abs(O.rotate(x, q, O.FULL) - x @ R.T)) < 1e-13
+    assert np.max(np.abs(O.rotate_inverse(x, q, O.FULL) - x @ R)) < 1e-13
+
+
+@pytest.mark.parametrize("d,full,fast", [(128, 1024, 512), (256, 2048, 1024), (512, 4096, 2048)])
+def test_so4_multiply_counts(golden, d, full, fast):
+    g = golden("pages_closed_forms.json")
+    q = inputs.quaternions(1, d)[0]
+    x = np.random.default_rng(d).standard_normal(d)
+    yf, cf = O.rotate_scalar(x, q, O.FULL)
+    ys, cs = O.rotate_scalar(x, q, O.FAST)
+    assert cf["so4_mul"] == full and cs["so4_mul"] == fast
+    assert cf["wht_addsub"] == d * int(math.log2(d))
+    assert np.max(np.abs(yf - O.rotate(x, q, O.FULL))) < 1e-13
+    assert np.max(np.abs(ys - O.rotate(x, q, O.FAST))) < 1e-13
+    if d == 128:
+        assert cf["so4_mul"] == g["so4_full_mul_d128"]["value"]
+        assert cs["so4_mul"] == g["so4_fast_mul_d128"]["value"]
+        # P1's 1,408 = WHT 896 + 16 per block (a 4x4 matrix per block)
+        assert cf["wht_addsub"] + 16 * (d // 4) == g["combined_ops_d128"]["value"]
+        assert g["dense_ops_d128"]["value"] == d * d
+
+
+def test_post_wht_coordinate_variance():
+    # RotaryQuant §3.2: each coordinate of H x^ has variance 1/d (statistical)
+    d = 128
+    x = inputs.unit_vectors(20000, d, np.float64, seed=21)
+    y = O.wht(x)
+    assert abs(np.mean(y * y) * d - 1.0) < 1e-12       # exact: orthogonal, unit vectors
+    var = np.var(y, axis=0)
+    assert np.max(np.abs(var * d - 1.0)) < 0.1           # every coordinate near 1/d
+
+
+def test_stored_parameter_count(golden):
+    g = golden("pages_closed_forms.json")
+    q = inputs.quaternions(1, 128)[0]
+    assert q.size == g["stored_quaternion_floats_d128"]["value"]
+    assert (128 // 4) * 6 == g["dof_d128"]["value"]
