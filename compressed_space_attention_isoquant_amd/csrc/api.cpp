@@ -1,0 +1,261 @@
+// extern "C" entry points of libiq.so: argument validation, per-call tables,
+// launch geometry and kernel dispatch.  See include/iq.h for the contract.
+#include "iq.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "iq_internal.h"
+
+namespace {
+
+using iq::Tables;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_config(const iq_config *cfg) {
+  if (!cfg || !cfg->quats || !cfg->centroids) return IQ_ERR_INVALID_ARG;
+  if (cfg->head_dim != 128 && cfg->head_dim != 256 && cfg->head_dim != 512) return IQ_ERR_UNSUPPORTED;
+  if (cfg->bits < 2 || cfg->bits > 4) return IQ_ERR_UNSUPPORTED;
+  if (cfg->variant != IQ_FULL && cfg->variant != IQ_FAST) return IQ_ERR_INVALID_ARG;
+  if (cfg->num_kv_heads < 1) return IQ_ERR_INVALID_ARG;
+  if (!aligned16(cfg->quats)) return IQ_ERR_MISALIGNED;
+  const int n = 1 << cfg->bits;
+  for (int k = 0; k < n; ++k) {
+    if (!std::isfinite(cfg->centroids[k])) return IQ_ERR_INVALID_ARG;
+    if (k > 0 && !(cfg->centroids[k] > cfg->centroids[k - 1])) return IQ_ERR_INVALID_ARG;
+  }
+  return IQ_OK;
+}
+
+int check_cache(const iq_cache *c) {
+  if (!c || !c->codes || !c->norms) return IQ_ERR_INVALID_ARG;
+  if (c->capacity < 1) return IQ_ERR_INVALID_ARG;
+  if (!aligned16(c->codes) || !aligned16(c->norms)) return IQ_ERR_MISALIGNED;
+  return IQ_OK;
+}
+
+bool valid_dtype(int32_t t) { return t == IQ_F32 || t == IQ_F16; }
+
+Tables make_tables(const iq_config *cfg) {
+  Tables t;
+  std::memset(&t, 0, sizeof(t));
+  const int n = 1 << cfg->bits;
+  for (int k = 0; k < n; ++k) t.cent[k] = cfg->centroids[k];
+  // midpoint of neighbouring centroids, evaluated in double and rounded once
+  for (int k = 0; k + 1 < n; ++k)
+    t.thr[k] = static_cast<float>(0.5 * (static_cast<double>(cfg->centroids[k]) +
+                                         static_cast<double>(cfg->centroids[k + 1])));
+  return t;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_HIP; }
+
+// Split-K geometry of the decode kernels: enough workgroups to cover the
+// 256 compute units several times, each holding a whole number of
+// (waves x tile) token blocks.
+struct Geometry {
+  int chunk;
+  int n_split;
+};
+
+Geometry decode_geometry(int32_t batch, int32_t hkv, int64_t max_kv_len) {
+  const int64_t unit = (int64_t)iq::kDecodeWaves * iq::kDecodeTile;
+  const int64_t T = max_kv_len > 0 ? max_kv_len : 1;
+  const int64_t pairs = (int64_t)batch * hkv;
+  const int64_t target_groups = 2048;
+  int64_t want = (target_groups + pairs - 1) / pairs;
+  if (want < 1) want = 1;
+  int64_t chunk = (T + want - 1) / want;
+  chunk = (chunk + unit - 1) / unit * unit;
+  Geometry g;
+  g.chunk = (int)chunk;
+  g.n_split = (int)((T + chunk - 1) / chunk);
+  return g;
+}
+
+// Lloyd iteration for the minimum-MSE quantiser of N(0,1): thresholds are the
+// midpoints of neighbouring levels; levels are the conditional means of their
+// cells, (phi(a) - phi(b)) / P(a < X <= b).
+double std_normal_pdf(double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) * 0.39894228040143267794; }
+
+double cell_mass(double a, double b) {
+  const double r2 = 0.70710678118654752440;
+  if (a >= 0.0) {
+    const double qa = 0.5 * std::erfc(a * r2);
+    const double qb = std::isinf(b) ? 0.0 : 0.5 * std::erfc(b * r2);
+    return qa - qb;
+  }
+  const double pb = std::isinf(b) ? 1.0 : 0.5 * std::erfc(-b * r2);
+  const double pa = std::isinf(a) ? 0.0 : 0.5 * std::erfc(-a * r2);
+  return pb - pa;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *iq_status_string(int status) {
+  switch (status) {
+    case IQ_OK: return "ok";
+    case IQ_ERR_INVALID_ARG: return "invalid argument";
+    case IQ_ERR_UNSUPPORTED: return "unsupported head_dim, bits, group size or dtype";
+    case IQ_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case IQ_ERR_WORKSPACE: return "workspace too small";
+    case IQ_ERR_HIP: return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out) {
+  if (!centroids_out) return IQ_ERR_INVALID_ARG;
+  if (bits < 1 || bits > 4) return IQ_ERR_UNSUPPORTED;
+  if (head_dim < 1) return IQ_ERR_UNSUPPORTED;
+  const int n = 1 << bits;
+  double c[16], t[17];
+  for (int k = 0; k < n; ++k) c[k] = -2.0 + 4.0 * k / (n - 1);
+  for (int it = 0; it < 200000; ++it) {
+    t[0] = -INFINITY;
+    t[n] = INFINITY;
+    for (int k = 1; k < n; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+    double moved = 0.0;
+    for (int k = 0; k < n; ++k) {
+      const double next = (std_normal_pdf(t[k]) - std_normal_pdf(t[k + 1])) / cell_mass(t[k], t[k + 1]);
+      moved = std::fmax(moved, std::fabs(next - c[k]));
+      c[k] = next;
+    }
+    if (moved < 1e-15) break;
+  }
+  const double s = 1.0 / std::sqrt(static_cast<double>(head_dim));
+  for (int k = 0; k < n; ++k) centroids_out[k] = static_cast<float>(c[k] * s);
+  return IQ_OK;
+}
+
+int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch,
+                       int32_t n_new, const int32_t *start_pos, const iq_cache *out,
+                       hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != IQ_OK) return st;
+  if (!x || !start_pos) return IQ_ERR_INVALID_ARG;
+  if (!valid_dtype(x_dtype)) return IQ_ERR_UNSUPPORTED;
+  if (batch < 1 || n_new < 1) return IQ_ERR_INVALID_ARG;
+  st = check_cache(out);
+  if (st != IQ_OK) return st;
+  if (n_new > out->capacity) return IQ_ERR_INVALID_ARG;
+  if (!aligned16(x)) return IQ_ERR_MISALIGNED;
+  iq::QuantArgs a;
+  a.x = x;
+  a.quats = cfg->quats;
+  a.start_pos = start_pos;
+  a.codes = out->codes;
+  a.norms = out->norms;
+  a.capacity = out->capacity;
+  a.batch = batch;
+  a.n = n_new;
+  a.hkv = cfg->num_kv_heads;
+  a.tab = make_tables(cfg);
+  return hip_status(iq::launch_quantize(cfg->head_dim, cfg->bits, cfg->variant, x_dtype == IQ_F16, a, stream));
+}
+
+int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch, const int32_t *start_pos,
+                  int32_t n, void *out, int32_t out_dtype, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != IQ_OK) return st;
+  st = check_cache(in);
+  if (st != IQ_OK) return st;
+  if (!out || !start_pos) return IQ_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
+  if (batch < 1 || n < 1 || n > in->capacity) return IQ_ERR_INVALID_ARG;
+  if (!aligned16(out)) return IQ_ERR_MISALIGNED;
+  iq::DequantArgs a;
+  a.codes = in->codes;
+  a.norms = in->norms;
+  a.quats = cfg->quats;
+  a.start_pos = start_pos;
+  a.out = out;
+  a.capacity = in->capacity;
+  a.batch = batch;
+  a.n = n;
+  a.hkv = cfg->num_kv_heads;
+  a.tab = make_tables(cfg);
+  return hip_status(iq::launch_dequantize(cfg->head_dim, cfg->bits, cfg->variant, out_dtype == IQ_F16, a, stream));
+}
+
+size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
+                                 int64_t max_kv_len) {
+  if (check_config(cfg) != IQ_OK) return 0;
+  if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return 0;
+  if (num_q_heads % cfg->num_kv_heads) return 0;
+  const Geometry g = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
+  return (size_t)batch * num_q_heads * g.n_split * iq::kDecodeWaves * (cfg->head_dim + iq::kRecHeader) *
+         sizeof(float);
+}
+
+int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
+                        int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
+                        const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out,
+                        int32_t out_dtype, float *lse_out, int32_t *argmax_out, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != IQ_OK) return st;
+  if (!q || !kv_len || !out || !workspace) return IQ_ERR_INVALID_ARG;
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
+  if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return IQ_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return IQ_ERR_INVALID_ARG;
+  if (num_q_heads % cfg->num_kv_heads) return IQ_ERR_INVALID_ARG;
+  const int group = num_q_heads / cfg->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return IQ_ERR_UNSUPPORTED;
+  st = check_cache(k);
+  if (st != IQ_OK) return st;
+  st = check_cache(v);
+  if (st != IQ_OK) return st;
+  if (max_kv_len > k->capacity || max_kv_len > v->capacity) return IQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return IQ_ERR_MISALIGNED;
+  if ((lse_out && !aligned16(lse_out)) || (argmax_out && !aligned16(argmax_out))) return IQ_ERR_MISALIGNED;
+  const size_t need = iq_decode_workspace_bytes(cfg, batch, num_q_heads, max_kv_len);
+  if (workspace_bytes < need) return IQ_ERR_WORKSPACE;
+
+  const Geometry geo = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
+  const Tables tab = make_tables(cfg);
+  iq::DecodeArgs a;
+  a.q = q;
+  a.q_f16 = q_dtype == IQ_F16;
+  a.kc = k->codes;
+  a.kn = k->norms;
+  a.vc = v->codes;
+  a.vn = v->norms;
+  a.kcap = k->capacity;
+  a.vcap = v->capacity;
+  a.kv_len = kv_len;
+  a.quats = cfg->quats;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = cfg->num_kv_heads;
+  a.group = group;
+  a.variant = cfg->variant;
+  a.chunk = geo.chunk;
+  a.n_split = geo.n_split;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  a.ws = static_cast<float *>(workspace);
+  a.tab = tab;
+  st = hip_status(iq::launch_decode(cfg->head_dim, cfg->bits, a, stream));
+  if (st != IQ_OK) return st;
+
+  iq::MergeArgs m;
+  m.ws = a.ws;
+  m.kv_len = kv_len;
+  m.quats = cfg->quats;
+  m.out = out;
+  m.out_f16 = out_dtype == IQ_F16;
+  m.lse = lse_out;
+  m.argmax = argmax_out;
+  m.batch = batch;
+  m.hq = num_q_heads;
+  m.group = group;
+  m.n_part = geo.n_split * iq::kDecodeWaves;
+  m.tab = tab;
+  return hip_status(iq::launch_merge(cfg->head_dim, cfg->variant, m, stream));
+}
+
+}  // extern "C"

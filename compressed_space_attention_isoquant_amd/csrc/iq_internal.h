@@ -1,0 +1,88 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+// Not installed; the public interface is include/iq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iq {
+
+constexpr int kMaxLevels = 16;  // 2^4 centroids at most
+
+// Per-call quantiser tables, passed to kernels by value (kernel arguments).
+struct Tables {
+  float cent[kMaxLevels];  // ascending centroids (fp32, as given by the caller)
+  float thr[kMaxLevels];   // thr[k] = (cent[k] + cent[k+1]) / 2, k < 2^b - 1
+};
+
+struct QuantArgs {
+  const void *x;           // [batch][n][H_kv][d]
+  const float *quats;      // [H_kv][d/4][2][4]
+  const int32_t *start_pos;
+  uint8_t *codes;          // [batch][H_kv][cap][row]
+  uint16_t *norms;         // [batch][H_kv][cap]
+  long long capacity;
+  int batch, n, hkv;
+  Tables tab;
+};
+
+struct DequantArgs {
+  const uint8_t *codes;
+  const uint16_t *norms;
+  const float *quats;
+  const int32_t *start_pos;
+  void *out;               // [batch][n][H_kv][d]
+  long long capacity;
+  int batch, n, hkv;
+  Tables tab;
+};
+
+// Split-K decode.  Each wave of the attention kernel produces one partial
+// softmax state (m, l, argmax, o~[d]) per query head of its KV group; the
+// merge kernel combines the partials of a (sequence, query head) and applies
+// the inverse rotation.
+constexpr int kDecodeWaves = 4;            // waves per attention workgroup
+constexpr int kDecodeTile = 64;            // tokens per wave iteration
+constexpr int kRecHeader = 4;              // m, l, argmax (int bits), pad
+
+struct DecodeArgs {
+  const void *q;           // [batch][Hq][d]
+  int q_f16;
+  const uint8_t *kc;
+  const uint16_t *kn;
+  const uint8_t *vc;
+  const uint16_t *vn;
+  long long kcap, vcap;
+  const int32_t *kv_len;
+  const float *quats;
+  int batch, hq, hkv, group;
+  int variant;
+  int chunk;               // tokens per workgroup (multiple of kDecodeWaves * kDecodeTile)
+  int n_split;             // workgroups per (sequence, KV head)
+  float qscale;            // softmax_scale * log2(e)
+  float *ws;               // partial records [batch][Hq][n_split * kDecodeWaves][d + kRecHeader]
+  Tables tab;
+};
+
+struct MergeArgs {
+  const float *ws;
+  const int32_t *kv_len;
+  const float *quats;
+  void *out;               // [batch][Hq][d]
+  int out_f16;
+  float *lse;              // nullable
+  int32_t *argmax;         // nullable
+  int batch, hq, group;
+  int n_part;              // partial records per (sequence, query head)
+  Tables tab;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_quantize(int d, int bits, int variant, int in_f16, const QuantArgs &a,
+                           hipStream_t s);
+hipError_t launch_dequantize(int d, int bits, int variant, int out_f16, const DequantArgs &a,
+                             hipStream_t s);
+hipError_t launch_decode(int d, int bits, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_merge(int d, int variant, const MergeArgs &a, hipStream_t s);
+
+}  // namespace iq

@@ -1,0 +1,157 @@
+/*
+ * iq.h -- C ABI of the MI355X (gfx950) IsoQuant packed-KV library (libiq.so).
+ *
+ * What is computed (the operations are defined on the pages of
+ * "RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via Fused
+ * Compressed-Space Attention", arXiv 2608.08081, and "IsoQuant:
+ * Hardware-Aligned SO(4) Isoclinic Rotations for LLM KV Cache Compression",
+ * arXiv 2603.28430):
+ *
+ *   quantize (RotaryQuant §3.2, Algorithm 1 and eq. (2)):
+ *     s = ||x||_2, x^ = x / s, x~ = R_SO(4)(H_d x^), codes = LloydMax(x~),
+ *     row = BitPack_b(codes), norm = fp16(s).
+ *     R_SO(4) acts on contiguous 4-element blocks seen as quaternions:
+ *     Full: v -> q_L v conj(q_R); Fast: v -> q_L v (IsoQuant abstract).
+ *   dequantize (RotaryQuant §3.4: R^-1 = R^T via the same butterfly and the
+ *     block transpose): x' = fp16(s) * H_d R_SO(4)^T c[codes].
+ *   decode attention (RotaryQuant §3.4 Table 2 and Appendix A): q~ = R q once
+ *     per query head, scores and an online softmax on the packed K rows in
+ *     rotated space, value accumulation on the packed V rows in rotated space,
+ *     one R^T on the aggregated output.  No fp16/fp32 K or V is written.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is DEVICE memory owned by the caller unless marked HOST.
+ *     The library never allocates device memory and keeps no mutable global
+ *     state; calls on different streams may run concurrently.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without host synchronisation.
+ *   - Arguments are validated before anything is enqueued; a negative
+ *     iq_status is returned and nothing runs.  Launch failures return
+ *     IQ_ERR_HIP.  Values that live in device memory (start_pos, kv_len) cannot
+ *     be checked without a synchronisation: keeping every row index inside
+ *     [0, capacity) is the caller's precondition.  NaN/Inf inputs and norms
+ *     above 65504 (fp16 overflow of the stored scale) are outside the contract.
+ *   - No C++ exception crosses this interface.
+ *
+ * Data layout
+ *   head vectors x      [batch][n][H_kv][d]              fp32 or fp16
+ *   quaternions         [H_kv][d/4][2][4] fp32, (w,x,y,z), q_L then q_R, unit
+ *                       length; one rotation per KV head shared by K, V and the
+ *                       query heads of that group (RotaryQuant Appendix A).
+ *   packed codes        [batch][H_kv][capacity][d*b/8]   uint8
+ *                       LSB-first bitstream: bit r of code i is bit (b*i + r)
+ *                       of the row, bytes little-endian (d*b/8 = 48 bytes at
+ *                       d = 128, b = 3, RotaryQuant §3.2 Step 4).
+ *   norms               [batch][H_kv][capacity]          IEEE fp16 bits
+ *   queries / outputs   [batch][Hq][d]                   fp32 or fp16
+ *   code of a value v:  number of thresholds t_k = (c_k + c_{k+1})/2 with
+ *                       v > t_k (ascending centroids c).
+ */
+#ifndef IQ_H
+#define IQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IQ_OK = 0,
+  IQ_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum value */
+  IQ_ERR_UNSUPPORTED = -2, /* d, b, group size or dtype outside the built set */
+  IQ_ERR_MISALIGNED = -3,  /* a base pointer is not 16-byte aligned */
+  IQ_ERR_WORKSPACE = -4,   /* workspace smaller than iq_decode_workspace_bytes */
+  IQ_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
+} iq_status;
+
+typedef enum { IQ_FULL = 0, IQ_FAST = 1 } iq_variant;
+typedef enum { IQ_F32 = 0, IQ_F16 = 1 } iq_dtype;
+
+/* Per-layer quantiser configuration (a HOST struct). */
+typedef struct {
+  int32_t head_dim;        /* d: 128, 256 or 512 */
+  int32_t bits;            /* b: 2, 3 or 4 */
+  int32_t variant;         /* iq_variant; Fast reads q_L only */
+  int32_t num_kv_heads;    /* H_kv >= 1 */
+  const float *quats;      /* DEVICE [H_kv][d/4][2][4] fp32 unit quaternions */
+  const float *centroids;  /* HOST [2^b] fp32, strictly ascending, finite */
+} iq_config;
+
+/* One packed tensor (K or V) of a KV cache (a HOST struct). */
+typedef struct {
+  uint8_t *codes;          /* DEVICE [batch][H_kv][capacity][d*b/8], 16-B aligned */
+  uint16_t *norms;         /* DEVICE [batch][H_kv][capacity] fp16 bits, 16-B aligned */
+  int64_t capacity;        /* rows per (sequence, KV head), >= 1 */
+} iq_cache;
+
+/* Lloyd-Max codebook for the coordinates of a rotated unit vector, taken as
+ * N(0, 1/d) (RotaryQuant §3.2 Step 3: minimum expected distortion under the
+ * post-rotation marginal).  Runs the Lloyd iteration for N(0,1) in double on
+ * the host, scales by 1/sqrt(d) and rounds to fp32.
+ *   centroids_out: HOST array of 2^bits floats, written in ascending order.
+ * Returns IQ_OK, IQ_ERR_INVALID_ARG (null) or IQ_ERR_UNSUPPORTED (bits, d). */
+int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out);
+
+/* Quantize and append (RotaryQuant Algorithm 1; appends as in §3.4 "deferred
+ * prefill" and Appendix D: each new K or V vector is compressed on arrival).
+ *   x:         [batch][n_new][H_kv][d] of x_dtype (IQ_F32 or IQ_F16).
+ *   start_pos: DEVICE int32 [batch]; vector t of sequence b is written to row
+ *              start_pos[b] + t of `out`.  The library does not advance it.
+ *   out:       the packed tensor written (codes and norms).
+ * K and V are two calls on two caches that share one iq_config. */
+int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype,
+                       int32_t batch, int32_t n_new, const int32_t *start_pos,
+                       const iq_cache *out, hipStream_t stream);
+
+/* Dequantize n rows per (sequence, KV head) starting at start_pos[b]
+ * (the stage-1 return path of the IsoQuant abstract; inverse of RotaryQuant
+ * eq. (2) as in §3.4):  out[b][t][h][:] = fp16(s) * R^T c[codes].
+ *   start_pos: DEVICE int32 [batch].
+ *   out:       [batch][n][H_kv][d] of out_dtype. */
+int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch,
+                  const int32_t *start_pos, int32_t n, void *out,
+                  int32_t out_dtype, hipStream_t stream);
+
+/* Bytes of workspace iq_decode_attention needs for these sizes.  Returns 0 if
+ * the arguments are invalid.  O(batch * Hq * splits * d) floats: never
+ * O(T * d) -- the decode path writes no dequantized K or V. */
+size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch,
+                                 int32_t num_q_heads, int64_t max_kv_len);
+
+/* Decode attention on packed K/V (RotaryQuant §3.4 Table 2, Appendix A).
+ * One query token per sequence; query head h reads KV head h / (Hq / H_kv).
+ *   q:          [batch][Hq][d] of q_dtype.
+ *   k, v:       packed caches written by iq_quantize_append with this cfg.
+ *   kv_len:     DEVICE int32 [batch]; attends rows [0, kv_len[b]) (includes a
+ *               token appended this step).  kv_len[b] = 0 gives out = 0,
+ *               lse = -inf, argmax = -1.
+ *   max_kv_len: HOST upper bound of kv_len, used for the grid only.
+ *   softmax_scale: multiplies q.k (1/sqrt(d) in Appendix A).
+ *   out:        [batch][Hq][d] of out_dtype, in the original (un-rotated)
+ *               domain.
+ *   lse_out:    nullable, [batch][Hq] fp32 natural-log sum of exp(scores).
+ *   argmax_out: nullable, [batch][Hq] int32 position of the largest score
+ *               (ties: lowest position).
+ *   workspace:  at least iq_decode_workspace_bytes(...) bytes, 16-B aligned;
+ *               its content on entry does not matter. */
+int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype,
+                        int32_t batch, int32_t num_q_heads,
+                        const iq_cache *k, const iq_cache *v,
+                        const int32_t *kv_len, int64_t max_kv_len,
+                        float softmax_scale, void *out, int32_t out_dtype,
+                        float *lse_out, int32_t *argmax_out,
+                        void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *iq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQ_H */

@@ -1,0 +1,157 @@
+"""The C-ABI library loads, exports every symbol include/iq.h declares, and
+validates arguments on the host before anything is enqueued (CPU only: no
+compute is launched here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from compressed_space_attention_isoquant_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "iq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(iq_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"iq_quantize_append", "iq_dequantize", "iq_decode_attention",
+                          "iq_decode_workspace_bytes", "iq_status_string", "iq_codebook"}
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert B.iq_status_string(s)
+    assert B.iq_status_string(123) == "unknown status"
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_library_codebook_equals_oracle(bits, d):
+    # independent implementations of the Lloyd iteration reach the same
+    # fixed point and the same fp32 rounding
+    assert np.array_equal(B.iq_codebook(bits, d), O.codebook(bits, d))
+
+
+def test_codebook_errors():
+    L = B.lib()
+    assert L.iq_codebook(3, 128, None) == -1
+    buf = (ctypes.c_float * 64)()
+    assert L.iq_codebook(5, 128, buf) == -2
+    assert L.iq_codebook(0, 128, buf) == -2
+
+
+class FakeTensor:
+    """Stand-in carrying only a device address: every call below must fail in
+    host validation, before any HIP call."""
+
+    def __init__(self, addr, shape=(1, 1, 1, 1), dtype="float32"):
+        self.addr = addr
+        self.shape = shape
+        import torch
+        self.dtype = getattr(torch, dtype)
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return int(np.prod(self.shape))
+
+    def element_size(self):
+        return 1
+
+
+def cfg(d=128, bits=3, variant=0, hkv=4, quats=0x1000, centroids=None):
+    c = B.Config(d, bits, variant, hkv, FakeTensor(quats),
+                 O.codebook(bits, d) if centroids is None else centroids)
+    return c
+
+
+def call_quant(c, x=0x2000, xdt=0, batch=1, n=1, sp=0x3000, codes=0x4000, norms=0x5000, cap=8):
+    L = B.lib()
+    cc = c.c()
+    cache = B.IQCacheC(codes, norms, cap)
+    return L.iq_quantize_append(ctypes.byref(cc), x, xdt, batch, n, sp, ctypes.byref(cache), None)
+
+
+def test_quantize_validation():
+    assert call_quant(cfg(d=96)) == -2
+    assert call_quant(cfg(bits=5)) == -2
+    assert call_quant(cfg(variant=2)) == -1
+    assert call_quant(cfg(hkv=0)) == -1
+    assert call_quant(cfg(quats=0x1004)) == -3
+    assert call_quant(cfg(), x=0) == -1
+    assert call_quant(cfg(), x=0x2008) == -3
+    assert call_quant(cfg(), xdt=7) == -2
+    assert call_quant(cfg(), batch=0) == -1
+    assert call_quant(cfg(), n=9, cap=8) == -1
+    assert call_quant(cfg(), sp=0) == -1
+    assert call_quant(cfg(), codes=0) == -1
+    assert call_quant(cfg(), norms=0x5002) == -3
+    assert call_quant(cfg(), cap=0) == -1
+    bad = O.codebook(3, 128).copy()
+    bad[3], bad[4] = bad[4], bad[3]
+    assert call_quant(cfg(centroids=bad)) == -1
+    nan = O.codebook(3, 128).copy()
+    nan[0] = np.nan
+    assert call_quant(cfg(centroids=nan)) == -1
+
+
+def call_decode(c, hq=32, batch=1, max_len=16, cap=16, ws_bytes=None, q=0x2000, out=0x6000,
+                ws=0x7000, lse=None, arg=None, qdt=1, odt=0, kv=0x8000, scale=0.088):
+    L = B.lib()
+    cc = c.c()
+    k = B.IQCacheC(0x4000, 0x5000, cap)
+    v = B.IQCacheC(0x4000, 0x5000, cap)
+    if ws_bytes is None:
+        ws_bytes = L.iq_decode_workspace_bytes(ctypes.byref(cc), batch, hq, max_len)
+    return L.iq_decode_attention(ctypes.byref(cc), q, qdt, batch, hq, ctypes.byref(k), ctypes.byref(v),
+                                 kv, max_len, scale, out, odt, lse, arg, ws, ws_bytes, None)
+
+
+def test_decode_validation():
+    L = B.lib()
+    c = cfg()
+    cc = c.c()
+    need = L.iq_decode_workspace_bytes(ctypes.byref(cc), 1, 32, 16)
+    assert need > 0
+    # workspace is O(splits x d) per query head, never O(T x d)
+    big = L.iq_decode_workspace_bytes(ctypes.byref(cc), 64, 32, 32768)
+    assert big < 64 * 4 * 32768 * 128 * 2 // 16
+    assert L.iq_decode_workspace_bytes(ctypes.byref(cc), 1, 30, 16) == 0
+    assert call_decode(c, hq=30) == -1                      # Hq % H_kv != 0
+    assert call_decode(c, hq=64) == -2                      # group 16 not built
+    assert call_decode(c, ws_bytes=need - 1) == -4
+    assert call_decode(c, max_len=17, cap=16) == -1
+    assert call_decode(c, q=0x2004) == -3
+    assert call_decode(c, lse=0x9004) == -3
+    assert call_decode(c, qdt=3) == -2
+    assert call_decode(c, kv=0) == -1
+    assert call_decode(c, scale=float("inf")) == -1
+    assert call_decode(c, batch=0) == -1
+    assert call_decode(cfg(d=64)) == -2
+
+
+def test_dequantize_validation():
+    L = B.lib()
+    c = cfg()
+    cc = c.c()
+    cache = B.IQCacheC(0x4000, 0x5000, 8)
+    assert L.iq_dequantize(ctypes.byref(cc), ctypes.byref(cache), 1, 0x3000, 9, 0x6000, 0, None) == -1
+    assert L.iq_dequantize(ctypes.byref(cc), ctypes.byref(cache), 1, 0x3000, 4, 0x6002, 0, None) == -3
+    assert L.iq_dequantize(ctypes.byref(cc), ctypes.byref(cache), 1, 0x3000, 4, 0x6000, 9, None) == -2
+    assert L.iq_dequantize(ctypes.byref(cc), None, 1, 0x3000, 4, 0x6000, 0, None) == -1

@@ -1,0 +1,158 @@
+"""GPU parity of the stage-1 path (quantize -> dequantize) against the oracle.
+
+Bars (from the method's tolerance statement): packed codes bit-exact except
+elements within 1e-6 of a decision threshold (counted and reported); fp16
+norms bit-exact except norms within 1e-6 of an fp16 rounding midpoint;
+dequantized vectors within max-abs 1e-5 (fp32 output) or 2e-3 (fp16 output)
+of the oracle's dequantization of its own codes and norms (inside the bands,
+where both neighbours are correct, with the GPU's validated choice).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from compressed_space_attention_isoquant_amd import binding as B
+from compressed_space_attention_isoquant_amd import inputs
+from tests.gpu_helpers import (DEV, host_cache, make_config, quantize_rows, reconcile_codes,
+                               reconcile_norms, say, torch)
+from tests.test_oracle_quantizer import quant_mse_closed_form
+
+pytestmark = pytest.mark.gpu
+
+TOL = {np.float32: 1e-5, np.float16: 2e-3}
+SETTINGS = [(v, d, b, dt) for v in (O.FULL, O.FAST) for d in (128, 256, 512) for b in (2, 3, 4)
+            for dt in (np.float16, np.float32)]
+
+
+def dequantize_gpu(cfg, cache, batch, n, hkv, d, out_dtype, start=0):
+    t = torch()
+    out = t.empty((batch, n, hkv, d), dtype=t.float16 if out_dtype == np.float16 else t.float32, device=DEV)
+    sp = t.full((batch,), start, dtype=t.int32, device=DEV)
+    B.iq_dequantize(cfg, cache, sp, n, out)
+    t.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def check_stage1(x, variant, d, bits, out_dtype, label):
+    """x: (n, d) host vectors, one head.  Full element-by-element comparison."""
+    n = x.shape[0]
+    cfg, quats = make_config(d, bits, variant, 1)
+    cache = quantize_rows(cfg, x[None, :, None, :])
+    codes, norms = host_cache(cache)
+    ref = O.quantize(x, quats[0], O.codebook(bits, d), variant)
+    rc, nf, nfm = reconcile_codes(codes[0, 0], ref["codes"], ref["flags"], bits, d)
+    rn, nnf, nnm = reconcile_norms(norms[0, 0], ref["norm16"], ref["norm_flags"])
+    got = dequantize_gpu(cfg, cache, 1, n, 1, d, out_dtype)[0, :, 0]
+    # the oracle dequantizes its own codes (boundary-band ties as the GPU chose)
+    want = O.dequantize_codes(rc, rn, quats[0], O.codebook(bits, d), variant)
+    err = float(np.max(np.abs(got - want)))
+    say(f"{label}: n={n} flagged={nf} flagged_mismatch={nfm} norm_flagged={nnf} "
+        f"norm_mismatch={nnm} dequant_maxabs={err:.3g}")
+    assert err <= TOL[out_dtype], err
+    return codes, norms, got
+
+
+def test_c1_full_d128_b3_fp32():
+    """4,096 unit vectors, d = 128, fp32, 3-bit, Full, quaternions from seed 0."""
+    d, bits = 128, 3
+    x = inputs.unit_vectors(4096, d, np.float32, seed=1)
+    codes, norms, xr = check_stage1(x, O.FULL, d, bits, np.float32, "C1")
+    err = np.sum((x.astype(np.float64) - xr) ** 2, axis=-1)
+    expect = quant_mse_closed_form(d, O.codebook(bits, d))
+    se = np.std(err) / math.sqrt(len(err))
+    say(f"C1 MSE={np.mean(err):.6f} closed-form={expect:.6f} (+-4se {4 * se:.2g})")
+    assert abs(np.mean(err) - expect) < 4 * se
+
+
+@pytest.mark.parametrize("variant,d,bits,dt", SETTINGS)
+def test_stage1_settings_ragged(variant, d, bits, dt):
+    # a count that is not a multiple of the per-workgroup vector count
+    x = inputs.unit_vectors(1037, d, dt, seed=7 + d + bits)
+    check_stage1(x, variant, d, bits, dt, f"ragged v={variant} d={d} b={bits} {np.dtype(dt).name}")
+
+
+def test_edge_vectors():
+    d, bits = 128, 3
+    x = np.zeros((5, d), np.float32)
+    x[1, 7] = 1.0                                  # a basis vector
+    x[2] = 1e-20                                   # tiny
+    x[3] = np.linspace(-3, 3, d)                   # large, non-unit
+    x[4, :] = 0.5                                  # constant (WHT concentrates it)
+    check_stage1(x, O.FULL, d, bits, np.float32, "edge")
+    one = inputs.unit_vectors(1, 256, np.float16, seed=3)
+    check_stage1(one, O.FAST, 256, 2, np.float16, "single")
+
+
+def test_append_offsets_batches_and_heads():
+    """batch 3, 4 KV heads, rows appended at different start positions."""
+    t = torch()
+    d, bits, hkv, batch, n, cap = 256, 3, 4, 3, 40, 100
+    cfg, quats = make_config(d, bits, O.FAST, hkv)
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((batch, n, hkv, d)) * 5).astype(np.float16)
+    starts = np.array([0, 17, 60], np.int32)
+    cache = B.new_cache(batch, hkv, cap, d, bits, DEV)
+    B.iq_quantize_append(cfg, t.from_numpy(x).to(DEV), t.from_numpy(starts).to(DEV), cache)
+    codes, norms = host_cache(cache)
+    cb = O.codebook(bits, d)
+    own = {}
+    for b in range(batch):
+        for h in range(hkv):
+            ref = O.quantize(x[b, :, h], quats[h], cb, O.FAST)
+            rows = codes[b, h, starts[b]:starts[b] + n]
+            rc, _, _ = reconcile_codes(rows, ref["codes"], ref["flags"], bits, d)
+            rn, _, _ = reconcile_norms(norms[b, h, starts[b]:starts[b] + n], ref["norm16"], ref["norm_flags"])
+            own[b, h] = (rc, rn)
+            # rows outside the appended range stay untouched (zero)
+            untouched = np.ones(cap, bool)
+            untouched[starts[b]:starts[b] + n] = False
+            assert not codes[b, h, untouched].any() and not norms[b, h, untouched].any()
+    out = t.empty((batch, n, hkv, d), dtype=t.float32, device=DEV)
+    B.iq_dequantize(cfg, cache, t.from_numpy(starts).to(DEV), n, out)
+    got = out.cpu().numpy()
+    for b in range(batch):
+        for h in range(hkv):
+            want = O.dequantize_codes(own[b, h][0], own[b, h][1], quats[h], cb, O.FAST)
+            assert np.max(np.abs(got[b, :, h] - want)) <= 1e-5 * max(1.0, np.max(np.abs(want)))
+
+
+@pytest.mark.parametrize("idx,setting", list(enumerate(SETTINGS)))
+def test_c2_full_size_sampled(idx, setting):
+    """2^20 unit vectors per setting quantized and dequantized on the GPU; the
+    oracle checks 2,048 sampled vectors (the last ones included) element by
+    element, and the mean reconstruction error over all 2^20 vectors matches
+    the closed form."""
+    t = torch()
+    variant, d, bits, dt = setting
+    n = 1 << 20
+    tdt = t.float16 if dt == np.float16 else t.float32
+    cfg, quats = make_config(d, bits, variant, 1)
+    x = inputs.device_unit_vectors(2 + idx, n, d, DEV, tdt)
+    cache = B.new_cache(1, 1, n, d, bits, DEV)
+    sp = t.zeros((1,), dtype=t.int32, device=DEV)
+    B.iq_quantize_append(cfg, x.view(1, n, 1, d), sp, cache)
+    out = t.empty((1, n, 1, d), dtype=tdt, device=DEV)
+    B.iq_dequantize(cfg, cache, sp, n, out)
+    mse_all = float(((x.float() - out.float().view(n, d)) ** 2).sum(dim=-1).double().mean())
+    rng = np.random.default_rng(idx)
+    sample = np.unique(np.concatenate([rng.choice(n, 2000, replace=False), np.arange(n - 48, n)]))
+    sidx = t.from_numpy(sample).to(DEV)
+    xs = x[sidx].cpu().numpy()
+    rows = cache.codes[0, 0][sidx].cpu().numpy()
+    norms = cache.norms[0, 0][sidx].cpu().numpy().view(np.uint16)
+    got = out.view(n, d)[sidx].float().cpu().numpy().astype(np.float64)
+    cb = O.codebook(bits, d)
+    ref = O.quantize(xs, quats[0], cb, variant)
+    rc, nf, nfm = reconcile_codes(rows, ref["codes"], ref["flags"], bits, d)
+    rn, _, _ = reconcile_norms(norms, ref["norm16"], ref["norm_flags"])
+    want = O.dequantize_codes(rc, rn, quats[0], cb, variant)
+    err = float(np.max(np.abs(got - want)))
+    expect = quant_mse_closed_form(d, cb)
+    say(f"C2[{idx}] v={variant} d={d} b={bits} {np.dtype(dt).name}: flagged={nf}/{nfm} "
+        f"dequant_maxabs={err:.3g} mse={mse_all:.6f} closed={expect:.6f}")
+    assert err <= TOL[dt]
+    # fp16 inputs are unit vectors only to fp16 precision: allow 0.5% slack
+    assert abs(mse_all - expect) < (0.002 if dt == np.float32 else 0.005) * expect + 2e-5
