@@ -127,7 +127,7 @@ def test_c4_needles_32k():
     check_outputs("C4", got, lse, arg, ref, rlse, rarg, 2e-3)
     for h, g, p in case["needles"]:
         assert arg[0, h] == p, (h, g, p, arg[0, h])
-        assert rarg[h] == p
+        assert rarg[0, h] == p
     say(f"C4: all {len(case['needles'])} needle argmax positions preserved")
 
 
@@ -178,11 +178,14 @@ def test_split_geometry_invariance():
     geometry) agrees with the oracle each time."""
     d, bits, hq, hkv, T = 128, 3, 16, 2, 5000
     case = inputs.decode_case(seed=13, kv_len=T, num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
-    cfg, quats, kc, vc = decode_case_gpu(case, d, bits, O.FAST, hkv)
+    cfg, quats = make_config(d, bits, O.FAST, hkv)
+    cap = 5000 + 256 * 3          # rows beyond T stay zero and are never read
+    kc = quantize_rows(cfg, case["k"][None], capacity=cap)
+    vc = quantize_rows(cfg, case["v"][None], capacity=cap)
     q = case["q"][None]
     ref, rlse, rarg = oracle_decode(q, case["k"][None], case["v"][None], quats, cfg, [T],
                                     host_cache(kc), host_cache(vc))
-    for max_len in (T, T + 1, 6000, 5000 + 256 * 3):
+    for max_len in (T, T + 1, 5600, cap):
         got, lse, arg = run_decode(cfg, q, kc, vc, [T], max_len)
         check_outputs(f"split max_len={max_len}", got, lse, arg, ref, rlse, rarg, 2e-3)
 
