@@ -22,11 +22,52 @@ int check_config(const iq_config *cfg) {
   if (cfg->num_kv_heads < 1) return IQ_ERR_INVALID_ARG;
   if (!aligned16(cfg->quats)) return IQ_ERR_MISALIGNED;
   const int n = 1 << cfg->bits;
+  float lo = INFINITY, hi = 0.f;
   for (int k = 0; k < n; ++k) {
-    if (!std::isfinite(cfg->centroids[k])) return IQ_ERR_INVALID_ARG;
-    if (k > 0 && !(cfg->centroids[k] > cfg->centroids[k - 1])) return IQ_ERR_INVALID_ARG;
+    const float c = cfg->centroids[k];
+    if (!std::isfinite(c)) return IQ_ERR_INVALID_ARG;
+    if (k > 0 && !(c > cfg->centroids[k - 1])) return IQ_ERR_INVALID_ARG;
+    // fp16 precision: at most 11 significant bits (low 13 fp32 mantissa bits clear)
+    uint32_t u;
+    std::memcpy(&u, &c, 4);
+    if (c != 0.f && ((u & 0x1FFFu) != 0 || (u & 0x7F800000u) == 0)) return IQ_ERR_INVALID_ARG;
+    if (c != 0.f) {
+      lo = std::fmin(lo, std::fabs(c));
+      hi = std::fmax(hi, std::fabs(c));
+    }
   }
+  // one power-of-two scale must bring every level into the fp16 normal range
+  if (hi > 0.f && hi / lo >= 0x1p28f) return IQ_ERR_INVALID_ARG;
   return IQ_OK;
+}
+
+// Scale exponent e with max|c| * 2^e in [1, 2), and the table of fp16 pairs
+// (c_i 2^e, c_k 2^e) at index i | k << bits.  Exact: every level has at most
+// 11 significant bits (checked in check_config).
+int centroid_exponent(const iq_config *cfg) {
+  float hi = 0.f;
+  for (int k = 0; k < (1 << cfg->bits); ++k) hi = std::fmax(hi, std::fabs(cfg->centroids[k]));
+  if (hi == 0.f) return 0;
+  int e = 0;
+  std::frexp(hi, &e);        // hi = m 2^e, m in [0.5, 1)
+  return 1 - e;
+}
+
+uint16_t fp16_bits_exact(float x) {
+  const _Float16 h = static_cast<_Float16>(x);
+  uint16_t b;
+  std::memcpy(&b, &h, 2);
+  return b;
+}
+
+void fill_pair_table(const iq_config *cfg, int e, uint32_t *lut) {
+  const int n = 1 << cfg->bits;
+  for (int i = 0; i < n; ++i)
+    for (int k = 0; k < n; ++k) {
+      const uint32_t lo = fp16_bits_exact(std::ldexp(cfg->centroids[i], e));
+      const uint32_t hi = fp16_bits_exact(std::ldexp(cfg->centroids[k], e));
+      lut[i | (k << cfg->bits)] = lo | (hi << 16);
+    }
 }
 
 int check_cache(const iq_cache *c) {
@@ -61,10 +102,10 @@ struct Geometry {
 };
 
 Geometry decode_geometry(int32_t batch, int32_t hkv, int64_t max_kv_len) {
-  const int64_t unit = (int64_t)iq::kDecodeWaves * iq::kDecodeTile;
+  const int64_t unit = (int64_t)iq::kDecodeWaves * iq::kDecodeStep;
   const int64_t T = max_kv_len > 0 ? max_kv_len : 1;
   const int64_t pairs = (int64_t)batch * hkv;
-  const int64_t target_groups = 2048;
+  const int64_t target_groups = 1024;     // 4 resident workgroups on each of 256 CUs
   int64_t want = (target_groups + pairs - 1) / pairs;
   if (want < 1) want = 1;
   int64_t chunk = (T + want - 1) / want;
@@ -127,8 +168,15 @@ int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out) {
     }
     if (moved < 1e-15) break;
   }
+  // Levels held at fp16 precision: 11 significant bits, ties to even, so a
+  // power-of-two multiple of each is an exact fp16 number (the decode kernel
+  // feeds them to fp16 matrix instructions without rounding).
   const double s = 1.0 / std::sqrt(static_cast<double>(head_dim));
-  for (int k = 0; k < n; ++k) centroids_out[k] = static_cast<float>(c[k] * s);
+  for (int k = 0; k < n; ++k) {
+    int e = 0;
+    const double m = std::frexp(c[k] * s, &e);            // |m| in [0.5, 1)
+    centroids_out[k] = static_cast<float>(std::ldexp(std::nearbyint(std::ldexp(m, 11)), e - 11));
+  }
   return IQ_OK;
 }
 
@@ -188,36 +236,44 @@ size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch, int32_t nu
   if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return 0;
   if (num_q_heads % cfg->num_kv_heads) return 0;
   const Geometry g = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
-  return (size_t)batch * num_q_heads * g.n_split * iq::kDecodeWaves * (cfg->head_dim + iq::kRecHeader) *
-         sizeof(float);
+  return (size_t)batch * num_q_heads * g.n_split * (cfg->head_dim + iq::kRecHeader) * sizeof(float);
 }
 
-int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
-                        int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
-                        const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out,
-                        int32_t out_dtype, float *lse_out, int32_t *argmax_out, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
+                               int64_t max_kv_len, const void *workspace, size_t workspace_bytes,
+                               int *group) {
   int st = check_config(cfg);
   if (st != IQ_OK) return st;
-  if (!q || !kv_len || !out || !workspace) return IQ_ERR_INVALID_ARG;
-  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
+  if (!workspace) return IQ_ERR_INVALID_ARG;
   if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return IQ_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return IQ_ERR_INVALID_ARG;
   if (num_q_heads % cfg->num_kv_heads) return IQ_ERR_INVALID_ARG;
-  const int group = num_q_heads / cfg->num_kv_heads;
-  if (group != 1 && group != 2 && group != 4 && group != 8) return IQ_ERR_UNSUPPORTED;
+  *group = num_q_heads / cfg->num_kv_heads;
+  if (*group != 1 && *group != 2 && *group != 4 && *group != 8) return IQ_ERR_UNSUPPORTED;
+  if (!aligned16(workspace)) return IQ_ERR_MISALIGNED;
+  if (workspace_bytes < iq_decode_workspace_bytes(cfg, batch, num_q_heads, max_kv_len)) return IQ_ERR_WORKSPACE;
+  return IQ_OK;
+}
+
+int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
+                                int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
+                                const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  int group = 0;
+  int st = check_decode_common(cfg, batch, num_q_heads, max_kv_len, workspace, workspace_bytes, &group);
+  if (st != IQ_OK) return st;
+  if (!q || !kv_len) return IQ_ERR_INVALID_ARG;
+  if (!valid_dtype(q_dtype)) return IQ_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return IQ_ERR_INVALID_ARG;
   st = check_cache(k);
   if (st != IQ_OK) return st;
   st = check_cache(v);
   if (st != IQ_OK) return st;
   if (max_kv_len > k->capacity || max_kv_len > v->capacity) return IQ_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return IQ_ERR_MISALIGNED;
-  if ((lse_out && !aligned16(lse_out)) || (argmax_out && !aligned16(argmax_out))) return IQ_ERR_MISALIGNED;
-  const size_t need = iq_decode_workspace_bytes(cfg, batch, num_q_heads, max_kv_len);
-  if (workspace_bytes < need) return IQ_ERR_WORKSPACE;
+  if (!aligned16(q)) return IQ_ERR_MISALIGNED;
 
   const Geometry geo = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
-  const Tables tab = make_tables(cfg);
+  const int e = centroid_exponent(cfg);
+  constexpr int qexp = 8;
   iq::DecodeArgs a;
   a.q = q;
   a.q_f16 = q_dtype == IQ_F16;
@@ -236,15 +292,28 @@ int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, in
   a.variant = cfg->variant;
   a.chunk = geo.chunk;
   a.n_split = geo.n_split;
-  a.qscale = softmax_scale * 1.4426950408889634f;
+  a.qmul = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634 * std::ldexp(1.0, qexp - e));
+  a.kscale = std::ldexp(1.0f, -qexp);
   a.ws = static_cast<float *>(workspace);
-  a.tab = tab;
-  st = hip_status(iq::launch_decode(cfg->head_dim, cfg->bits, a, stream));
-  if (st != IQ_OK) return st;
+  std::memset(a.lut, 0, sizeof(a.lut));
+  fill_pair_table(cfg, e, a.lut);
+  return hip_status(iq::launch_decode(cfg->head_dim, cfg->bits, a, stream));
+}
 
+int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
+                              int64_t max_kv_len, void *out, int32_t out_dtype, float *lse_out,
+                              int32_t *argmax_out, const void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  int group = 0;
+  int st = check_decode_common(cfg, batch, num_q_heads, max_kv_len, workspace, workspace_bytes, &group);
+  if (st != IQ_OK) return st;
+  if (!out) return IQ_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
+  if (!aligned16(out)) return IQ_ERR_MISALIGNED;
+  if ((lse_out && !aligned16(lse_out)) || (argmax_out && !aligned16(argmax_out))) return IQ_ERR_MISALIGNED;
+  const Geometry geo = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
   iq::MergeArgs m;
-  m.ws = a.ws;
-  m.kv_len = kv_len;
+  m.ws = static_cast<const float *>(workspace);
   m.quats = cfg->quats;
   m.out = out;
   m.out_f16 = out_dtype == IQ_F16;
@@ -253,9 +322,29 @@ int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, in
   m.batch = batch;
   m.hq = num_q_heads;
   m.group = group;
-  m.n_part = geo.n_split * iq::kDecodeWaves;
-  m.tab = tab;
+  m.n_part = geo.n_split;
+  m.oscale = std::ldexp(1.0f, -centroid_exponent(cfg));
   return hip_status(iq::launch_merge(cfg->head_dim, cfg->variant, m, stream));
+}
+
+int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
+                        int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
+                        const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out,
+                        int32_t out_dtype, float *lse_out, int32_t *argmax_out, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  // validate both phases before enqueueing either
+  int group = 0;
+  int st = check_decode_common(cfg, batch, num_q_heads, max_kv_len, workspace, workspace_bytes, &group);
+  if (st != IQ_OK) return st;
+  if (!out) return IQ_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
+  if (!aligned16(out)) return IQ_ERR_MISALIGNED;
+  if ((lse_out && !aligned16(lse_out)) || (argmax_out && !aligned16(argmax_out))) return IQ_ERR_MISALIGNED;
+  st = iq_decode_attention_partial(cfg, q, q_dtype, batch, num_q_heads, k, v, kv_len, max_kv_len,
+                                   softmax_scale, workspace, workspace_bytes, stream);
+  if (st != IQ_OK) return st;
+  return iq_decode_attention_merge(cfg, batch, num_q_heads, max_kv_len, out, out_dtype, lse_out,
+                                   argmax_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,194 +1,350 @@
-// Compressed-space decode attention (RotaryQuant §3.4 Table 2, Appendix A).
+// Compressed-space decode attention (RotaryQuant §3.4 Table 2, Appendix A),
+// split-K over the context, scores and value accumulation on fp16 matrix
+// cores (v_mfma_f32_16x16x32_f16) directly from the packed codes.
 //
-// attention kernel: one workgroup per (split, KV head, sequence).  Its
-//   prologue rotates the G query heads of the group once (q~ = R q, with
-//   softmax_scale * log2(e) folded in).  Each of its waves walks its share of
-//   the split in tiles of 64 tokens: scores of the G heads on the packed K rows
-//   (lane = token), online base-2 softmax, then value accumulation on the
-//   packed V rows staged in LDS (lane = output dimension).  Every wave writes
-//   one partial state (m, l, argmax, o~[d]) per query head.
-// merge kernel: one workgroup per (query head, sequence): merges the partial
-//   states, divides by the softmax denominator and applies R^T once.
+// partial kernel: one workgroup of 4 waves per (split, KV head, sequence).
+//   Prologue: q~ = R q for the G query heads of the KV head (WHT butterflies
+//   and SO(4) blocks in LDS), scaled, split into fp16 hi + lo parts and held
+//   in registers as the B operand of the score product.
+//   Each wave walks its token range 32 tokens at a time:
+//     scores  S^T (16 tokens x 16 columns) = C_K (16 x d) . Q~^T (d x 16) for
+//             two 16-token tiles; column j < G holds q~_hi of head j, column
+//             G + j holds q~_lo of head j, so S_hi + S_lo is the full-precision
+//             score.  C_K comes from the packed K rows through a 2-code table
+//             of exact fp16 centroid pairs (the codebook has 11 significant
+//             bits, scaled by a power of two).
+//     softmax online, base 2, with a lazily raised running maximum (only
+//             rescaled when a score exceeds it by more than kLazyTau).
+//     values  O~ (16 rows x d) += P (16 x 32 tokens) . C_V (32 x d); row j < G
+//             carries the fp16 hi part of p * ||v|| for head j, row G + j the
+//             lo part, so the fp32 accumulators see the weights to ~2^-22.
+//   The 4 waves merge their states in LDS; the workgroup writes one partial
+//   record (M, L, best score, best position, o~[d]) per query head.
+// merge kernel: one workgroup per (query head, sequence): combines the split
+//   records, divides by the softmax denominator and applies R^T once.
 #include "iq_device.h"
 #include "iq_internal.h"
 
 namespace iq {
 namespace {
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = kDecodeWaves * 64;
 
-template <int BITS>
-__device__ __forceinline__ uint32_t code_at(const uint32_t *row, int e) {
-  const int bit = BITS * e;
-  const int wd = bit >> 5;
-  const int off = bit & 31;
-  uint32_t c = row[wd] >> off;
-  if (off + BITS > 32) c |= row[wd + 1] << (32 - off);
-  return c & ((1u << BITS) - 1u);
+// W-bit field at bit position pos of the little-endian bit string w[].
+template <int N>
+__device__ __forceinline__ uint32_t field(const uint32_t (&w)[N], int pos, int width) {
+  const int wd = pos >> 5, off = pos & 31;
+  uint32_t v = (off + width <= 32 || wd + 1 >= N) ? (w[wd] >> off)
+                                                  : __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off);
+  return v & ((1u << width) - 1u);
 }
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+// Value of lane (lane ^ G) for the hi/lo partner column.
+template <int G>
+__device__ __forceinline__ float xor_g(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (G == 8)
+    r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);      // row_ror:8 == lane ^ 8
+  else if constexpr (G == 4)
+    r = __builtin_amdgcn_ds_swizzle(x, (4 << 10) | 0x1F);          // lane ^ 4
+  else if constexpr (G == 2)
+    r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);       // quad_perm [2,3,0,1]
+  else
+    r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);       // quad_perm [1,0,3,2]
+  return __builtin_bit_cast(float, r);
+}
+
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  u4 u = {a, b, c, d};
+  return __builtin_bit_cast(half8, u);
 }
 
 template <int D, int BITS, int G>
-__global__ __launch_bounds__(kThreads) void attention_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   constexpr int NLEV = 1 << BITS;
-  constexpr int ROWW = D * BITS / 32;   // dwords per packed row
-  constexpr int DPL = D / 64;           // output dimensions per lane
+  constexpr int KS = D / 32;                 // k-steps of the score product
+  constexpr int NB = D / 16;                 // 16-column blocks of the value product
+  constexpr int ROWW = D * BITS / 32;        // dwords per packed row
+  constexpr int CW = ROWW / 4;               // dwords of a row held by one lane group (d/4 dims)
+  constexpr int VCB = (D / 16) * BITS;       // bits of the d/16 codes a lane owns in the value product
+  constexpr int VW = (VCB + 31) / 32 + 1;    // dwords loaded to cover them at any bit offset
+  constexpr int VX = (VCB + 31) / 32;        // dwords after extraction
+  constexpr int NROW = 2 * G;                // live rows/columns (hi + lo)
+
   const int split = blockIdx.x;
-  const int g = blockIdx.y;
+  const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int T = a.kv_len[b];
 
-  __shared__ float qtmp[G][D];
-  __shared__ float qt[D][G];
-  __shared__ float cent[NLEV];
-  __shared__ uint32_t vrow[kDecodeWaves][kDecodeTile][ROWW + 1];
-  __shared__ float pw[kDecodeWaves][kDecodeTile][G];
+  __shared__ uint32_t lut[NLEV * NLEV];
+  __shared__ float qs[G][D];
+  __shared__ float red_o[kDecodeWaves][G][D];
+  __shared__ float red_h[kDecodeWaves][G][4];
 
-  // ---- prologue: q~ = R q for the G query heads of this KV head -------------
+  // ---- prologue: q~ = R q for this KV head's query heads --------------------
+  for (int i = threadIdx.x; i < NLEV * NLEV; i += kThreads) lut[i] = a.lut[i];
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int hh = idx / D, i = idx % D;
-    const size_t off = ((size_t)b * a.hq + g * G + hh) * D + i;
-    qtmp[hh][i] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[off])
-                          : static_cast<const float *>(a.q)[off];
+    const size_t off = ((size_t)b * a.hq + kvh * G + hh) * D + i;
+    qs[hh][i] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[off])
+                        : static_cast<const float *>(a.q)[off];
   }
-  if (threadIdx.x < NLEV) cent[threadIdx.x] = a.tab.cent[threadIdx.x];
   __syncthreads();
   for (int st = 1; st < D; st <<= 1) {
     for (int p = threadIdx.x; p < G * D / 2; p += kThreads) {
       const int hh = p / (D / 2), pp = p % (D / 2);
       const int i = (pp / st) * 2 * st + (pp % st);
-      const float x0 = qtmp[hh][i], x1 = qtmp[hh][i + st];
-      qtmp[hh][i] = x0 + x1;
-      qtmp[hh][i + st] = x0 - x1;
+      const float x0 = qs[hh][i], x1 = qs[hh][i + st];
+      qs[hh][i] = x0 + x1;
+      qs[hh][i + st] = x0 - x1;
     }
     __syncthreads();
   }
   {
-    const float scale = a.qscale / sqrtf((float)D);
-    const float4 *qg = reinterpret_cast<const float4 *>(a.quats) + (size_t)g * (D / 4) * 2;
+    const float scale = a.qmul / sqrtf((float)D);
+    const float4 *qg = reinterpret_cast<const float4 *>(a.quats) + (size_t)kvh * (D / 4) * 2;
     for (int p = threadIdx.x; p < G * D / 4; p += kThreads) {
       const int hh = p / (D / 4), blk = p % (D / 4);
-      float4 v = make_float4(qtmp[hh][4 * blk] * scale, qtmp[hh][4 * blk + 1] * scale,
-                             qtmp[hh][4 * blk + 2] * scale, qtmp[hh][4 * blk + 3] * scale);
+      float4 v = make_float4(qs[hh][4 * blk] * scale, qs[hh][4 * blk + 1] * scale,
+                             qs[hh][4 * blk + 2] * scale, qs[hh][4 * blk + 3] * scale);
       const float4 qL = qg[2 * blk], qR = qg[2 * blk + 1];
       float4 t = a.variant == 0 ? so4_fwd<0>(v, qL, qR) : so4_fwd<1>(v, qL, qR);
-      qt[4 * blk][hh] = t.x;
-      qt[4 * blk + 1][hh] = t.y;
-      qt[4 * blk + 2][hh] = t.z;
-      qt[4 * blk + 3][hh] = t.w;
+      qs[hh][4 * blk] = t.x;
+      qs[hh][4 * blk + 1] = t.y;
+      qs[hh][4 * blk + 2] = t.z;
+      qs[hh][4 * blk + 3] = t.w;
     }
   }
   __syncthreads();
 
-  // ---- main loop over this wave's tokens -------------------------------------
+  const int j = lane & 15;      // column of the score tile / row of the value operand
+  const int g4 = lane >> 4;     // lane group: k-slice of the operands, row quad of results
+  const bool live = j < NROW;
+  const bool lo_lane = live && j >= G;
+  const int head = j % G;
+
+  // B operand of the score product: lane group g4 covers dims [g4*D/4, (g4+1)*D/4).
+  half8 qB[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = live ? qs[head][g4 * (D / 4) + 8 * s + e] : 0.f;
+      const _Float16 hi = static_cast<_Float16>(v);
+      qB[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
+    }
+  }
+
+  // ---- main loop ---------------------------------------------------------------
   const int sub = a.chunk / kDecodeWaves;
   const int begin = split * a.chunk + wave * sub;
   const int end = min(T, begin + sub);
-  const long long headrow = (long long)b * a.hkv + g;
-  const uint32_t *kbase = reinterpret_cast<const uint32_t *>(a.kc) + headrow * a.kcap * ROWW;
-  const uint32_t *vbase = reinterpret_cast<const uint32_t *>(a.vc) + headrow * a.vcap * ROWW;
-  const uint16_t *knb = a.kn + headrow * a.kcap;
-  const uint16_t *vnb = a.vn + headrow * a.vcap;
+  const long long hrow = (long long)b * a.hkv + kvh;
+  const uint32_t *kbase = reinterpret_cast<const uint32_t *>(a.kc) + hrow * a.kcap * ROWW;
+  const uint32_t *vbase = reinterpret_cast<const uint32_t *>(a.vc) + hrow * a.vcap * ROWW;
+  const uint16_t *knb = a.kn + hrow * a.kcap;
+  const uint16_t *vnb = a.vn + hrow * a.vcap;
+  const int my_tile = lo_lane ? 1 : 0;
+  const int vbit = VCB * j;                  // bit offset of this lane's codes in a row
 
-  float m[G], l[G], bs[G], acc[G][DPL];
-  int bj[G];
+  float Mh = -INFINITY, Lh = 0.f, best_s = -INFINITY;
+  int best_j = -1;
+  floatx4 O[NB];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-    bs[h] = -INFINITY;
-    bj[h] = -1;
+  for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = begin; t0 < end; t0 += kDecodeStep) {
+    const int last = end - 1;
+    // packed K rows of the two 16-token tiles (lane: token j, dims slice g4)
+    uint32_t kw[2][CW];
 #pragma unroll
-    for (int r = 0; r < DPL; ++r) acc[h][r] = 0.f;
+    for (int tile = 0; tile < 2; ++tile) {
+      const int row = min(t0 + 16 * tile + j, last);
+#pragma unroll
+      for (int i = 0; i < CW; ++i) kw[tile][i] = kbase[(long long)row * ROWW + g4 * CW + i];
+    }
+    // the 8 tokens this lane holds in the result/operand layouts: 4*g4 + r of each tile
+    float nk[4], nv[4], ev[4];
+    uint32_t vch[8][VX];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int tile = r >> 2;
+      const int row = min(t0 + 16 * tile + 4 * g4 + (r & 3), last);
+      uint32_t w[VW];
+      const uint32_t *src = vbase + (long long)row * ROWW + (vbit >> 5);
+#pragma unroll
+      for (int i = 0; i < VW; ++i) w[i] = (vbit >> 5) + i < ROWW ? src[i] : 0u;
+#pragma unroll
+      for (int i = 0; i < VX; ++i) vch[r][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], vbit & 31);
+      if (tile == my_tile) {
+        const uint16_t kb = knb[row], vb = vnb[row];
+        nk[r & 3] = half_bits_to_float(kb) * a.kscale;
+        nv[r & 3] = live ? half_bits_to_float(vb) : 0.f;
+        ev[r & 3] = (float)((vb >> 10) & 31);
+      }
+    }
+
+    // scores for both tiles
+    floatx4 S[2];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      S[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) w4[p] = lut[field(kw[tile], (8 * s + 2 * p) * BITS, 2 * BITS)];
+        S[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(w4[0], w4[1], w4[2], w4[3]), qB[s],
+                                                         S[tile], 0, 0, 0);
+      }
+    }
+
+    // softmax on this lane's tile (hi lanes: tile 0, lo lanes: tile 1)
+    float sig[4], u[4];
+    float umax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float c0 = S[0][r] + xor_g<G>(S[0][r]);
+      const float c1 = S[1][r] + xor_g<G>(S[1][r]);
+      const int tok = t0 + 16 * my_tile + 4 * g4 + r;
+      const bool ok = live && tok < end;
+      sig[r] = ok ? (my_tile ? c1 : c0) * nk[r] : -INFINITY;
+      u[r] = sig[r] + ev[r];
+      umax = fmaxf(umax, u[r]);
+      if (sig[r] > best_s) {
+        best_s = sig[r];
+        best_j = tok;
+      }
+    }
+    umax = fmaxf(umax, xor_g<G>(umax));
+    umax = fmaxf(umax, __shfl_xor(umax, 16, 64));
+    umax = fmaxf(umax, __shfl_xor(umax, 32, 64));
+    if (__any(umax > Mh + kLazyTau)) {
+      const float mnew = fmaxf(Mh, umax);
+      const float alpha = (Mh == -INFINITY) ? 0.f : exp2f(Mh - mnew);
+      Lh *= alpha;
+      Mh = mnew;
+      // rows 4*g4 + i of the value accumulators belong to head (4*g4 + i) % G
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g4 + i;
+        const float ar = __shfl(alpha, row < NROW ? row % G : 0, 64);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) O[nb][i] *= ar;
+      }
+    }
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = exp2f(sig[r] - Mh + kWeightBias);   // 0 for masked tokens
+      Lh += x;
+      y[r] = x * nv[r];
+    }
+    // A operand: k order = tile-0 tokens 4*g4..+3, then tile-1 tokens 4*g4..+3
+    half8 P;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float other = xor_g<G>(y[r]);
+      const float p0 = my_tile ? other : y[r];
+      const float p1 = my_tile ? y[r] : other;
+      const _Float16 h0 = static_cast<_Float16>(p0), h1 = static_cast<_Float16>(p1);
+      P[r] = lo_lane ? static_cast<_Float16>(p0 - static_cast<float>(h0)) : h0;
+      P[4 + r] = lo_lane ? static_cast<_Float16>(p1 - static_cast<float>(h1)) : h1;
+    }
+
+    // values: column block nb holds dims (D/16) * n + nb of lane column n = j
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t c0 = field(vch[2 * p], nb * BITS, BITS);
+        const uint32_t c1 = field(vch[2 * p + 1], nb * BITS, BITS);
+        w4[p] = lut[c0 | (c1 << BITS)];
+      }
+      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(w4[0], w4[1], w4[2], w4[3]), O[nb], 0, 0, 0);
+    }
   }
 
-  for (int t0 = begin; t0 < end; t0 += kDecodeTile) {
-    const int j = t0 + lane;
-    const bool valid = j < end;
-    const int jr = valid ? j : t0;
-    uint32_t kw[ROWW];
-#pragma unroll
-    for (int i = 0; i < ROWW; ++i) kw[i] = kbase[(long long)jr * ROWW + i];
-    float sc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = 0.f;
-#pragma unroll 4
-    for (int e = 0; e < D; ++e) {
-      const float c = cent[code_at<BITS>(kw, e)];
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = fmaf(qt[e][h], c, sc[h]);
-    }
-    const float kn = half_bits_to_float(knb[jr]);
-    const float vn = half_bits_to_float(vnb[jr]);
-#pragma unroll
-    for (int i = 0; i < ROWW; ++i) vrow[wave][lane][i] = vbase[(long long)jr * ROWW + i];
-
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float s = valid ? sc[h] * kn : -INFINITY;
-      const float mnew = fmaxf(m[h], wave_max(s));
-      const float alpha = exp2f(m[h] - mnew);      // m = -inf -> 0
-      const float p = valid ? exp2f(s - mnew) : 0.f;
-      l[h] = l[h] * alpha + p;
-#pragma unroll
-      for (int r = 0; r < DPL; ++r) acc[h][r] *= alpha;
-      m[h] = mnew;
-      if (valid && s > bs[h]) {
-        bs[h] = s;
-        bj[h] = j;
+  // ---- wave state -> LDS -----------------------------------------------------------
+  // softmax denominator and argmax per head: lanes (head, head + G) x 4 groups
+  float lsum = live ? Lh : 0.f;
+  lsum += xor_g<G>(lsum);
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  float bs = live ? best_s : -INFINITY;
+  int bj = live ? best_j : -1;
+  {
+    auto take = [&](float os, int oj) {
+      if (os > bs || (os == bs && oj >= 0 && (bj < 0 || oj < bj))) {
+        bs = os;
+        bj = oj;
       }
-      pw[wave][lane][h] = p * vn;
-    }
-    wave_sync();
-
-    const int nt = min(kDecodeTile, end - t0);
-    for (int jj = 0; jj < nt; ++jj) {
-      const uint32_t *row = vrow[wave][jj];
-      float pv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = pw[wave][jj][h];
-#pragma unroll
-      for (int r = 0; r < DPL; ++r) {
-        const float c = cent[code_at<BITS>(row, lane + 64 * r)];
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h][r] = fmaf(pv[h], c, acc[h][r]);
-      }
-    }
-    wave_sync();
+    };
+    take(xor_g<G>(bs), __builtin_bit_cast(int, xor_g<G>(__builtin_bit_cast(float, bj))));
+    take(__shfl_xor(bs, 16, 64), __shfl_xor(bj, 16, 64));
+    take(__shfl_xor(bs, 32, 64), __shfl_xor(bj, 32, 64));
   }
+  if (lane < G) {
+    red_h[wave][lane][0] = Mh;
+    red_h[wave][lane][1] = lsum;
+    red_h[wave][lane][2] = bs;
+    red_h[wave][lane][3] = __builtin_bit_cast(float, bj);
+  }
+  // value rows: hi row h + lo row h + G
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = O[nb][i];
+      float partner;
+      if constexpr (G >= 4)
+        partner = __shfl_xor(v, 16 * (G / 4), 64);
+      else
+        partner = O[nb][i ^ G];
+      const int row = 4 * g4 + i;
+      if (row < G) red_o[wave][row][(D / 16) * j + nb] = v + partner;
+    }
+  }
+  __syncthreads();
 
-  // ---- this wave's partial state ---------------------------------------------
-  const int n_part = a.n_split * kDecodeWaves;
-  const int part = split * kDecodeWaves + wave;
+  // ---- combine the waves, write this split's records ---------------------------------
+  const int n_part = a.n_split;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int hh = idx / D, i = idx % D;
+    float M = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float lsum = wave_sum(l[h]);
-    float s = bs[h];
-    int jj = bj[h];
+    for (int w = 0; w < kDecodeWaves; ++w)
+      if (red_h[w][hh][1] > 0.f) M = fmaxf(M, red_h[w][hh][0]);
+    float o = 0.f, L = 0.f, bsc = -INFINITY;
+    int bpos = -1;
 #pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) {
-      const float os = __shfl_xor(s, msk, 64);
-      const int oj = __shfl_xor(jj, msk, 64);
-      if (os > s || (os == s && oj >= 0 && (jj < 0 || oj < jj))) {
-        s = os;
-        jj = oj;
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      if (red_h[w][hh][1] > 0.f) {
+        const float sc = exp2f(red_h[w][hh][0] - M);
+        o += red_o[w][hh][i] * sc;
+        L += red_h[w][hh][1] * sc;
+        if (red_h[w][hh][2] > bsc) {
+          bsc = red_h[w][hh][2];
+          bpos = __builtin_bit_cast(int, red_h[w][hh][3]);
+        }
       }
     }
-    float *rec = a.ws + (((size_t)b * a.hq + g * G + h) * n_part + part) * (D + kRecHeader);
-    if (lane == 0) {
-      rec[0] = m[h];
-      rec[1] = lsum;
-      rec[2] = __builtin_bit_cast(float, jj);
-      rec[3] = 0.f;
+    float *rec = a.ws + (((size_t)b * a.hq + kvh * G + hh) * n_part + split) * (D + kRecHeader);
+    rec[kRecHeader + i] = o;
+    if (i == 0) {
+      rec[0] = M;
+      rec[1] = L;
+      rec[2] = bsc;
+      rec[3] = __builtin_bit_cast(float, bpos);
     }
-#pragma unroll
-    for (int r = 0; r < DPL; ++r) rec[kRecHeader + lane + 64 * r] = acc[h][r];
   }
 }
 
@@ -205,7 +361,7 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
     const float *rec = recs + (size_t)p * (D + kRecHeader);
     if (rec[1] > 0.f) M = fmaxf(M, rec[0]);
   }
-  float L = 0.f, o = 0.f;
+  float L = 0.f, o = 0.f, bsc = -INFINITY;
   int arg = -1;
   for (int p = 0; p < a.n_part; ++p) {
     const float *rec = recs + (size_t)p * (D + kRecHeader);
@@ -214,12 +370,15 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
       const float w = exp2f(rec[0] - M);
       L += lp * w;
       o += rec[kRecHeader + i] * w;
-      if (arg < 0 && rec[0] == M) arg = __builtin_bit_cast(int, rec[2]);
+      if (rec[2] > bsc) {          // strict: ties keep the earlier (lower) positions
+        bsc = rec[2];
+        arg = __builtin_bit_cast(int, rec[3]);
+      }
     }
   }
 
   __shared__ float y[D];
-  y[i] = L > 0.f ? o / L : 0.f;
+  y[i] = L > 0.f ? o * a.oscale / L : 0.f;
   __syncthreads();
   if (i < D / 4) {
     const float4 *qg = reinterpret_cast<const float4 *>(a.quats) + (size_t)g * (D / 4) * 2;
@@ -254,30 +413,30 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
     static_cast<float *>(a.out)[off] = val;
   if (i == 0) {
     const size_t oh = (size_t)b * a.hq + h;
-    if (a.lse) a.lse[oh] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    if (a.lse) a.lse[oh] = L > 0.f ? (M - kWeightBias + log2f(L)) * 0.69314718055994531f : -INFINITY;
     if (a.argmax) a.argmax[oh] = L > 0.f ? arg : -1;
   }
 }
 
 template <int D, int BITS>
-hipError_t decode_dispatch_group(const DecodeArgs &a, hipStream_t s) {
+hipError_t partial_dispatch_group(const DecodeArgs &a, hipStream_t s) {
   dim3 grid((unsigned)a.n_split, (unsigned)a.hkv, (unsigned)a.batch);
   switch (a.group) {
-    case 1: hipLaunchKernelGGL((attention_kernel<D, BITS, 1>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attention_kernel<D, BITS, 2>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attention_kernel<D, BITS, 4>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attention_kernel<D, BITS, 8>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((partial_kernel<D, BITS, 1>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((partial_kernel<D, BITS, 2>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((partial_kernel<D, BITS, 4>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((partial_kernel<D, BITS, 8>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t decode_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
+hipError_t partial_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
   switch (bits) {
-    case 2: return decode_dispatch_group<D, 2>(a, s);
-    case 3: return decode_dispatch_group<D, 3>(a, s);
-    case 4: return decode_dispatch_group<D, 4>(a, s);
+    case 2: return partial_dispatch_group<D, 2>(a, s);
+    case 3: return partial_dispatch_group<D, 3>(a, s);
+    case 4: return partial_dispatch_group<D, 4>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -296,9 +455,9 @@ hipError_t merge_dispatch(int variant, const MergeArgs &a, hipStream_t s) {
 
 hipError_t launch_decode(int d, int bits, const DecodeArgs &a, hipStream_t s) {
   switch (d) {
-    case 128: return decode_dispatch_bits<128>(bits, a, s);
-    case 256: return decode_dispatch_bits<256>(bits, a, s);
-    case 512: return decode_dispatch_bits<512>(bits, a, s);
+    case 128: return partial_dispatch_bits<128>(bits, a, s);
+    case 256: return partial_dispatch_bits<256>(bits, a, s);
+    case 512: return partial_dispatch_bits<512>(bits, a, s);
   }
   return hipErrorInvalidValue;
 }

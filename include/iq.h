@@ -78,7 +78,10 @@ typedef struct {
   int32_t variant;         /* iq_variant; Fast reads q_L only */
   int32_t num_kv_heads;    /* H_kv >= 1 */
   const float *quats;      /* DEVICE [H_kv][d/4][2][4] fp32 unit quaternions */
-  const float *centroids;  /* HOST [2^b] fp32, strictly ascending, finite */
+  const float *centroids;  /* HOST [2^b] fp32, strictly ascending, finite, each
+                              with at most 11 significant bits (fp16 precision,
+                              as iq_codebook produces) and max/min nonzero
+                              magnitude below 2^28; else IQ_ERR_INVALID_ARG */
 } iq_config;
 
 /* One packed tensor (K or V) of a KV cache (a HOST struct). */
@@ -91,7 +94,9 @@ typedef struct {
 /* Lloyd-Max codebook for the coordinates of a rotated unit vector, taken as
  * N(0, 1/d) (RotaryQuant §3.2 Step 3: minimum expected distortion under the
  * post-rotation marginal).  Runs the Lloyd iteration for N(0,1) in double on
- * the host, scales by 1/sqrt(d) and rounds to fp32.
+ * the host, scales by 1/sqrt(d) and rounds each level to 11 significant bits
+ * (ties to even): the codebook is held at fp16 precision so that the decode
+ * kernel's fp16 matrix operands represent every level exactly.
  *   centroids_out: HOST array of 2^bits floats, written in ascending order.
  * Returns IQ_OK, IQ_ERR_INVALID_ARG (null) or IQ_ERR_UNSUPPORTED (bits, d). */
 int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out);
@@ -123,13 +128,16 @@ size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch,
                                  int32_t num_q_heads, int64_t max_kv_len);
 
 /* Decode attention on packed K/V (RotaryQuant §3.4 Table 2, Appendix A).
+ * Equivalent to iq_decode_attention_partial followed by
+ * iq_decode_attention_merge on the same stream and workspace.
  * One query token per sequence; query head h reads KV head h / (Hq / H_kv).
  *   q:          [batch][Hq][d] of q_dtype.
  *   k, v:       packed caches written by iq_quantize_append with this cfg.
  *   kv_len:     DEVICE int32 [batch]; attends rows [0, kv_len[b]) (includes a
  *               token appended this step).  kv_len[b] = 0 gives out = 0,
  *               lse = -inf, argmax = -1.
- *   max_kv_len: HOST upper bound of kv_len, used for the grid only.
+ *   max_kv_len: HOST upper bound of kv_len, used for the grid only; every
+ *               kv_len[b] must be <= max_kv_len (rows beyond it are not read).
  *   softmax_scale: multiplies q.k (1/sqrt(d) in Appendix A).
  *   out:        [batch][Hq][d] of out_dtype, in the original (un-rotated)
  *               domain.
@@ -146,6 +154,31 @@ int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype,
                         float *lse_out, int32_t *argmax_out,
                         void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/* Split phase of iq_decode_attention (the context is cut into splits, as in
+ * FlashAttention's tiling that RotaryQuant §2 cites): rotates each query once,
+ * scores the packed K rows and accumulates the packed V rows in rotated space,
+ * and leaves one partial softmax state per (sequence, query head, split) in
+ * `workspace`.  Arguments as for iq_decode_attention.  The workspace content
+ * is opaque and valid only for a merge call with the same cfg, batch,
+ * num_q_heads and max_kv_len. */
+int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_dtype,
+                                int32_t batch, int32_t num_q_heads,
+                                const iq_cache *k, const iq_cache *v,
+                                const int32_t *kv_len, int64_t max_kv_len,
+                                float softmax_scale, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Merge phase: combines the partial states a preceding
+ * iq_decode_attention_partial left in `workspace`, divides by the softmax
+ * denominator and applies R^T once (RotaryQuant §3.4: the inverse rotation
+ * acts on the aggregated output, not per token).  Writes out, lse_out and
+ * argmax_out as iq_decode_attention does. */
+int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
+                              int64_t max_kv_len, void *out, int32_t out_dtype,
+                              float *lse_out, int32_t *argmax_out,
+                              const void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *iq_status_string(int status);

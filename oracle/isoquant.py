@@ -38,6 +38,7 @@ __all__ = [
     "BOUNDARY_BAND",
     "lloyd_max_gaussian",
     "codebook",
+    "round_significand",
     "thresholds",
     "wht",
     "qmul",
@@ -120,13 +121,23 @@ def lloyd_max_gaussian(bits: int, tol: float = 1e-15, max_iter: int = 200000) ->
     return c
 
 
-def codebook(bits: int, head_dim: int) -> np.ndarray:
-    """FP32 codebook for coordinates of a rotated unit vector, N(0, 1/d).
+def round_significand(x: np.ndarray, digits: int = 11) -> np.ndarray:
+    """Round FP64 values to ``digits`` significant bits, ties to even."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 2.0 ** digits), e - digits)
 
-    The Gaussian Lloyd-Max centroids scaled by 1/sqrt(d), rounded to FP32.
-    This FP32 array is what both the oracle and the device path consume.
+
+def codebook(bits: int, head_dim: int) -> np.ndarray:
+    """Codebook for coordinates of a rotated unit vector, N(0, 1/d).
+
+    The Gaussian Lloyd-Max centroids scaled by 1/sqrt(d) and held at fp16
+    precision: each value rounded (ties to even) to 11 significant bits, so
+    that a power-of-two multiple of it is an exact fp16 number.  Returned as
+    FP32 (exact); this array is what both the oracle and the device path
+    consume.
     """
-    return (lloyd_max_gaussian(bits) / math.sqrt(head_dim)).astype(np.float32)
+    return round_significand(lloyd_max_gaussian(bits) / math.sqrt(head_dim)).astype(np.float32)
 
 
 def thresholds(centroids: np.ndarray) -> np.ndarray:

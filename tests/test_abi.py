@@ -24,7 +24,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) >= {"iq_quantize_append", "iq_dequantize", "iq_decode_attention",
-                          "iq_decode_workspace_bytes", "iq_status_string", "iq_codebook"}
+                          "iq_decode_workspace_bytes", "iq_status_string", "iq_codebook",
+                          "iq_decode_attention_partial", "iq_decode_attention_merge"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -109,6 +110,10 @@ def test_quantize_validation():
     nan = O.codebook(3, 128).copy()
     nan[0] = np.nan
     assert call_quant(cfg(centroids=nan)) == -1
+    # levels must carry fp16 precision (at most 11 significant bits)
+    fine = O.codebook(3, 128).copy()
+    fine[5] = np.nextafter(fine[5], np.float32(1))
+    assert call_quant(cfg(centroids=fine)) == -1
 
 
 def call_decode(c, hq=32, batch=1, max_len=16, cap=16, ws_bytes=None, q=0x2000, out=0x6000,
@@ -155,3 +160,23 @@ def test_dequantize_validation():
     assert L.iq_dequantize(ctypes.byref(cc), ctypes.byref(cache), 1, 0x3000, 4, 0x6002, 0, None) == -3
     assert L.iq_dequantize(ctypes.byref(cc), ctypes.byref(cache), 1, 0x3000, 4, 0x6000, 9, None) == -2
     assert L.iq_dequantize(ctypes.byref(cc), None, 1, 0x3000, 4, 0x6000, 0, None) == -1
+
+
+def test_partial_and_merge_validation():
+    L = B.lib()
+    c = cfg()
+    cc = c.c()
+    need = L.iq_decode_workspace_bytes(ctypes.byref(cc), 1, 32, 16)
+    k = B.IQCacheC(0x4000, 0x5000, 16)
+    # partial: misaligned q, small workspace, bad group
+    assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2004, 1, 1, 32, ctypes.byref(k), ctypes.byref(k),
+                                         0x8000, 16, 0.1, 0x7000, need, None) == -3
+    assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 32, ctypes.byref(k), ctypes.byref(k),
+                                         0x8000, 16, 0.1, 0x7000, need - 16, None) == -4
+    assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 64, ctypes.byref(k), ctypes.byref(k),
+                                         0x8000, 16, 0.1, 0x7000, need, None) == -2
+    # merge: null out, bad dtype, misaligned argmax
+    assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, None, 0, None, None, 0x7000, need, None) == -1
+    assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 5, None, None, 0x7000, need, None) == -2
+    assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 0, None, 0x9002, 0x7000, need, None) == -3
+    assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 0, None, None, 0x7000, need - 4, None) == -4

@@ -252,3 +252,48 @@ def test_c5_batched_append_decode():
         say(f"C5 seq {b} (T={T}): out_maxabs={err:.3g} lse_maxabs={np.max(np.abs(glse[b] - rl)):.3g}")
         assert err <= 2e-3
         assert np.max(np.abs(glse[b] - rl)) <= 1e-4
+
+
+def test_partial_then_merge_equals_fused_call():
+    """iq_decode_attention == iq_decode_attention_partial + _merge, bit for bit."""
+    t = torch()
+    d, bits, hq, hkv, T = 128, 3, 32, 4, 3000
+    case = inputs.decode_case(seed=21, kv_len=T, num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
+    cfg, quats, kc, vc = decode_case_gpu(case, d, bits, O.FULL, hkv)
+    q = t.from_numpy(case["q"][None]).to(DEV)
+    lens = t.full((1,), T, dtype=t.int32, device=DEV)
+    ws = t.empty((B.iq_decode_workspace_bytes(cfg, 1, hq, T),), dtype=t.uint8, device=DEV)
+    outs = []
+    for fused in (True, False):
+        out = t.empty((1, hq, d), dtype=t.float32, device=DEV)
+        lse = t.empty((1, hq), dtype=t.float32, device=DEV)
+        arg = t.empty((1, hq), dtype=t.int32, device=DEV)
+        ws.fill_(0xAB)                              # content on entry must not matter
+        if fused:
+            B.iq_decode_attention(cfg, q, kc, vc, lens, T, scale_for(d), out, lse, arg, ws)
+        else:
+            B.iq_decode_attention_partial(cfg, q, kc, vc, lens, T, scale_for(d), ws)
+            B.iq_decode_attention_merge(cfg, 1, hq, T, out, lse, arg, ws)
+        t.cuda.synchronize()
+        outs.append((out.cpu().numpy(), lse.cpu().numpy(), arg.cpu().numpy()))
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("kscale,vscale", [(1.0, 1000.0), (1.0, 1e-3), (30.0, 1.0), (1e-3, 1e-3)])
+def test_decode_extreme_norms(kscale, vscale):
+    """Key/value norms from ~1e-2 to ~1e4: the softmax weight x ||v|| must stay
+    inside fp16 range on the matrix cores whatever the norms."""
+    d, bits, hq, hkv, T = 128, 3, 8, 1, 1500
+    rng = np.random.default_rng(int(vscale * 7 + kscale))
+    cfg, quats = make_config(d, bits, O.FULL, hkv)
+    k = (rng.standard_normal((1, T, hkv, d)) * kscale).astype(np.float16)
+    v = (rng.standard_normal((1, T, hkv, d)) * vscale).astype(np.float16)
+    v[0, ::7] *= 3                                  # norms spread over the tokens
+    q = rng.standard_normal((1, hq, d)).astype(np.float16)
+    kc = quantize_rows(cfg, k)
+    vc = quantize_rows(cfg, v)
+    got, lse, arg = run_decode(cfg, q, kc, vc, [T], T)
+    ref, rlse, rarg = oracle_decode(q, k, v, quats, cfg, [T], host_cache(kc), host_cache(vc))
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    check_outputs(f"norms k x{kscale} v x{vscale}", got / scale, lse, arg, ref / scale, rlse, rarg, 2e-3 / 4)
