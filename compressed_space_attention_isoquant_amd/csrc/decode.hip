@@ -64,29 +64,108 @@ __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, ui
   return __builtin_bit_cast(half8, u);
 }
 
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource (raw, stride 0) over `bytes` bytes at `base`: loads past the
+// end return zeros instead of touching memory.
+__device__ __forceinline__ int32x4_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  int32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xFFFF);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Asynchronous buffer -> LDS copy: lane i's SIZE bytes at byte offset
+// voff + soff of the buffer land at LDS byte address lds + SIZE * i.  The
+// instruction writes no registers; completion is awaited with wait_vmem.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(int32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4");
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Layout of one wave's LDS stage: 32 packed K rows, 32 packed V rows, 32 K
+// norms, 32 V norms.
+template <int D, int BITS>
+struct Stage {
+  static constexpr int ROWB = D * BITS / 8;
+  static constexpr int ROWS_B = kDecodeStep * ROWB;           // bytes of 32 rows
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = ROWS_B;
+  static constexpr int KN_OFF = 2 * ROWS_B;
+  static constexpr int VN_OFF = 2 * ROWS_B + 2 * kDecodeStep;
+  static constexpr int BYTES = 2 * ROWS_B + 4 * kDecodeStep;   // multiple of 16
+  static constexpr int ROW_LOADS = (ROWS_B + 1023) / 1024;    // 16-byte-per-lane loads per row block
+  static constexpr int LOADS = 2 * ROW_LOADS + 2;             // buffer->LDS loads per stage
+};
+
+// Issue the asynchronous buffer->LDS loads of one 32-token stage starting at
+// token t0 (wave-uniform); stage_lds is the stage's LDS byte address.
+template <int D, int BITS>
+__device__ __forceinline__ void load_stage(uint32_t stage_lds, int32x4_t kr, int32x4_t vr, int32x4_t knr,
+                                           int32x4_t vnr, int t0, int lane) {
+  using S = Stage<D, BITS>;
+  const uint32_t row_off = (uint32_t)__builtin_amdgcn_readfirstlane(t0 * S::ROWB);
+  const uint32_t norm_off = (uint32_t)__builtin_amdgcn_readfirstlane(t0 * 2);
+#pragma unroll
+  for (int c = 0; c < S::ROW_LOADS; ++c) {
+    if (c * 1024 + lane * 16 < S::ROWS_B) {
+      dma_to_lds<16>(kr, stage_lds + S::K_OFF + c * 1024, c * 1024 + lane * 16, row_off);
+      dma_to_lds<16>(vr, stage_lds + S::V_OFF + c * 1024, c * 1024 + lane * 16, row_off);
+    }
+  }
+  if (lane < kDecodeStep / 2) {
+    dma_to_lds<4>(knr, stage_lds + S::KN_OFF, lane * 4, norm_off);
+    dma_to_lds<4>(vnr, stage_lds + S::VN_OFF, lane * 4, norm_off);
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int D, int BITS, int G>
 __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   constexpr int NLEV = 1 << BITS;
   constexpr int KS = D / 32;                 // k-steps of the score product
   constexpr int NB = D / 16;                 // 16-column blocks of the value product
-  constexpr int ROWW = D * BITS / 32;        // dwords per packed row
-  constexpr int CW = ROWW / 4;               // dwords of a row held by one lane group (d/4 dims)
+  constexpr int ROWB = D * BITS / 8;         // bytes per packed row
+  constexpr int CW = ROWB / 16;              // dwords of a row held by one lane group (d/4 dims)
   constexpr int VCB = (D / 16) * BITS;       // bits of the d/16 codes a lane owns in the value product
-  constexpr int VW = (VCB + 31) / 32 + 1;    // dwords loaded to cover them at any bit offset
+  constexpr int VW = (VCB + 31) / 32 + 1;    // dwords read to cover them at any bit offset
   constexpr int VX = (VCB + 31) / 32;        // dwords after extraction
   constexpr int NROW = 2 * G;                // live rows/columns (hi + lo)
+  using S = Stage<D, BITS>;
+  constexpr int PRO_B = G * D * 4;                                  // prologue q~ staging
+  constexpr int STG_B = kDecodeWaves * 2 * S::BYTES;                // double-buffered stages
+  constexpr int RED_B = kDecodeWaves * G * (D + 4) * 4;             // wave states at the end
+  constexpr int MAIN_B = (PRO_B > STG_B ? (PRO_B > RED_B ? PRO_B : RED_B) : (STG_B > RED_B ? STG_B : RED_B));
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int T = a.kv_len[b];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
 
   __shared__ uint32_t lut[NLEV * NLEV];
-  __shared__ float qs[G][D];
-  __shared__ float red_o[kDecodeWaves][G][D];
-  __shared__ float red_h[kDecodeWaves][G][4];
+  __shared__ __attribute__((aligned(16))) char smem[MAIN_B];
+  float (*qs)[D] = reinterpret_cast<float (*)[D]>(smem);
 
   // ---- prologue: q~ = R q for this KV head's query heads --------------------
   for (int i = threadIdx.x; i < NLEV * NLEV; i += kThreads) lut[i] = a.lut[i];
@@ -141,16 +220,19 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
       qB[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
     }
   }
+  __syncthreads();                           // qs is reused as stage memory below
 
   // ---- main loop ---------------------------------------------------------------
   const int sub = a.chunk / kDecodeWaves;
   const int begin = split * a.chunk + wave * sub;
   const int end = min(T, begin + sub);
   const long long hrow = (long long)b * a.hkv + kvh;
-  const uint32_t *kbase = reinterpret_cast<const uint32_t *>(a.kc) + hrow * a.kcap * ROWW;
-  const uint32_t *vbase = reinterpret_cast<const uint32_t *>(a.vc) + hrow * a.vcap * ROWW;
-  const uint16_t *knb = a.kn + hrow * a.kcap;
-  const uint16_t *vnb = a.vn + hrow * a.vcap;
+  const int32x4_t kr = make_rsrc(a.kc + hrow * a.kcap * ROWB, (uint32_t)(a.kcap * ROWB));
+  const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
+  const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
+  const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
+  char *stages = smem + wave * 2 * S::BYTES;
+  const uint32_t stages_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(stages));
   const int my_tile = lo_lane ? 1 : 0;
   const int vbit = VCB * j;                  // bit offset of this lane's codes in a row
 
@@ -160,64 +242,77 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = begin; t0 < end; t0 += kDecodeStep) {
-    const int last = end - 1;
+  if (begin < end) load_stage<D, BITS>(stages_lds, kr, vr, knr, vnr, begin, lane);
+  int it = 0;
+  for (int t0 = begin; t0 < end; t0 += kDecodeStep, ++it) {
+    char *cur = stages + (it & 1) * S::BYTES;
+    if (t0 + kDecodeStep < end) {
+      load_stage<D, BITS>(stages_lds + ((it + 1) & 1) * S::BYTES, kr, vr, knr, vnr, t0 + kDecodeStep, lane);
+      wait_vmem<S::LOADS>();
+    } else {
+      wait_vmem<0>();
+    }
+
     // packed K rows of the two 16-token tiles (lane: token j, dims slice g4)
     uint32_t kw[2][CW];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const int row = min(t0 + 16 * tile + j, last);
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + S::K_OFF + (16 * tile + j) * ROWB) + g4 * CW;
 #pragma unroll
-      for (int i = 0; i < CW; ++i) kw[tile][i] = kbase[(long long)row * ROWW + g4 * CW + i];
+      for (int i = 0; i < CW; ++i) kw[tile][i] = src[i];
     }
     // the 8 tokens this lane holds in the result/operand layouts: 4*g4 + r of each tile
-    float nk[4], nv[4], ev[4];
     uint32_t vch[8][VX];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int tile = r >> 2;
-      const int row = min(t0 + 16 * tile + 4 * g4 + (r & 3), last);
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + S::V_OFF + (16 * (r >> 2) + 4 * g4 + (r & 3)) * ROWB) +
+                            (vbit >> 5);
       uint32_t w[VW];
-      const uint32_t *src = vbase + (long long)row * ROWW + (vbit >> 5);
 #pragma unroll
-      for (int i = 0; i < VW; ++i) w[i] = (vbit >> 5) + i < ROWW ? src[i] : 0u;
+      for (int i = 0; i < VW; ++i) w[i] = src[i];            // may read one dword past the row: still in LDS
 #pragma unroll
       for (int i = 0; i < VX; ++i) vch[r][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], vbit & 31);
-      if (tile == my_tile) {
-        const uint16_t kb = knb[row], vb = vnb[row];
-        nk[r & 3] = half_bits_to_float(kb) * a.kscale;
-        nv[r & 3] = live ? half_bits_to_float(vb) : 0.f;
-        ev[r & 3] = (float)((vb >> 10) & 31);
+    }
+    float nk[4], nv[4], ev[4];
+    {
+      typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+      const u16x4 kb = *reinterpret_cast<const u16x4 *>(cur + S::KN_OFF + (16 * my_tile + 4 * g4) * 2);
+      const u16x4 vb = *reinterpret_cast<const u16x4 *>(cur + S::VN_OFF + (16 * my_tile + 4 * g4) * 2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        nk[r] = half_bits_to_float(kb[r]) * a.kscale;
+        nv[r] = live ? half_bits_to_float(vb[r]) : 0.f;
+        ev[r] = (float)((vb[r] >> 10) & 31);
       }
     }
 
     // scores for both tiles
-    floatx4 S[2];
+    floatx4 S2[2];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      S[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
+      S2[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         uint32_t w4[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) w4[p] = lut[field(kw[tile], (8 * s + 2 * p) * BITS, 2 * BITS)];
-        S[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(w4[0], w4[1], w4[2], w4[3]), qB[s],
-                                                         S[tile], 0, 0, 0);
+        S2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(w4[0], w4[1], w4[2], w4[3]), qB[s],
+                                                          S2[tile], 0, 0, 0);
       }
     }
 
     // softmax on this lane's tile (hi lanes: tile 0, lo lanes: tile 1)
-    float sig[4], u[4];
+    const bool full = t0 + kDecodeStep <= end;
+    float sig[4];
     float umax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float c0 = S[0][r] + xor_g<G>(S[0][r]);
-      const float c1 = S[1][r] + xor_g<G>(S[1][r]);
+      const float c0 = S2[0][r] + xor_g<G>(S2[0][r]);
+      const float c1 = S2[1][r] + xor_g<G>(S2[1][r]);
       const int tok = t0 + 16 * my_tile + 4 * g4 + r;
-      const bool ok = live && tok < end;
+      const bool ok = live && (full || tok < end);
       sig[r] = ok ? (my_tile ? c1 : c0) * nk[r] : -INFINITY;
-      u[r] = sig[r] + ev[r];
-      umax = fmaxf(umax, u[r]);
+      umax = fmaxf(umax, sig[r] + ev[r]);
       if (sig[r] > best_s) {
         best_s = sig[r];
         best_j = tok;
@@ -272,6 +367,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
       O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(w4[0], w4[1], w4[2], w4[3]), O[nb], 0, 0, 0);
     }
   }
+  __syncthreads();                           // stage memory is reused for the wave states below
+  float (*red_o)[G][D + 4] = reinterpret_cast<float (*)[G][D + 4]>(smem);
 
   // ---- wave state -> LDS -----------------------------------------------------------
   // softmax denominator and argmax per head: lanes (head, head + G) x 4 groups
@@ -293,10 +390,10 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
     take(__shfl_xor(bs, 32, 64), __shfl_xor(bj, 32, 64));
   }
   if (lane < G) {
-    red_h[wave][lane][0] = Mh;
-    red_h[wave][lane][1] = lsum;
-    red_h[wave][lane][2] = bs;
-    red_h[wave][lane][3] = __builtin_bit_cast(float, bj);
+    red_o[wave][lane][D + 0] = Mh;
+    red_o[wave][lane][D + 1] = lsum;
+    red_o[wave][lane][D + 2] = bs;
+    red_o[wave][lane][D + 3] = __builtin_bit_cast(float, bj);
   }
   // value rows: hi row h + lo row h + G
 #pragma unroll
@@ -322,18 +419,18 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w)
-      if (red_h[w][hh][1] > 0.f) M = fmaxf(M, red_h[w][hh][0]);
+      if (red_o[w][hh][D + 1] > 0.f) M = fmaxf(M, red_o[w][hh][D]);
     float o = 0.f, L = 0.f, bsc = -INFINITY;
     int bpos = -1;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) {
-      if (red_h[w][hh][1] > 0.f) {
-        const float sc = exp2f(red_h[w][hh][0] - M);
+      if (red_o[w][hh][D + 1] > 0.f) {
+        const float sc = exp2f(red_o[w][hh][D] - M);
         o += red_o[w][hh][i] * sc;
-        L += red_h[w][hh][1] * sc;
-        if (red_h[w][hh][2] > bsc) {
-          bsc = red_h[w][hh][2];
-          bpos = __builtin_bit_cast(int, red_h[w][hh][3]);
+        L += red_o[w][hh][D + 1] * sc;
+        if (red_o[w][hh][D + 2] > bsc) {
+          bsc = red_o[w][hh][D + 2];
+          bpos = __builtin_bit_cast(int, red_o[w][hh][D + 3]);
         }
       }
     }
