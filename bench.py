@@ -126,11 +126,11 @@ def main():
             e0.record(stream)
         # the two phases of iq_decode_attention, so that the events bracket the
         # partial (dominant) kernel alone
-        B.iq_decode_attention_partial(cfg, qs[s % P], kc, vc, kv_len, T, scale, ws)
+        B.iq_decode_attention_partial(cfg, qs[s % P], kc, vc, kv_len, T, scale, ws, track_argmax=False)
         if record:
             e1.record(stream)
             events.append((e0, e1))
-        B.iq_decode_attention_merge(cfg, batch, hq, T, out, lse, arg, ws)
+        B.iq_decode_attention_merge(cfg, batch, hq, T, out, lse, None, ws)
 
     for s in range(args.warmup):
         step(s, False)

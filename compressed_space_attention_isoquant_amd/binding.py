@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.iq_decode_attention.restype = ctypes.c_int
         L.iq_decode_attention_partial.argtypes = [ctypes.POINTER(IQConfigC), P, i32, i32, i32,
                                                   ctypes.POINTER(IQCacheC), ctypes.POINTER(IQCacheC), P,
-                                                  i64, ctypes.c_float, P, ctypes.c_size_t, P]
+                                                  i64, ctypes.c_float, i32, P, ctypes.c_size_t, P]
         L.iq_decode_attention_partial.restype = ctypes.c_int
         L.iq_decode_attention_merge.argtypes = [ctypes.POINTER(IQConfigC), i32, i32, i64, P, i32, P, P,
                                                 P, ctypes.c_size_t, P]
@@ -209,15 +209,16 @@ def iq_decode_attention(cfg: Config, q, k: PackedCache, v: PackedCache, kv_len, 
 
 
 def iq_decode_attention_partial(cfg: Config, q, k: PackedCache, v: PackedCache, kv_len, max_kv_len: int,
-                                softmax_scale: float, workspace, stream=None) -> None:
+                                softmax_scale: float, workspace, track_argmax: bool = True,
+                                stream=None) -> None:
     """Split phase of iq_decode_attention (partial softmax states into workspace)."""
     batch, hq = int(q.shape[0]), int(q.shape[1])
     cc, kc, vc = cfg.c(), k.c(), v.c()
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().iq_decode_attention_partial(ctypes.byref(cc), _ptr(q), _dtype_code(q), batch, hq,
                                              ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_len),
-                                             int(max_kv_len), float(softmax_scale), _ptr(workspace),
-                                             ws_bytes, _stream(stream)))
+                                             int(max_kv_len), float(softmax_scale), int(bool(track_argmax)),
+                                             _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def iq_decode_attention_merge(cfg: Config, batch: int, num_q_heads: int, max_kv_len: int, out,

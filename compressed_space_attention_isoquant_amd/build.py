@@ -22,7 +22,15 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libiq.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "decode.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "decode_128.hip", "decode_256.hip", "decode_512.hip"]
+
+# Matrix-core accumulators kept in the unified VGPR file (no AGPR copies around
+# the value accumulators).  Not for head_dim 512, whose register pressure makes
+# this compiler's AGPR-rewrite pass fail.
+EXTRA = {
+    "decode_128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "decode_256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 # gfx950 only.  Packed-fp32 instruction selection is switched off for device
 # code (the host pass warns that it does not know the feature; harmless).
@@ -43,7 +51,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

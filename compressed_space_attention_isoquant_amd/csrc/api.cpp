@@ -257,7 +257,8 @@ static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_
 int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
                                 int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
                                 const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                                int32_t track_argmax, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
   int group = 0;
   int st = check_decode_common(cfg, batch, num_q_heads, max_kv_len, workspace, workspace_bytes, &group);
   if (st != IQ_OK) return st;
@@ -273,7 +274,6 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
 
   const Geometry geo = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
   const int e = centroid_exponent(cfg);
-  constexpr int qexp = 8;
   iq::DecodeArgs a;
   a.q = q;
   a.q_f16 = q_dtype == IQ_F16;
@@ -292,8 +292,8 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
   a.variant = cfg->variant;
   a.chunk = geo.chunk;
   a.n_split = geo.n_split;
-  a.qmul = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634 * std::ldexp(1.0, qexp - e));
-  a.kscale = std::ldexp(1.0f, -qexp);
+  a.qmul = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634 * std::ldexp(1.0, -e));
+  a.argmax = track_argmax != 0;
   a.ws = static_cast<float *>(workspace);
   std::memset(a.lut, 0, sizeof(a.lut));
   fill_pair_table(cfg, e, a.lut);
@@ -341,7 +341,7 @@ int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, in
   if (!aligned16(out)) return IQ_ERR_MISALIGNED;
   if ((lse_out && !aligned16(lse_out)) || (argmax_out && !aligned16(argmax_out))) return IQ_ERR_MISALIGNED;
   st = iq_decode_attention_partial(cfg, q, q_dtype, batch, num_q_heads, k, v, kv_len, max_kv_len,
-                                   softmax_scale, workspace, workspace_bytes, stream);
+                                   softmax_scale, argmax_out != nullptr, workspace, workspace_bytes, stream);
   if (st != IQ_OK) return st;
   return iq_decode_attention_merge(cfg, batch, num_q_heads, max_kv_len, out, out_dtype, lse_out,
                                    argmax_out, workspace, workspace_bytes, stream);

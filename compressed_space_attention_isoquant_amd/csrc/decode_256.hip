@@ -1,0 +1,15 @@
+// Decode-attention kernels instantiated for head_dim 256 (kernels and their
+// description are in decode_kernels.h).
+#include "decode_kernels.h"
+
+namespace iq {
+
+hipError_t launch_decode_256(int bits, const DecodeArgs &a, hipStream_t s) {
+  return partial_dispatch_bits<256>(bits, a, s);
+}
+
+hipError_t launch_merge_256(int variant, const MergeArgs &a, hipStream_t s) {
+  return merge_dispatch<256>(variant, a, s);
+}
+
+}  // namespace iq

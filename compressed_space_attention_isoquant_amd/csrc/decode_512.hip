@@ -1,0 +1,15 @@
+// Decode-attention kernels instantiated for head_dim 512 (kernels and their
+// description are in decode_kernels.h).
+#include "decode_kernels.h"
+
+namespace iq {
+
+hipError_t launch_decode_512(int bits, const DecodeArgs &a, hipStream_t s) {
+  return partial_dispatch_bits<512>(bits, a, s);
+}
+
+hipError_t launch_merge_512(int variant, const MergeArgs &a, hipStream_t s) {
+  return merge_dispatch<512>(variant, a, s);
+}
+
+}  // namespace iq

@@ -1,0 +1,585 @@
+// Compressed-space decode attention (RotaryQuant §3.4 Table 2, Appendix A),
+// split-K over the context, scores and value accumulation on fp16 matrix
+// cores (v_mfma_f32_16x16x32_f16) directly from the packed codes.
+//
+// partial kernel: one workgroup of 4 waves per (split, KV head, sequence).
+//   Prologue: q~ = R q for the G query heads of the KV head (WHT butterflies
+//   and SO(4) blocks in LDS), scaled, split into fp16 hi + lo parts and held
+//   in registers as the B operand of the score product.
+//   Each wave walks its token range 32 tokens at a time:
+//     scores  S^T (16 tokens x 16 columns) = C_K (16 x d) . Q~^T (d x 16) for
+//             two 16-token tiles; column j < G holds q~_hi of head j, column
+//             G + j holds q~_lo of head j, so S_hi + S_lo is the full-precision
+//             score.  C_K comes from the packed K rows through a 2-code table
+//             of exact fp16 centroid pairs (the codebook has 11 significant
+//             bits, scaled by a power of two).
+//     softmax online, base 2, with a lazily raised running maximum (only
+//             rescaled when a score exceeds it by more than kLazyTau).
+//     values  O~ (16 rows x d) += P (16 x 32 tokens) . C_V (32 x d); row j < G
+//             carries the fp16 hi part of p * ||v|| for head j, row G + j the
+//             lo part, so the fp32 accumulators see the weights to ~2^-22.
+//   The 4 waves merge their states in LDS; the workgroup writes one partial
+//   record (M, L, best score, best position, o~[d]) per query head.
+// merge kernel: one workgroup per (query head, sequence): combines the split
+//   records, divides by the softmax denominator and applies R^T once.
+#pragma once
+
+#include <type_traits>
+
+#include "iq_device.h"
+#include "iq_internal.h"
+
+namespace iq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = kDecodeWaves * 64;
+
+// W-bit field at bit position pos of the little-endian bit string w[].
+template <int N>
+__device__ __forceinline__ uint32_t field(const uint32_t (&w)[N], int pos, int width) {
+  const int wd = pos >> 5, off = pos & 31;
+  uint32_t v = (off + width <= 32 || wd + 1 >= N) ? (w[wd] >> off)
+                                                  : __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off);
+  return v & ((1u << width) - 1u);
+}
+
+// Value of lane (lane ^ G) for the hi/lo partner column.
+template <int G>
+__device__ __forceinline__ float xor_g(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (G == 8)
+    r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);      // row_ror:8 == lane ^ 8
+  else if constexpr (G == 4)
+    r = __builtin_amdgcn_ds_swizzle(x, (4 << 10) | 0x1F);          // lane ^ 4
+  else if constexpr (G == 2)
+    r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);       // quad_perm [2,3,0,1]
+  else
+    r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);       // quad_perm [1,0,3,2]
+  return __builtin_bit_cast(float, r);
+}
+
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  u4 u = {a, b, c, d};
+  return __builtin_bit_cast(half8, u);
+}
+
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource (raw, stride 0) over `bytes` bytes at `base`: loads past the
+// end return zeros instead of touching memory.
+__device__ __forceinline__ int32x4_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  int32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xFFFF);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Asynchronous buffer -> LDS copy: lane i's SIZE bytes at byte offset
+// voff + soff of the buffer land at LDS byte address lds + SIZE * i.  The
+// instruction writes no registers; completion is awaited with wait_vmem.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(int32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4");
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Layout of one wave's LDS stage: 32 packed K rows, 32 packed V rows, 32 K
+// norms, 32 V norms.
+template <int D, int BITS>
+struct Stage {
+  static constexpr int ROWB = D * BITS / 8;
+  static constexpr int ROWS_B = kDecodeStep * ROWB;           // bytes of 32 rows
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = ROWS_B;
+  static constexpr int KN_OFF = 2 * ROWS_B;
+  static constexpr int VN_OFF = 2 * ROWS_B + 2 * kDecodeStep;
+  static constexpr int BYTES = 2 * ROWS_B + 4 * kDecodeStep;   // multiple of 16
+  static constexpr int ROW_LOADS = (ROWS_B + 1023) / 1024;    // 16-byte-per-lane loads per row block
+  static constexpr int LOADS = 2 * ROW_LOADS + 2;             // buffer->LDS loads per stage
+};
+
+// Issue the asynchronous buffer->LDS loads of one 32-token stage starting at
+// token t0 (wave-uniform); stage_lds is the stage's LDS byte address.
+template <int D, int BITS>
+__device__ __forceinline__ void load_stage(uint32_t stage_lds, int32x4_t kr, int32x4_t vr, int32x4_t knr,
+                                           int32x4_t vnr, int t0, int lane) {
+  using S = Stage<D, BITS>;
+  const uint32_t row_off = (uint32_t)__builtin_amdgcn_readfirstlane(t0 * S::ROWB);
+  const uint32_t norm_off = (uint32_t)__builtin_amdgcn_readfirstlane(t0 * 2);
+#pragma unroll
+  for (int c = 0; c < S::ROW_LOADS; ++c) {
+    if (c * 1024 + lane * 16 < S::ROWS_B) {
+      dma_to_lds<16>(kr, stage_lds + S::K_OFF + c * 1024, c * 1024 + lane * 16, row_off);
+      dma_to_lds<16>(vr, stage_lds + S::V_OFF + c * 1024, c * 1024 + lane * 16, row_off);
+    }
+  }
+  if (lane < kDecodeStep / 2) {
+    dma_to_lds<4>(knr, stage_lds + S::KN_OFF, lane * 4, norm_off);
+    dma_to_lds<4>(vnr, stage_lds + S::VN_OFF, lane * 4, norm_off);
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int D, int BITS, int G, bool ARGMAX>
+__global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
+  constexpr int NLEV = 1 << BITS;
+  constexpr int KS = D / 32;                 // k-steps of the score product
+  constexpr int NB = D / 16;                 // 16-column blocks of the value product
+  constexpr int ROWB = D * BITS / 8;         // bytes per packed row
+  constexpr int CW = ROWB / 16;              // dwords of a row held by one lane group (d/4 dims)
+  constexpr int VCB = (D / 16) * BITS;       // bits of the d/16 codes a lane owns in the value product
+  constexpr int VW = (VCB + 31) / 32 + 1;    // dwords read to cover them at any bit offset
+  constexpr int VX = (VCB + 31) / 32;        // dwords after extraction
+  constexpr int NROW = 2 * G;                // live rows/columns (hi + lo)
+  using S = Stage<D, BITS>;
+  constexpr int PRO_B = G * D * 4;                                  // prologue q~ staging
+  constexpr int STG_B = kDecodeWaves * 2 * S::BYTES;                // double-buffered stages
+  constexpr int RED_B = kDecodeWaves * G * (D + 4) * 4;             // wave states at the end
+  constexpr int MAIN_B = (PRO_B > STG_B ? (PRO_B > RED_B ? PRO_B : RED_B) : (STG_B > RED_B ? STG_B : RED_B));
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
+
+  __shared__ uint32_t lut[NLEV * NLEV];
+  __shared__ __attribute__((aligned(16))) char smem[MAIN_B];
+  float (*qs)[D] = reinterpret_cast<float (*)[D]>(smem);
+
+  // ---- prologue: q~ = R q for this KV head's query heads --------------------
+  for (int i = threadIdx.x; i < NLEV * NLEV; i += kThreads) lut[i] = a.lut[i];
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int hh = idx / D, i = idx % D;
+    const size_t off = ((size_t)b * a.hq + kvh * G + hh) * D + i;
+    qs[hh][i] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[off])
+                        : static_cast<const float *>(a.q)[off];
+  }
+  __syncthreads();
+  for (int st = 1; st < D; st <<= 1) {
+    for (int p = threadIdx.x; p < G * D / 2; p += kThreads) {
+      const int hh = p / (D / 2), pp = p % (D / 2);
+      const int i = (pp / st) * 2 * st + (pp % st);
+      const float x0 = qs[hh][i], x1 = qs[hh][i + st];
+      qs[hh][i] = x0 + x1;
+      qs[hh][i + st] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  {
+    const float scale = a.qmul / sqrtf((float)D);
+    const float4 *qg = reinterpret_cast<const float4 *>(a.quats) + (size_t)kvh * (D / 4) * 2;
+    for (int p = threadIdx.x; p < G * D / 4; p += kThreads) {
+      const int hh = p / (D / 4), blk = p % (D / 4);
+      float4 v = make_float4(qs[hh][4 * blk] * scale, qs[hh][4 * blk + 1] * scale,
+                             qs[hh][4 * blk + 2] * scale, qs[hh][4 * blk + 3] * scale);
+      const float4 qL = qg[2 * blk], qR = qg[2 * blk + 1];
+      float4 t = a.variant == 0 ? so4_fwd<0>(v, qL, qR) : so4_fwd<1>(v, qL, qR);
+      qs[hh][4 * blk] = t.x;
+      qs[hh][4 * blk + 1] = t.y;
+      qs[hh][4 * blk + 2] = t.z;
+      qs[hh][4 * blk + 3] = t.w;
+    }
+  }
+  __syncthreads();
+
+  const int j = lane & 15;      // column of the score tile / row of the value operand
+  const int g4 = lane >> 4;     // lane group: k-slice of the operands, row quad of results
+  const bool live = j < NROW;
+  const bool lo_lane = live && j >= G;
+  const int head = j % G;
+
+  // B operand of the score product: lane group g4 covers dims [g4*D/4, (g4+1)*D/4).
+  half8 qB[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = live ? qs[head][g4 * (D / 4) + 8 * s + e] : 0.f;
+      const _Float16 hi = static_cast<_Float16>(v);
+      qB[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
+    }
+  }
+  __syncthreads();                           // qs is reused as stage memory below
+
+  // ---- main loop ---------------------------------------------------------------
+  const int sub = a.chunk / kDecodeWaves;
+  const int begin = split * a.chunk + wave * sub;
+  const int end = min(T, begin + sub);
+  const long long hrow = (long long)b * a.hkv + kvh;
+  const int32x4_t kr = make_rsrc(a.kc + hrow * a.kcap * ROWB, (uint32_t)(a.kcap * ROWB));
+  const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
+  const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
+  const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
+  char *stages = smem + wave * 2 * S::BYTES;
+  const uint32_t stages_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(stages));
+  const int my_tile = lo_lane ? 1 : 0;
+  const int vbit = VCB * j;                  // bit offset of this lane's codes in a row
+  const float lo_mask = lo_lane ? 1.f : 0.f;
+  // per-lane LDS byte offsets inside a stage
+  const int k_off = S::K_OFF + j * ROWB + g4 * CW * 4;
+  const int v_off = S::V_OFF + 4 * g4 * ROWB + (vbit >> 5) * 4;
+  const int n_off = (16 * my_tile + 4 * g4) * 2;
+
+  float Mh = -INFINITY, Mb = -INFINITY, Lh = 0.f, best_s = -INFINITY;
+  int best_j = -1;
+  floatx4 O[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](const char *cur, const int t0, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    // packed K rows of the two 16-token tiles (lane: token j, dims slice g4)
+    uint32_t kw[2][CW];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + k_off + tile * 16 * ROWB);
+#pragma unroll
+      for (int i = 0; i < CW; ++i) kw[tile][i] = src[i];
+    }
+    // the 8 tokens of this lane in the operand/result layouts: 4*g4 + r of each tile
+    uint32_t vch[8][VX];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + v_off + (16 * (r >> 2) + (r & 3)) * ROWB);
+      uint32_t w[VW];
+#pragma unroll
+      for (int i = 0; i < VW; ++i) w[i] = src[i];            // may read one dword past the row: still in LDS
+#pragma unroll
+      for (int i = 0; i < VX; ++i) vch[r][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], vbit & 31);
+    }
+    typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+    const u16x4 kb = *reinterpret_cast<const u16x4 *>(cur + S::KN_OFF + n_off);
+    const u16x4 vb = *reinterpret_cast<const u16x4 *>(cur + S::VN_OFF + n_off);
+
+    // scores for both tiles
+    floatx4 S2[2];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      S2[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) w4[p] = lut[field(kw[tile], (8 * s + 2 * p) * BITS, 2 * BITS)];
+        S2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(w4[0], w4[1], w4[2], w4[3]), qB[s],
+                                                          S2[tile], 0, 0, 0);
+      }
+    }
+
+    // softmax on this lane's tile (hi lanes: tile 0, lo lanes: tile 1).
+    // u = score + an upper bound of the value-norm exponent (byte 1 of its
+    // fp16 bits / 4) drives the running maximum.
+    float sig[4], u[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float own = my_tile ? S2[1][r] : S2[0][r];
+      const float give = my_tile ? S2[0][r] : S2[1][r];      // what the partner lane needs
+      float c = (own + xor_g<G>(give)) * half_bits_to_float(kb[r]);
+      if constexpr (!FULL) {
+        const int tok = t0 + 16 * my_tile + 4 * g4 + r;
+        c = (live && tok < end) ? c : -INFINITY;
+      } else {
+        c = live ? c : -INFINITY;
+      }
+      sig[r] = c;
+      u[r] = fmaf((float)((vb[r] >> 8) & 0xFF), 0.25f, c);
+    }
+    if constexpr (ARGMAX) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (sig[r] > best_s) {
+          best_s = sig[r];
+          best_j = t0 + 16 * my_tile + 4 * g4 + r;
+        }
+      }
+    }
+    const float lmax = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+    if (__any(lmax > Mh + kLazyTau)) {
+      float umax = fmaxf(lmax, xor_g<G>(lmax));
+      umax = fmaxf(umax, __shfl_xor(umax, 16, 64));
+      umax = fmaxf(umax, __shfl_xor(umax, 32, 64));
+      const float mnew = fmaxf(Mh, umax);
+      const float alpha = (Mh == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mh - mnew);
+      Lh *= alpha;
+      Mh = mnew;
+      Mb = mnew - kWeightBias;
+      // rows 4*g4 + i of the value accumulators belong to head (4*g4 + i) % G
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g4 + i;
+        const float ar = __shfl(alpha, row < NROW ? row % G : 0, 64);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) O[nb][i] *= ar;
+      }
+    }
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = __builtin_amdgcn_exp2f(sig[r] - Mb);   // 2^(s - M + bias); 0 for masked tokens
+      Lh += x;
+      y[r] = live ? x * half_bits_to_float(vb[r]) : 0.f;
+    }
+    // A operand, k order = tile-0 tokens 4*g4..+3 then tile-1 tokens; hi lanes
+    // carry fp16(y) (round toward zero), lo lanes the exact remainder.
+    uint32_t pw[4];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      float pa[2], pb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = 2 * q2 + t;
+        const float other = xor_g<G>(y[r]);
+        pa[t] = my_tile ? other : y[r];      // tile 0 token 4*g4 + r
+        pb[t] = my_tile ? y[r] : other;      // tile 1 token 4*g4 + r
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float e0 = half ? pb[0] : pa[0];
+        const float e1 = half ? pb[1] : pa[1];
+        const auto h = __builtin_amdgcn_cvt_pkrtz(e0, e1);
+        const float d0 = fmaf(-lo_mask, static_cast<float>(h[0]), e0);
+        const float d1 = fmaf(-lo_mask, static_cast<float>(h[1]), e1);
+        pw[2 * half + q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(d0, d1));
+      }
+    }
+    const half8 P = as_half8(pw[0], pw[1], pw[2], pw[3]);
+
+    // values: column block nb holds dims (D/16) * n + nb of lane column n = j.
+    // Pair index of tokens (2p, 2p+1) at dim nb: code_a | code_b << BITS.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t c0 = field(vch[2 * p], nb * BITS, BITS);
+        const uint32_t c1 = field(vch[2 * p + 1], nb * BITS, BITS);
+        w4[p] = lut[c0 | (c1 << BITS)];
+      }
+      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(w4[0], w4[1], w4[2], w4[3]), O[nb], 0, 0, 0);
+    }
+  };
+
+  if (begin < end) load_stage<D, BITS>(stages_lds, kr, vr, knr, vnr, begin, lane);
+  int it = 0;
+  for (int t0 = begin; t0 < end; t0 += kDecodeStep, ++it) {
+    const char *cur = stages + (it & 1) * S::BYTES;
+    if (t0 + kDecodeStep < end) {
+      load_stage<D, BITS>(stages_lds + ((it + 1) & 1) * S::BYTES, kr, vr, knr, vnr, t0 + kDecodeStep, lane);
+      wait_vmem<S::LOADS>();
+      process(cur, t0, std::true_type{});
+    } else {
+      wait_vmem<0>();
+      if (t0 + kDecodeStep == end)
+        process(cur, t0, std::true_type{});
+      else
+        process(cur, t0, std::false_type{});
+    }
+  }
+  __syncthreads();                           // stage memory is reused for the wave states below
+  float (*red_o)[G][D + 4] = reinterpret_cast<float (*)[G][D + 4]>(smem);
+
+  // ---- wave state -> LDS -----------------------------------------------------------
+  // softmax denominator and argmax per head: lanes (head, head + G) x 4 groups
+  float lsum = live ? Lh : 0.f;
+  lsum += xor_g<G>(lsum);
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  float bs = live ? best_s : -INFINITY;
+  int bj = live ? best_j : -1;
+  {
+    auto take = [&](float os, int oj) {
+      if (os > bs || (os == bs && oj >= 0 && (bj < 0 || oj < bj))) {
+        bs = os;
+        bj = oj;
+      }
+    };
+    take(xor_g<G>(bs), __builtin_bit_cast(int, xor_g<G>(__builtin_bit_cast(float, bj))));
+    take(__shfl_xor(bs, 16, 64), __shfl_xor(bj, 16, 64));
+    take(__shfl_xor(bs, 32, 64), __shfl_xor(bj, 32, 64));
+  }
+  if (lane < G) {
+    red_o[wave][lane][D + 0] = Mh;
+    red_o[wave][lane][D + 1] = lsum;
+    red_o[wave][lane][D + 2] = bs;
+    red_o[wave][lane][D + 3] = __builtin_bit_cast(float, bj);
+  }
+  // value rows: hi row h + lo row h + G
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = O[nb][i];
+      float partner;
+      if constexpr (G >= 4)
+        partner = __shfl_xor(v, 16 * (G / 4), 64);
+      else
+        partner = O[nb][i ^ G];
+      const int row = 4 * g4 + i;
+      if (row < G) red_o[wave][row][(D / 16) * j + nb] = v + partner;
+    }
+  }
+  __syncthreads();
+
+  // ---- combine the waves, write this split's records ---------------------------------
+  const int n_part = a.n_split;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int hh = idx / D, i = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w)
+      if (red_o[w][hh][D + 1] > 0.f) M = fmaxf(M, red_o[w][hh][D]);
+    float o = 0.f, L = 0.f, bsc = -INFINITY;
+    int bpos = -1;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      if (red_o[w][hh][D + 1] > 0.f) {
+        const float sc = exp2f(red_o[w][hh][D] - M);
+        o += red_o[w][hh][i] * sc;
+        L += red_o[w][hh][D + 1] * sc;
+        if (red_o[w][hh][D + 2] > bsc) {
+          bsc = red_o[w][hh][D + 2];
+          bpos = __builtin_bit_cast(int, red_o[w][hh][D + 3]);
+        }
+      }
+    }
+    float *rec = a.ws + (((size_t)b * a.hq + kvh * G + hh) * n_part + split) * (D + kRecHeader);
+    rec[kRecHeader + i] = o;
+    if (i == 0) {
+      rec[0] = M;
+      rec[1] = L;
+      rec[2] = bsc;
+      rec[3] = __builtin_bit_cast(float, bpos);
+    }
+  }
+}
+
+template <int D, int VARIANT>
+__global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = h / a.group;
+  const int i = threadIdx.x;
+  const float *recs = a.ws + ((size_t)b * a.hq + h) * a.n_part * (D + kRecHeader);
+
+  float M = -INFINITY;
+  for (int p = 0; p < a.n_part; ++p) {
+    const float *rec = recs + (size_t)p * (D + kRecHeader);
+    if (rec[1] > 0.f) M = fmaxf(M, rec[0]);
+  }
+  float L = 0.f, o = 0.f, bsc = -INFINITY;
+  int arg = -1;
+  for (int p = 0; p < a.n_part; ++p) {
+    const float *rec = recs + (size_t)p * (D + kRecHeader);
+    const float lp = rec[1];
+    if (lp > 0.f) {
+      const float w = exp2f(rec[0] - M);
+      L += lp * w;
+      o += rec[kRecHeader + i] * w;
+      if (rec[2] > bsc) {          // strict: ties keep the earlier (lower) positions
+        bsc = rec[2];
+        arg = __builtin_bit_cast(int, rec[3]);
+      }
+    }
+  }
+
+  __shared__ float y[D];
+  y[i] = L > 0.f ? o * a.oscale / L : 0.f;
+  __syncthreads();
+  if (i < D / 4) {
+    const float4 *qg = reinterpret_cast<const float4 *>(a.quats) + (size_t)g * (D / 4) * 2;
+    float4 u = so4_inv<VARIANT>(make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]),
+                                qg[2 * i], qg[2 * i + 1]);
+    y[4 * i] = u.x;
+    y[4 * i + 1] = u.y;
+    y[4 * i + 2] = u.z;
+    y[4 * i + 3] = u.w;
+  }
+  __syncthreads();
+  for (int st = 1; st < D; st <<= 1) {
+    float x0 = 0.f, x1 = 0.f;
+    int lo = 0;
+    if (i < D / 2) {
+      lo = (i / st) * 2 * st + (i % st);
+      x0 = y[lo];
+      x1 = y[lo + st];
+    }
+    __syncthreads();
+    if (i < D / 2) {
+      y[lo] = x0 + x1;
+      y[lo + st] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  const float val = y[i] / sqrtf((float)D);
+  const size_t off = ((size_t)b * a.hq + h) * D + i;
+  if (a.out_f16)
+    static_cast<_Float16 *>(a.out)[off] = static_cast<_Float16>(val);
+  else
+    static_cast<float *>(a.out)[off] = val;
+  if (i == 0) {
+    const size_t oh = (size_t)b * a.hq + h;
+    if (a.lse) a.lse[oh] = L > 0.f ? (M - kWeightBias + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    if (a.argmax) a.argmax[oh] = L > 0.f ? arg : -1;
+  }
+}
+
+template <int D, int BITS, bool ARGMAX>
+hipError_t partial_dispatch_group(const DecodeArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)a.n_split, (unsigned)a.hkv, (unsigned)a.batch);
+  switch (a.group) {
+    case 1: hipLaunchKernelGGL((partial_kernel<D, BITS, 1, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((partial_kernel<D, BITS, 2, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((partial_kernel<D, BITS, 4, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((partial_kernel<D, BITS, 8, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t partial_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
+  switch (bits) {
+    case 2: return a.argmax ? partial_dispatch_group<D, 2, true>(a, s) : partial_dispatch_group<D, 2, false>(a, s);
+    case 3: return a.argmax ? partial_dispatch_group<D, 3, true>(a, s) : partial_dispatch_group<D, 3, false>(a, s);
+    case 4: return a.argmax ? partial_dispatch_group<D, 4, true>(a, s) : partial_dispatch_group<D, 4, false>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t merge_dispatch(int variant, const MergeArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)a.hq, (unsigned)a.batch);
+  if (variant == 0)
+    hipLaunchKernelGGL((merge_kernel<D, 0>), grid, dim3(D), 0, s, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace iq

@@ -63,8 +63,8 @@ struct DecodeArgs {
   int variant;
   int chunk;               // tokens per workgroup (multiple of kDecodeWaves * kDecodeStep)
   int n_split;             // workgroups per (sequence, KV head)
-  float qmul;              // softmax_scale * log2(e) * 2^qexp / 2^cexp, applied to R q
-  float kscale;            // 2^-qexp, applied with the key norm
+  float qmul;              // softmax_scale * log2(e) / 2^cexp, applied to R q
+  int argmax;              // track the position of the largest score
   float *ws;               // records [batch][Hq][n_split][d + kRecHeader]
   uint32_t lut[256];       // fp16 pairs (c_i 2^cexp | c_k 2^cexp << 16) at index i | k << bits
 };

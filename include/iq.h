@@ -159,15 +159,17 @@ int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype,
  * FlashAttention's tiling that RotaryQuant §2 cites): rotates each query once,
  * scores the packed K rows and accumulates the packed V rows in rotated space,
  * and leaves one partial softmax state per (sequence, query head, split) in
- * `workspace`.  Arguments as for iq_decode_attention.  The workspace content
- * is opaque and valid only for a merge call with the same cfg, batch,
- * num_q_heads and max_kv_len. */
+ * `workspace`.  Arguments as for iq_decode_attention; track_argmax != 0 also
+ * records the position of the largest score (otherwise the merge reports -1
+ * as every argmax).  The workspace content is opaque and valid only for a
+ * merge call with the same cfg, batch, num_q_heads and max_kv_len. */
 int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_dtype,
                                 int32_t batch, int32_t num_q_heads,
                                 const iq_cache *k, const iq_cache *v,
                                 const int32_t *kv_len, int64_t max_kv_len,
-                                float softmax_scale, void *workspace,
-                                size_t workspace_bytes, hipStream_t stream);
+                                float softmax_scale, int32_t track_argmax,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* Merge phase: combines the partial states a preceding
  * iq_decode_attention_partial left in `workspace`, divides by the softmax

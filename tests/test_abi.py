@@ -170,11 +170,11 @@ def test_partial_and_merge_validation():
     k = B.IQCacheC(0x4000, 0x5000, 16)
     # partial: misaligned q, small workspace, bad group
     assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2004, 1, 1, 32, ctypes.byref(k), ctypes.byref(k),
-                                         0x8000, 16, 0.1, 0x7000, need, None) == -3
+                                         0x8000, 16, 0.1, 1, 0x7000, need, None) == -3
     assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 32, ctypes.byref(k), ctypes.byref(k),
-                                         0x8000, 16, 0.1, 0x7000, need - 16, None) == -4
+                                         0x8000, 16, 0.1, 1, 0x7000, need - 16, None) == -4
     assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 64, ctypes.byref(k), ctypes.byref(k),
-                                         0x8000, 16, 0.1, 0x7000, need, None) == -2
+                                         0x8000, 16, 0.1, 1, 0x7000, need, None) == -2
     # merge: null out, bad dtype, misaligned argmax
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, None, 0, None, None, 0x7000, need, None) == -1
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 5, None, None, 0x7000, need, None) == -2
