@@ -270,6 +270,10 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
   st = check_cache(v);
   if (st != IQ_OK) return st;
   if (max_kv_len > k->capacity || max_kv_len > v->capacity) return IQ_ERR_INVALID_ARG;
+  // the kernels address one (sequence, head) region of packed rows with 32-bit
+  // offsets and use offsets from 2^30 up as out of range
+  const int64_t rb = int64_t(cfg->head_dim) * cfg->bits / 8;
+  if (k->capacity * rb >= (int64_t(1) << 30) || v->capacity * rb >= (int64_t(1) << 30)) return IQ_ERR_UNSUPPORTED;
   if (!aligned16(q)) return IQ_ERR_MISALIGNED;
 
   const Geometry geo = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);

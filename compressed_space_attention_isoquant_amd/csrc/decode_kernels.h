@@ -25,6 +25,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "iq_device.h"
 #include "iq_internal.h"
@@ -44,6 +45,17 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[N], int pos, int w
   uint32_t v = (off + width <= 32 || wd + 1 >= N) ? (w[wd] >> off)
                                                   : __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off);
   return v & ((1u << width) - 1u);
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1: loop indices that stay
+// constant expressions (bit positions of immediate operands).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Value of lane (lane ^ G) for the hi/lo partner column.
@@ -115,24 +127,32 @@ struct Stage {
   static constexpr int LOADS = 2 * ROW_LOADS + 2;             // buffer->LDS loads per stage
 };
 
+// Byte offset past every cache buffer (the host keeps each (sequence, head)
+// region of packed rows below it): loads there return zeros and touch no
+// memory.
+constexpr uint32_t kOutOfRange = 0x40000000u;
+
 // Issue the asynchronous buffer->LDS loads of one 32-token stage starting at
-// token t0 (wave-uniform); stage_lds is the stage's LDS byte address.
+// token t0 (wave-uniform); stage_lds is the stage's LDS byte address.  The
+// token offset rides in the per-lane offset, which the buffer range check
+// always covers.  A stage that is not needed (valid false) is still issued,
+// pointing out of range, so that every stage counts the same number of loads.
 template <int D, int BITS>
 __device__ __forceinline__ void load_stage(uint32_t stage_lds, int32x4_t kr, int32x4_t vr, int32x4_t knr,
-                                           int32x4_t vnr, int t0, int lane) {
+                                           int32x4_t vnr, int t0, bool valid, int lane) {
   using S = Stage<D, BITS>;
-  const uint32_t row_off = (uint32_t)__builtin_amdgcn_readfirstlane(t0 * S::ROWB);
-  const uint32_t norm_off = (uint32_t)__builtin_amdgcn_readfirstlane(t0 * 2);
+  const uint32_t row_off = valid ? (uint32_t)(t0 * S::ROWB) : kOutOfRange;
+  const uint32_t norm_off = valid ? (uint32_t)(t0 * 2) : kOutOfRange;
 #pragma unroll
   for (int c = 0; c < S::ROW_LOADS; ++c) {
     if (c * 1024 + lane * 16 < S::ROWS_B) {
-      dma_to_lds<16>(kr, stage_lds + S::K_OFF + c * 1024, c * 1024 + lane * 16, row_off);
-      dma_to_lds<16>(vr, stage_lds + S::V_OFF + c * 1024, c * 1024 + lane * 16, row_off);
+      dma_to_lds<16>(kr, stage_lds + S::K_OFF + c * 1024, row_off + c * 1024 + lane * 16, 0);
+      dma_to_lds<16>(vr, stage_lds + S::V_OFF + c * 1024, row_off + c * 1024 + lane * 16, 0);
     }
   }
   if (lane < kDecodeStep / 2) {
-    dma_to_lds<4>(knr, stage_lds + S::KN_OFF, lane * 4, norm_off);
-    dma_to_lds<4>(vnr, stage_lds + S::VN_OFF, lane * 4, norm_off);
+    dma_to_lds<4>(knr, stage_lds + S::KN_OFF, norm_off + lane * 4, 0);
+    dma_to_lds<4>(vnr, stage_lds + S::VN_OFF, norm_off + lane * 4, 0);
   }
 }
 
@@ -141,6 +161,27 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Replicas of the code-pair table in LDS: lane l reads replica l % REPL
+// (entry e at dword e * REPL + l % REPL), so that a wave's table reads fall
+// in distinct banks whatever the codes are.
+template <int BITS>
+constexpr int lut_repl() {
+  return BITS <= 3 ? 32 : 8;
+}
+
+template <int N>
+constexpr int ilog2() {
+  return N <= 1 ? 0 : 1 + ilog2<N / 2>();
+}
+
+// Stages per wave: as many as fit (up to 4) in the LDS two workgroups per CU
+// can hold alongside each other, at least 2 (double buffering).
+template <int D, int BITS>
+constexpr int stage_count() {
+  constexpr int n = (80 * 1024) / (kDecodeWaves * Stage<D, BITS>::BYTES);
+  return n > 4 ? 4 : (n < 2 ? 2 : n);
 }
 
 template <int D, int BITS, int G, bool ARGMAX>
@@ -156,7 +197,9 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   constexpr int NROW = 2 * G;                // live rows/columns (hi + lo)
   using S = Stage<D, BITS>;
   constexpr int PRO_B = G * D * 4;                                  // prologue q~ staging
-  constexpr int STG_B = kDecodeWaves * 2 * S::BYTES;                // double-buffered stages
+  constexpr int NST = stage_count<D, BITS>();
+  static_assert((NST - 1) * S::LOADS < 64, "in-flight loads exceed the vmcnt range");
+  constexpr int STG_B = kDecodeWaves * NST * S::BYTES;              // ring of stages per wave
   constexpr int RED_B = kDecodeWaves * G * (D + 4) * 4;             // wave states at the end
   constexpr int MAIN_B = (PRO_B > STG_B ? (PRO_B > RED_B ? PRO_B : RED_B) : (STG_B > RED_B ? STG_B : RED_B));
 
@@ -167,12 +210,14 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
 
-  __shared__ uint32_t lut[NLEV * NLEV];
+  constexpr int REPL = lut_repl<BITS>();
+  constexpr int LSH = ilog2<REPL * 4>();     // table entry -> byte offset shift
+  __shared__ uint32_t lut[NLEV * NLEV * REPL];
   __shared__ __attribute__((aligned(16))) char smem[MAIN_B];
   float (*qs)[D] = reinterpret_cast<float (*)[D]>(smem);
 
   // ---- prologue: q~ = R q for this KV head's query heads --------------------
-  for (int i = threadIdx.x; i < NLEV * NLEV; i += kThreads) lut[i] = a.lut[i];
+  for (int i = threadIdx.x; i < NLEV * NLEV * REPL; i += kThreads) lut[i] = a.lut[i / REPL];
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int hh = idx / D, i = idx % D;
     const size_t off = ((size_t)b * a.hq + kvh * G + hh) * D + i;
@@ -235,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
   const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
   const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
-  char *stages = smem + wave * 2 * S::BYTES;
+  char *stages = smem + wave * NST * S::BYTES;
   const uint32_t stages_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(stages));
   const int my_tile = lo_lane ? 1 : 0;
   const int vbit = VCB * j;                  // bit offset of this lane's codes in a row
@@ -244,6 +289,21 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   const int k_off = S::K_OFF + j * ROWB + g4 * CW * 4;
   const int v_off = S::V_OFF + 4 * g4 * ROWB + (vbit >> 5) * 4;
   const int n_off = (16 * my_tile + 4 * g4) * 2;
+  // byte address of this lane's replica of table entry 0
+  const uint32_t lut_base = lds_addr(lut) + (uint32_t)(lane % REPL) * 4u;
+  // table entry at the 2*BITS-bit field at bit `pos` of w: bit-field extract
+  // plus one shift-add for the address
+  auto pair = [&](uint32_t w, auto pos) -> uint32_t {
+    uint32_t idx = __builtin_amdgcn_ubfe(w, decltype(pos)::value, 2 * BITS);
+    // The empty asm keeps the extract a v_bfe_u32 followed by one shift-add
+    // (left alone, the compiler folds it into shift, and, add).  It emits no
+    // instruction: a real instruction written in asm here would escape the
+    // compiler's matrix-core hazard tracking (a VALU write to a register an
+    // in-flight MFMA still writes needs wait states that asm does not get).
+    asm("" : "+v"(idx));
+    const uint32_t addr = (idx << LSH) + lut_base;
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
+  };
 
   float Mh = -INFINITY, Mb = -INFINITY, Lh = 0.f, best_s = -INFINITY;
   int best_j = -1;
@@ -281,14 +341,20 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
       S2[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
+      static_for<KS>([&](auto s) {
         uint32_t w4[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) w4[p] = lut[field(kw[tile], (8 * s + 2 * p) * BITS, 2 * BITS)];
+        static_for<4>([&](auto p) {
+          constexpr int W = 2 * BITS;
+          constexpr int pos = (8 * decltype(s)::value + 2 * decltype(p)::value) * BITS;
+          constexpr int wd = pos >> 5, off = pos & 31;
+          if constexpr (off + W <= 32 || wd + 1 >= CW)
+            w4[p] = pair(kw[tile][wd], std::integral_constant<int, off>{});
+          else
+            w4[p] = pair(__builtin_amdgcn_alignbit(kw[tile][wd + 1], kw[tile][wd], off), std::integral_constant<int, 0>{});
+        });
         S2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(w4[0], w4[1], w4[2], w4[3]), qB[s],
                                                           S2[tile], 0, 0, 0);
-      }
+      });
     }
 
     // softmax on this lane's tile (hi lanes: tile 0, lo lanes: tile 1).
@@ -371,34 +437,63 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
 
     // values: column block nb holds dims (D/16) * n + nb of lane column n = j.
     // Pair index of tokens (2p, 2p+1) at dim nb: code_a | code_b << BITS.
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      uint32_t w4[4];
+    if constexpr (VX == 1 && NB == 8) {
+      // Interleave two tokens' fields (SWAR): X[p][parity] holds the pair
+      // indices code_a | code_b << BITS of the dims of that parity at
+      // 2*BITS-bit strides.
+      constexpr uint32_t M = (1u << BITS) - 1u;
+      constexpr uint32_t ME = M | (M << (2 * BITS)) | (M << (4 * BITS)) | (M << (6 * BITS));
+      uint32_t X[4][2];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t c0 = field(vch[2 * p], nb * BITS, BITS);
-        const uint32_t c1 = field(vch[2 * p + 1], nb * BITS, BITS);
-        w4[p] = lut[c0 | (c1 << BITS)];
+        const uint32_t ca = vch[2 * p][0], cb = vch[2 * p + 1][0];
+        X[p][0] = (ca & ME) | ((cb & ME) << BITS);
+        X[p][1] = ((ca >> BITS) & ME) | (cb & (ME << BITS));
       }
-      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(w4[0], w4[1], w4[2], w4[3]), O[nb], 0, 0, 0);
+      static_for<NB>([&](auto nb) {
+        constexpr int sh = (decltype(nb)::value >> 1) * 2 * BITS;
+        uint32_t w4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) w4[p] = pair(X[p][nb & 1], std::integral_constant<int, sh>{});
+        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(w4[0], w4[1], w4[2], w4[3]), O[nb], 0, 0, 0);
+      });
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t c0 = field(vch[2 * p], nb * BITS, BITS);
+          const uint32_t c1 = field(vch[2 * p + 1], nb * BITS, BITS);
+          w4[p] = pair(c0 | (c1 << BITS), std::integral_constant<int, 0>{});
+        }
+        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(w4[0], w4[1], w4[2], w4[3]), O[nb], 0, 0, 0);
+      }
     }
   };
 
-  if (begin < end) load_stage<D, BITS>(stages_lds, kr, vr, knr, vnr, begin, lane);
-  int it = 0;
-  for (int t0 = begin; t0 < end; t0 += kDecodeStep, ++it) {
-    const char *cur = stages + (it & 1) * S::BYTES;
-    if (t0 + kDecodeStep < end) {
-      load_stage<D, BITS>(stages_lds + ((it + 1) & 1) * S::BYTES, kr, vr, knr, vnr, t0 + kDecodeStep, lane);
-      wait_vmem<S::LOADS>();
-      process(cur, t0, std::true_type{});
-    } else {
-      wait_vmem<0>();
-      if (t0 + kDecodeStep == end)
-        process(cur, t0, std::true_type{});
-      else
-        process(cur, t0, std::false_type{});
+  // Ring of NST stages per wave: the next NST - 1 tiles are in flight while
+  // one is processed.  Every iteration issues one stage (out of range past
+  // the wave's last tile), so one fixed wait finds the oldest stage landed.
+  const int n_tiles = end > begin ? (end - begin + kDecodeStep - 1) / kDecodeStep : 0;
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i)
+      load_stage<D, BITS>(stages_lds + i * S::BYTES, kr, vr, knr, vnr, begin + i * kDecodeStep, i < n_tiles, lane);
+    const int n_full = (end - begin) / kDecodeStep;
+    int slot = 0;                            // stage of tile `it`
+    for (int it = 0; it < n_full; ++it) {
+      const int ahead = it + NST - 1;
+      const int aslot = slot == 0 ? NST - 1 : slot - 1;     // (it + NST - 1) mod NST, processed last iteration
+      load_stage<D, BITS>(stages_lds + aslot * S::BYTES, kr, vr, knr, vnr, begin + ahead * kDecodeStep,
+                          ahead < n_tiles, lane);
+      wait_vmem<(NST - 1) * S::LOADS>();
+      process(stages + slot * S::BYTES, begin + it * kDecodeStep, std::true_type{});
+      slot = slot == NST - 1 ? 0 : slot + 1;
     }
+    wait_vmem<0>();                          // also drains the out-of-range stages before LDS is reused
+    if (n_full < n_tiles)                    // the last, partial tile
+      process(stages + slot * S::BYTES, begin + n_full * kDecodeStep, std::false_type{});
   }
   __syncthreads();                           // stage memory is reused for the wave states below
   float (*red_o)[G][D + 4] = reinterpret_cast<float (*)[G][D + 4]>(smem);

@@ -137,7 +137,9 @@ size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch,
  *               token appended this step).  kv_len[b] = 0 gives out = 0,
  *               lse = -inf, argmax = -1.
  *   max_kv_len: HOST upper bound of kv_len, used for the grid only; every
- *               kv_len[b] must be <= max_kv_len (rows beyond it are not read).
+ *               kv_len[b] must be <= max_kv_len (rows at and past kv_len[b]
+ *               do not affect the results).  Each cache's capacity * d*b/8
+ *               must stay below 2^30 bytes (IQ_ERR_UNSUPPORTED otherwise).
  *   softmax_scale: multiplies q.k (1/sqrt(d) in Appendix A).
  *   out:        [batch][Hq][d] of out_dtype, in the original (un-rotated)
  *               domain.
