@@ -1,22 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the IsoQuant packed-KV decode step on one MI355X.
 
-Workload (fp16 I/O, synthetic): 64 independent sequences at 32,768 tokens of
-context, 32 query heads / 4 KV heads (GQA 8:1), head_dim 128, 3-bit
-IsoQuant-Full codes for K and V (838.9 MB of packed KV).  One step = quantize
-and append one new K and one new V vector per sequence and KV head (into the
-last row, so every step attends over exactly 32,768 rows), then decode
-attention for the 32 query heads of every sequence over the packed caches.
+Headline workload (the batched decode-with-append configuration, synthetic):
+64 sequences whose context lengths are drawn uniformly from [1,024, 32,768]
+(seeded), 16 query heads / 8 KV heads (GQA 2:1), head_dim 256, 3-bit
+IsoQuant-Fast codes for K and V, fp16 I/O.  One step = quantize and append one
+new K and one new V vector per sequence and KV head at the end of its context,
+then decode attention for every query head over the packed caches (the
+sequences grow by one token per step).  100 steps are timed by default.
 
-Prints one JSON line: value = packed-KV bytes the step's attention reads per
-second of step time (GB/s), plus the dominant kernel's roofline, the stage-1
-quantize/dequantize rates on 2^20 vectors (d=128, 3-bit, Full, fp16), and the
-FP64 oracle timed on the host as a baseline.
+Prints one JSON line: value = packed-KV (+ q, o) bytes the steps' attention
+reads and writes per second of step time (GB/s); the dominant kernel's
+roofline (its algorithmic bytes per launch over its average launch time,
+measured with HIP events on its stream); stage-1 quantize / dequantize rates
+over the whole d x bits x variant x dtype sweep on 2^20 unit vectors; a
+supplementary uniform 32K-context run (64 sequences, 32/4 heads, d=128,
+3-bit Full); and the FP64 oracle timed on the host as a baseline.
+
+  --calibrate-copy  also runs one plain device-to-device copy of 256 MiB first
+                    (the reference kernel for scaling the HBM byte counters).
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -29,71 +37,233 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 256 << 20
 
-WORKLOAD = dict(batch=64, kv_len=32768, num_q_heads=32, num_kv_heads=4, head_dim=128, bits=3,
-                variant="full")
+HEADLINE = dict(batch=64, len_lo=1024, len_hi=32768, num_q_heads=16, num_kv_heads=8, head_dim=256, bits=3,
+                variant="fast", length_seed=45)
+UNIFORM_32K = dict(batch=64, kv_len=32768, num_q_heads=32, num_kv_heads=4, head_dim=128, bits=3,
+                   variant="full")
+
+# Sources of the decode kernel; HBM counter readings recorded for it are
+# reported only while these are unchanged.
+KERNEL_SOURCES = ["compressed_space_attention_isoquant_amd/csrc/decode_kernels.h",
+                  "compressed_space_attention_isoquant_amd/csrc/decode_256.hip",
+                  "compressed_space_attention_isoquant_amd/csrc/decode_128.hip",
+                  "compressed_space_attention_isoquant_amd/csrc/iq_internal.h",
+                  "compressed_space_attention_isoquant_amd/csrc/api.cpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_hbm_traffic.json")
 
 
-def packed_row_bytes(d, bits):
+def row_bytes(d, bits):
     return d * bits // 8
 
 
-def kv_bytes(w):
-    """Every packed K and V row and its fp16 norm, read once."""
-    rows = w["batch"] * w["num_kv_heads"] * w["kv_len"]
-    return rows * 2 * (packed_row_bytes(w["head_dim"], w["bits"]) + 2)
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def attention_bytes(w):
-    """Algorithmic HBM bytes of one decode attention: the packed K/V with
-    norms, q read (fp16) and o written (fp16)."""
-    return kv_bytes(w) + 2 * w["batch"] * w["num_q_heads"] * w["head_dim"] * 2
-
-
-def partial_bytes(w):
-    """Algorithmic HBM bytes of the split (partial) kernel: packed K/V with
-    norms and q (fp16).  Its partial states are O(splits x d) per head and not
-    counted."""
-    return kv_bytes(w) + w["batch"] * w["num_q_heads"] * w["head_dim"] * 2
-
-
-def append_bytes(w):
-    """Two quantize-appends per step: fp16 vectors in, packed rows + norms out."""
-    n = w["batch"] * w["num_kv_heads"]
-    return 2 * n * (w["head_dim"] * 2 + packed_row_bytes(w["head_dim"], w["bits"]) + 2)
+def recorded_traffic(workload_name):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload_name)
+    if not entry or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
-                          "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark measures one GPU only; runs on several GPUs are not "
+                                   "part of it", "n_gpus": args.gpus}))
         return 2
 
     import torch
 
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        a = torch.empty((COPY_BYTES,), dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    head = run_headline(torch, dev, args)
+    extras = {}
+    if not args.no_extras:
+        extras["uniform_32k"] = run_uniform_32k(torch, dev, max(10, args.steps // 5), args.warmup)
+        extras["stage1"] = run_stage1(torch, dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head["lengths"], args.cpu_seconds)
+
+    w = HEADLINE
+    traffic = recorded_traffic("headline")
+    result = {
+        "metric": "packed-KV decode-attn GB/s (% HBM peak) at 32K ctx; quantize Mvec/s",
+        "value": round(head["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16/f32",
+        "data": "synthetic (seeded torch/NumPy draws: N(0,1) K/V with 4 x10 outlier channels per head, "
+                "N(0,1) queries, context lengths uniform in [1024, 32768])",
+        "config": {
+            "workload": "batched decode with append: 64 sequences, context lengths uniform in [1024, 32768] "
+                        "(+1 per step), 16 query heads / 8 KV heads, head_dim 256, 3-bit IsoQuant-Fast, fp16 I/O; "
+                        "each step quantize+append one K/V token per sequence, then attend",
+            "batch": w["batch"], "num_q_heads": w["num_q_heads"], "num_kv_heads": w["num_kv_heads"],
+            "head_dim": w["head_dim"], "bits": w["bits"], "variant": w["variant"],
+            "mean_kv_len": round(float(np.mean(head["lengths"])), 1),
+            "attention_bytes_per_step": int(head["attn_bytes_per_step"]),
+        },
+        "pct_hbm_peak": round(100.0 * head["value"] / HBM_PEAK_GBS, 2),
+        "partial_kernel_ms": round(head["partial_ms"], 5),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["achieved"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": f"partial_kernel<{w['head_dim']},{w['bits']},{w['num_q_heads'] // w['num_kv_heads']}> "
+                      "(split-K decode over packed K/V)",
+            "algorithmic_bytes_per_launch": int(head["partial_bytes_per_launch"]),
+        },
+        "cpu_baseline": cpu,
+    }
+    result.update(extras)
+    print(json.dumps(result))
+    return 0
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def run_headline(torch, dev, args):
     from compressed_space_attention_isoquant_amd import binding as B
     from compressed_space_attention_isoquant_amd import inputs
 
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    w = dict(WORKLOAD)
-    batch, T, hq, hkv, d, bits = (w[k] for k in ("batch", "kv_len", "num_q_heads", "num_kv_heads",
-                                                 "head_dim", "bits"))
-    variant = B.IQ_FULL
+    w = HEADLINE
+    batch, hq, hkv, d, bits = (w[k] for k in ("batch", "num_q_heads", "num_kv_heads", "head_dim", "bits"))
+    lengths = inputs.batch_lengths(w["length_seed"], batch, w["len_lo"], w["len_hi"])
+    n_total = args.warmup + args.steps
+    cap = int(lengths.max()) + n_total
     quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
-    cfg = B.Config(d, bits, variant, hkv, quats, B.iq_codebook(bits, d))
-    rng = np.random.default_rng(4)
+    cfg = B.Config(d, bits, B.IQ_FAST, hkv, quats, B.iq_codebook(bits, d))
+    rng = np.random.default_rng(46)
     ch_k = inputs.outlier_channels(rng, hkv, d)
     ch_v = inputs.outlier_channels(rng, hkv, d)
 
-    # ---- set-up: prefill caches with T-1 tokens per sequence (not timed) ----
+    # ---- set-up (not timed): fill every cache row with quantized tokens ----
+    kc = B.new_cache(batch, hkv, cap, d, bits, dev)
+    vc = B.new_cache(batch, hkv, cap, d, bits, dev)
+    sb, st = 8, 4096
+    for cache, idx, ch in ((kc, 0, ch_k), (vc, 1, ch_v)):
+        for b0 in range(0, batch, sb):
+            sub = B.PackedCache(cache.codes[b0:b0 + sb], cache.norms[b0:b0 + sb])
+            for t0 in range(0, cap, st):
+                nt = min(st, cap - t0)
+                x = inputs.device_kv(47 + idx, (b0 // sb) * 1000 + t0 // st, sb * nt, ch, d, dev)
+                pos = torch.full((sb,), t0, dtype=torch.int32, device=dev)
+                B.iq_quantize_append(cfg, x.view(sb, nt, hkv, d), pos, sub)
+                del x
+    torch.cuda.synchronize()
+    P = 8   # distinct new-token / query draws cycled over the steps
+    knew = [inputs.device_kv(48, s, batch, ch_k, d, dev).view(batch, 1, hkv, d) for s in range(P)]
+    vnew = [inputs.device_kv(49, s, batch, ch_v, d, dev).view(batch, 1, hkv, d) for s in range(P)]
+    qs = [inputs.device_normal(50, s, (batch, hq, d), dev, torch.float16) for s in range(P)]
+    lens = lengths.astype(np.int64)
+    pos_dev = [torch.from_numpy((lens - 1 + g).astype(np.int32)).to(dev) for g in range(n_total)]
+    len_dev = [torch.from_numpy((lens + g).astype(np.int32)).to(dev) for g in range(n_total)]
+    max_len = [int(lens.max()) + g for g in range(n_total)]
+    out = torch.empty((batch, hq, d), dtype=torch.float16, device=dev)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    ws = torch.empty((B.iq_decode_workspace_bytes(cfg, batch, hq, max(max_len)),), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+    rb = row_bytes(d, bits)
+    events = []
+
+    def step(g, record):
+        s = g % P
+        B.iq_quantize_append(cfg, knew[s], pos_dev[g], kc)
+        B.iq_quantize_append(cfg, vnew[s], pos_dev[g], vc)
+        if record:
+            e0, e1 = _events(torch)
+            e0.record(stream)
+        # the two phases of iq_decode_attention, so that the events bracket the
+        # partial (dominant) kernel alone
+        B.iq_decode_attention_partial(cfg, qs[s], kc, vc, len_dev[g], max_len[g], scale, ws, track_argmax=False)
+        if record:
+            e1.record(stream)
+            events.append((e0, e1))
+        B.iq_decode_attention_merge(cfg, batch, hq, max_len[g], out, lse, None, ws)
+
+    for g in range(args.warmup):
+        step(g, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in range(args.warmup, n_total):
+        step(g, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    kv = np.array([float((lens + g).sum()) * hkv * 2 * (rb + 2) for g in range(args.warmup, n_total)])
+    qo = batch * hq * d * 2
+    attn_bytes = kv + 2 * qo                 # packed K/V with norms read, q read, o written
+    partial_bytes = kv + qo                  # the split kernel reads K/V and q; its partial states are O(splits*d)
+    value = attn_bytes.sum() / (t1 - t0) / 1e9
+    achieved = partial_bytes.mean() / (partial_ms * 1e-3) / 1e9
+    print(f"[bench] headline step {ms_per_step:.4f} ms, partial kernel {partial_ms:.4f} ms, "
+          f"{achieved:.1f} GB/s", file=sys.stderr, flush=True)
+    return dict(value=value, ms_per_step=ms_per_step, partial_ms=partial_ms, achieved=achieved,
+                attn_bytes_per_step=attn_bytes.mean(), partial_bytes_per_launch=partial_bytes.mean(),
+                lengths=lens)
+
+
+def run_uniform_32k(torch, dev, steps, warmup):
+    """Supplementary: 64 sequences at exactly 32,768 tokens, 32 query / 4 KV
+    heads, d=128, 3-bit Full (the long-context head layout, batched to fill
+    the GPU).  Each step appends into the last row, so every step attends over
+    32,768 rows."""
+    from compressed_space_attention_isoquant_amd import binding as B
+    from compressed_space_attention_isoquant_amd import inputs
+
+    w = UNIFORM_32K
+    batch, T, hq, hkv, d, bits = (w[k] for k in ("batch", "kv_len", "num_q_heads", "num_kv_heads",
+                                                 "head_dim", "bits"))
+    quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
+    cfg = B.Config(d, bits, B.IQ_FULL, hkv, quats, B.iq_codebook(bits, d))
+    rng = np.random.default_rng(4)
+    ch_k = inputs.outlier_channels(rng, hkv, d)
+    ch_v = inputs.outlier_channels(rng, hkv, d)
     kc = B.new_cache(batch, hkv, T, d, bits, dev)
     vc = B.new_cache(batch, hkv, T, d, bits, dev)
     zero = torch.zeros((batch,), dtype=torch.int32, device=dev)
@@ -102,7 +272,7 @@ def main():
         B.iq_quantize_append(cfg, x, zero, cache)
         del x
     torch.cuda.synchronize()
-    P = 8   # distinct new-token / query draws cycled over the steps
+    P = 8
     knew = [inputs.device_kv(41, s, batch, ch_k, d, dev).view(batch, 1, hkv, d) for s in range(P)]
     vnew = [inputs.device_kv(42, s, batch, ch_v, d, dev).view(batch, 1, hkv, d) for s in range(P)]
     qs = [inputs.device_normal(43, s, (batch, hq, d), dev, torch.float16) for s in range(P)]
@@ -110,152 +280,131 @@ def main():
     kv_len = torch.full((batch,), T, dtype=torch.int32, device=dev)
     out = torch.empty((batch, hq, d), dtype=torch.float16, device=dev)
     lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
-    arg = torch.empty((batch, hq), dtype=torch.int32, device=dev)
     ws = torch.empty((B.iq_decode_workspace_bytes(cfg, batch, hq, T),), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream()
-
     events = []
 
     def step(s, record):
         B.iq_quantize_append(cfg, knew[s % P], last, kc)
         B.iq_quantize_append(cfg, vnew[s % P], last, vc)
         if record:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+            e0, e1 = _events(torch)
             e0.record(stream)
-        # the two phases of iq_decode_attention, so that the events bracket the
-        # partial (dominant) kernel alone
         B.iq_decode_attention_partial(cfg, qs[s % P], kc, vc, kv_len, T, scale, ws, track_argmax=False)
         if record:
             e1.record(stream)
             events.append((e0, e1))
         B.iq_decode_attention_merge(cfg, batch, hq, T, out, lse, None, ws)
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         step(s, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(s, True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
-    print(f"[bench] decode step {ms_per_step:.4f} ms, partial kernel {attn_ms:.4f} ms", file=sys.stderr, flush=True)
+    ms = (t1 - t0) * 1e3 / steps
+    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    kv = batch * hkv * T * 2 * (row_bytes(d, bits) + 2)
+    qo = batch * hq * d * 2
+    achieved = (kv + qo) / (partial_ms * 1e-3) / 1e9
+    print(f"[bench] uniform 32K step {ms:.4f} ms, partial kernel {partial_ms:.4f} ms, {achieved:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    return {"workload": "64 sequences x 32768 tokens, 32 query / 4 KV heads, d=128, 3-bit IsoQuant-Full, fp16 I/O",
+            "steps": steps, "ms_per_step": round(ms, 5), "value": round((kv + 2 * qo) / (ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s", "partial_kernel_ms": round(partial_ms, 5),
+            "partial_achieved_gbs": round(achieved, 2), "frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("uniform_32k")}
 
-    abytes = attention_bytes(w)
-    step_bytes = abytes + append_bytes(w)
-    value = abytes / (ms_per_step * 1e-3) / 1e9
-    achieved = partial_bytes(w) / (attn_ms * 1e-3) / 1e9
 
-    # ---- stage-1 rates: 2^20 vectors, d=128, 3-bit, Full, fp16 I/O ----------
+def run_stage1(torch, dev):
+    """Quantize / dequantize rates on 2^20 unit vectors for every setting of
+    the stage-1 sweep (d x bits x variant x I/O dtype)."""
+    from compressed_space_attention_isoquant_amd import binding as B
+    from compressed_space_attention_isoquant_amd import inputs
+
     n = 1 << 20
-    cfg1 = B.Config(d, bits, variant, 1, quats[:1].contiguous(), B.iq_codebook(bits, d))
-    x1 = inputs.device_unit_vectors(2, n, d, dev, torch.float16).view(1, n, 1, d)
-    c1 = B.new_cache(1, 1, n, d, bits, dev)
-    o1 = torch.empty_like(x1)
-    sp1 = torch.zeros((1,), dtype=torch.int32, device=dev)
-    for _ in range(3):
-        B.iq_quantize_append(cfg1, x1, sp1, c1)
-        B.iq_dequantize(cfg1, c1, sp1, n, o1)
-    reps = 20
-    eq = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    eq[0].record(stream)
-    for _ in range(reps):
-        B.iq_quantize_append(cfg1, x1, sp1, c1)
-    eq[1].record(stream)
-    for _ in range(reps):
-        B.iq_dequantize(cfg1, c1, sp1, n, o1)
-    eq[2].record(stream)
-    torch.cuda.synchronize()
-    q_ms = eq[0].elapsed_time(eq[1]) / reps
-    dq_ms = eq[1].elapsed_time(eq[2]) / reps
-    row = packed_row_bytes(d, bits)
-    stage1 = {
-        "quantize_mvec_s": n / (q_ms * 1e-3) / 1e6,
-        "quantize_gbs": n * (2 * d + row + 2) / (q_ms * 1e-3) / 1e9,
-        "dequantize_mvec_s": n / (dq_ms * 1e-3) / 1e6,
-        "dequantize_gbs": n * (2 * d + row + 2) / (dq_ms * 1e-3) / 1e9,
-        "workload": "2^20 unit vectors, d=128, 3-bit, IsoQuant-Full, fp16 in/out",
-    }
-    print(f"[bench] stage-1 quantize {q_ms:.4f} ms, dequantize {dq_ms:.4f} ms", file=sys.stderr, flush=True)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, ch_k, ch_v, args.cpu_seconds)
-
-    result = {
-        "metric": "packed-KV decode-attn GB/s (% HBM peak) at 32K ctx; quantize Mvec/s",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded torch/NumPy draws: N(0,1) K/V with 4 x10 outlier channels per head)",
-        "config": {
-            "workload": "decode step: append 1 K + 1 V token per sequence, then attention over packed "
-                        "3-bit K/V; 64 seqs x 32768 ctx, Hq=32, H_kv=4, d=128, IsoQuant-Full, fp16 I/O",
-            "batch": batch, "kv_len": T, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
-            "bits": bits, "variant": "full", "packed_kv_bytes_per_step": abytes,
-            "step_bytes": step_bytes,
-        },
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "partial_kernel_ms": round(attn_ms, 5),
-        "stage1": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in stage1.items()},
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "partial_kernel<128,3,8> (split-K decode over packed K/V)",
-        },
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(result))
-    return 0
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for d in (128, 256, 512):
+        quats = torch.from_numpy(inputs.quaternions(1, d)).to(dev)
+        for bits in (2, 3, 4):
+            for variant, vname in ((B.IQ_FULL, "full"), (B.IQ_FAST, "fast")):
+                cfg = B.Config(d, bits, variant, 1, quats, B.iq_codebook(bits, d))
+                c1 = B.new_cache(1, 1, n, d, bits, dev)
+                sp = torch.zeros((1,), dtype=torch.int32, device=dev)
+                for dt, dname in ((torch.float16, "fp16"), (torch.float32, "fp32")):
+                    x = inputs.device_unit_vectors(2, n, d, dev, dt).view(1, n, 1, d)
+                    o = torch.empty_like(x)
+                    B.iq_quantize_append(cfg, x, sp, c1)
+                    B.iq_dequantize(cfg, c1, sp, n, o)
+                    reps = 10
+                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                    ev[0].record(stream)
+                    for _ in range(reps):
+                        B.iq_quantize_append(cfg, x, sp, c1)
+                    ev[1].record(stream)
+                    for _ in range(reps):
+                        B.iq_dequantize(cfg, c1, sp, n, o)
+                    ev[2].record(stream)
+                    torch.cuda.synchronize()
+                    qms = ev[0].elapsed_time(ev[1]) / reps
+                    dms = ev[1].elapsed_time(ev[2]) / reps
+                    io = n * (d * x.element_size() + row_bytes(d, bits) + 2)
+                    rates[f"d{d}_b{bits}_{vname}_{dname}"] = {
+                        "quantize_mvec_s": round(n / (qms * 1e-3) / 1e6, 1),
+                        "dequantize_mvec_s": round(n / (dms * 1e-3) / 1e6, 1),
+                        "quantize_gbs": round(io / (qms * 1e-3) / 1e9, 1),
+                        "dequantize_gbs": round(io / (dms * 1e-3) / 1e9, 1)}
+                    del x, o
+                del c1
+    head = rates["d128_b3_full_fp16"]
+    print(f"[bench] stage-1 d=128 b=3 Full fp16: quantize {head['quantize_mvec_s']} Mvec/s, "
+          f"dequantize {head['dequantize_mvec_s']} Mvec/s", file=sys.stderr, flush=True)
+    return {"workload": "2^20 unit vectors per setting, d in {128,256,512} x bits in {2,3,4} x "
+                        "{Full,Fast} x {fp16,fp32} I/O", "rates": rates}
 
 
-def cpu_baseline(w, ch_k, ch_v, seconds):
-    """The FP64 oracle's dequantize-then-attend on a bounded sample of the same
-    workload: one (sequence, KV head) pair at the full context with its 8 query
-    heads, repeated for about ``seconds`` of host time."""
+def cpu_baseline(lengths, seconds):
+    """The FP64 oracle's dequantize-then-attend on a bounded sample of the
+    headline workload: one (sequence, KV head) pair at the median context
+    length with its query heads, repeated for about ``seconds`` of host
+    time.  Single-threaded NumPy."""
     import oracle as O
     from compressed_space_attention_isoquant_amd import inputs
 
-    d, bits, T = w["head_dim"], w["bits"], w["kv_len"]
+    w = HEADLINE
+    d, bits = w["head_dim"], w["bits"]
+    T = int(np.median(lengths))
     group = w["num_q_heads"] // w["num_kv_heads"]
     rng = np.random.default_rng(44)
+    ch = inputs.outlier_channels(rng, 1, d)[0]
     k = rng.standard_normal((T, d))
     v = rng.standard_normal((T, d))
-    k[:, ch_k[0]] *= inputs.OUTLIER_SCALE
-    v[:, ch_v[0]] *= inputs.OUTLIER_SCALE
+    k[:, ch] *= inputs.OUTLIER_SCALE
+    v[:, ch] *= inputs.OUTLIER_SCALE
     k, v = k.astype(np.float16), v.astype(np.float16)
     q = rng.standard_normal((group, d)).astype(np.float16)
-    quats = inputs.quaternions(w["num_kv_heads"], d)[:1]
+    quats = inputs.quaternions(1, d)
     cb = O.codebook(bits, d)
-    rk = O.quantize(k, quats[0], cb, O.FULL)
-    rv = O.quantize(v, quats[0], cb, O.FULL)
+    rk = O.quantize(k, quats[0], cb, O.FAST)
+    rv = O.quantize(v, quats[0], cb, O.FAST)
     kr, kn = O.pack(rk["codes"], bits)[None], rk["norm16"][None]
     vr, vn = O.pack(rv["codes"], bits)[None], rv["norm16"][None]
     reps, t0 = 0, time.perf_counter()
     while True:
-        O.attend(q, kr, kn, vr, vn, quats, cb, bits, O.FULL, 1.0 / math.sqrt(d))
+        O.attend(q, kr, kn, vr, vn, quats, cb, bits, O.FAST, 1.0 / math.sqrt(d))
         reps += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = (time.perf_counter() - t0) / reps
-    nbytes = T * 2 * (packed_row_bytes(d, bits) + 2)
+    nbytes = T * 2 * (row_bytes(d, bits) + 2)
     return {"value": round(nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one (sequence, KV head) pair: {T} packed K/V rows, {group} query heads, "
-                      f"{reps} repetitions, {dt:.3f} s each (single-threaded NumPy FP64)"}
+            "sample": f"one (sequence, KV head) pair of the headline workload at the median context "
+                      f"length {T}: {T} packed K/V rows, {group} query heads, d={d}, {reps} repetitions, "
+                      f"{dt:.3f} s each (single-threaded NumPy FP64)"}
 
 
 if __name__ == "__main__":

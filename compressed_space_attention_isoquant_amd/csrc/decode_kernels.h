@@ -176,11 +176,13 @@ constexpr int ilog2() {
   return N <= 1 ? 0 : 1 + ilog2<N / 2>();
 }
 
-// Stages per wave: as many as fit (up to 4) in the LDS two workgroups per CU
-// can hold alongside each other, at least 2 (double buffering).
+// Stages per wave: as many as fit (up to 4) in the LDS that two workgroups
+// per CU can hold alongside each other next to their pair tables, at least 2
+// (double buffering).
 template <int D, int BITS>
 constexpr int stage_count() {
-  constexpr int n = (80 * 1024) / (kDecodeWaves * Stage<D, BITS>::BYTES);
+  constexpr int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
+  constexpr int n = (80 * 1024 - table) / (kDecodeWaves * Stage<D, BITS>::BYTES);
   return n > 4 ? 4 : (n < 2 ? 2 : n);
 }
 
@@ -336,25 +338,68 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
     const u16x4 kb = *reinterpret_cast<const u16x4 *>(cur + S::KN_OFF + n_off);
     const u16x4 vb = *reinterpret_cast<const u16x4 *>(cur + S::VN_OFF + n_off);
 
-    // scores for both tiles
-    floatx4 S2[2];
+    // Table reads for both operands are issued up front, so that their LDS
+    // latency overlaps the score products and the softmax.
+    // K operand: lane (token j, dims slice g4), k-step s holds dims 8s..8s+7
+    // of the slice as 4 code pairs.
+    uint32_t ka[2][KS][4];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      S2[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
       static_for<KS>([&](auto s) {
-        uint32_t w4[4];
         static_for<4>([&](auto p) {
           constexpr int W = 2 * BITS;
           constexpr int pos = (8 * decltype(s)::value + 2 * decltype(p)::value) * BITS;
           constexpr int wd = pos >> 5, off = pos & 31;
           if constexpr (off + W <= 32 || wd + 1 >= CW)
-            w4[p] = pair(kw[tile][wd], std::integral_constant<int, off>{});
+            ka[tile][s][p] = pair(kw[tile][wd], std::integral_constant<int, off>{});
           else
-            w4[p] = pair(__builtin_amdgcn_alignbit(kw[tile][wd + 1], kw[tile][wd], off), std::integral_constant<int, 0>{});
+            ka[tile][s][p] = pair(__builtin_amdgcn_alignbit(kw[tile][wd + 1], kw[tile][wd], off),
+                                  std::integral_constant<int, 0>{});
         });
-        S2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(w4[0], w4[1], w4[2], w4[3]), qB[s],
-                                                          S2[tile], 0, 0, 0);
       });
+    }
+    // V operand: column block nb holds dims (D/16) * n + nb of lane column
+    // n = j; dword p is the pair of tokens (2p, 2p+1) of the lane's 8
+    // (code_a | code_b << BITS).
+    uint32_t vbw[NB][4];
+    if constexpr (VX == 1 && NB == 8) {
+      // Interleave two tokens' fields (SWAR): X[p][parity] holds the pair
+      // indices of the dims of that parity at 2*BITS-bit strides.
+      constexpr uint32_t M = (1u << BITS) - 1u;
+      constexpr uint32_t ME = M | (M << (2 * BITS)) | (M << (4 * BITS)) | (M << (6 * BITS));
+      uint32_t X[4][2];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t ca = vch[2 * p][0], cb = vch[2 * p + 1][0];
+        X[p][0] = (ca & ME) | ((cb & ME) << BITS);
+        X[p][1] = ((ca >> BITS) & ME) | (cb & (ME << BITS));
+      }
+      static_for<NB>([&](auto nb) {
+        constexpr int sh = (decltype(nb)::value >> 1) * 2 * BITS;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) vbw[nb][p] = pair(X[p][nb & 1], std::integral_constant<int, sh>{});
+      });
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t c0 = field(vch[2 * p], nb * BITS, BITS);
+          const uint32_t c1 = field(vch[2 * p + 1], nb * BITS, BITS);
+          vbw[nb][p] = pair(c0 | (c1 << BITS), std::integral_constant<int, 0>{});
+        }
+      }
+    }
+
+    // scores for both tiles
+    floatx4 S2[2];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      S2[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        S2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            as_half8(ka[tile][s][0], ka[tile][s][1], ka[tile][s][2], ka[tile][s][3]), qB[s], S2[tile], 0, 0, 0);
     }
 
     // softmax on this lane's tile (hi lanes: tile 0, lo lanes: tile 1).
@@ -435,41 +480,11 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
     }
     const half8 P = as_half8(pw[0], pw[1], pw[2], pw[3]);
 
-    // values: column block nb holds dims (D/16) * n + nb of lane column n = j.
-    // Pair index of tokens (2p, 2p+1) at dim nb: code_a | code_b << BITS.
-    if constexpr (VX == 1 && NB == 8) {
-      // Interleave two tokens' fields (SWAR): X[p][parity] holds the pair
-      // indices code_a | code_b << BITS of the dims of that parity at
-      // 2*BITS-bit strides.
-      constexpr uint32_t M = (1u << BITS) - 1u;
-      constexpr uint32_t ME = M | (M << (2 * BITS)) | (M << (4 * BITS)) | (M << (6 * BITS));
-      uint32_t X[4][2];
+    // values
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t ca = vch[2 * p][0], cb = vch[2 * p + 1][0];
-        X[p][0] = (ca & ME) | ((cb & ME) << BITS);
-        X[p][1] = ((ca >> BITS) & ME) | (cb & (ME << BITS));
-      }
-      static_for<NB>([&](auto nb) {
-        constexpr int sh = (decltype(nb)::value >> 1) * 2 * BITS;
-        uint32_t w4[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) w4[p] = pair(X[p][nb & 1], std::integral_constant<int, sh>{});
-        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(w4[0], w4[1], w4[2], w4[3]), O[nb], 0, 0, 0);
-      });
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t c0 = field(vch[2 * p], nb * BITS, BITS);
-          const uint32_t c1 = field(vch[2 * p + 1], nb * BITS, BITS);
-          w4[p] = pair(c0 | (c1 << BITS), std::integral_constant<int, 0>{});
-        }
-        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(w4[0], w4[1], w4[2], w4[3]), O[nb], 0, 0, 0);
-      }
-    }
+    for (int nb = 0; nb < NB; ++nb)
+      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, as_half8(vbw[nb][0], vbw[nb][1], vbw[nb][2], vbw[nb][3]),
+                                                     O[nb], 0, 0, 0);
   };
 
   // Ring of NST stages per wave: the next NST - 1 tiles are in flight while
