@@ -19,6 +19,14 @@ supplementary uniform 32K-context run (64 sequences, 32/4 heads, d=128,
 
   --calibrate-copy  also runs one plain device-to-device copy of 256 MiB first
                     (the reference kernel for scaling the HBM byte counters).
+  --no-stage1       skips the stage-1 sweep (shorter profiled runs).
+  --summarize-counters FETCH_CSV WRITE_CSV
+                    reads the counter_collection.csv of a rocprofv3 FETCH_SIZE
+                    pass and of a WRITE_SIZE pass over a --calibrate-copy run,
+                    scales both by what they read for the 256 MiB copy, and
+                    writes the decode kernel's HBM bytes per launch to
+                    profiles/decode_partial_hbm_traffic.json (tagged with a
+                    hash of the kernel sources); no GPU needed.
 """
 
 from __future__ import annotations
@@ -89,7 +97,11 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--no-stage1", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU only; runs on several GPUs are not "
                                    "part of it", "n_gpus": args.gpus}))
@@ -111,7 +123,8 @@ def main():
     extras = {}
     if not args.no_extras:
         extras["uniform_32k"] = run_uniform_32k(torch, dev, max(10, args.steps // 5), args.warmup)
-        extras["stage1"] = run_stage1(torch, dev)
+        if not args.no_stage1:
+            extras["stage1"] = run_stage1(torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head["lengths"], args.cpu_seconds)
@@ -365,6 +378,62 @@ def run_stage1(torch, dev):
           f"dequantize {head['dequantize_mvec_s']} Mvec/s", file=sys.stderr, flush=True)
     return {"workload": "2^20 unit vectors per setting, d in {128,256,512} x bits in {2,3,4} x "
                         "{Full,Fast} x {fp16,fp32} I/O", "rates": rates}
+
+
+# Kernels whose HBM traffic is recorded, by the workload they run in.
+TRAFFIC_KERNELS = {"headline": "partial_kernel<256, 3, 2, false>", "uniform_32k": "partial_kernel<128, 3, 8, false>"}
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """FETCH_SIZE / WRITE_SIZE are KiB per dispatch.  Each is scaled by
+    (true bytes / reading) of the 256 MiB device copy, whose kernel reads and
+    writes exactly 256 MiB."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        by = {}
+        for r in rows:
+            by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return by
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    # the runtime's buffer-copy blit kernel carries the 256 MiB device copy;
+    # its largest dispatch is that copy (every other blit here is tiny)
+    copy_names = [k for k in fetch if "copybuffer" in k.lower() and k in write]
+    if not copy_names:
+        raise SystemExit("no buffer-copy kernel in the counter files (run the passes with --calibrate-copy)")
+    copy_name = max(copy_names, key=lambda k: max(write[k]))
+    true_kib = COPY_BYTES / 1024
+    f_read = true_kib / max(fetch[copy_name])
+    f_write = true_kib / max(write[copy_name])
+    out = {"commands": [
+               "export TMPDIR=/tmp",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o f -- python3 bench.py "
+               "--steps 3 --warmup 1 --no-cpu-baseline --no-stage1 --calibrate-copy",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o w -- python3 bench.py "
+               "--steps 3 --warmup 1 --no-cpu-baseline --no-stage1 --calibrate-copy",
+               "python3 bench.py --summarize-counters gpurun_out/pmc_fetch/f_counter_collection.csv "
+               "gpurun_out/pmc_write/w_counter_collection.csv"],
+           "kernel_source_hash": kernel_source_hash(),
+           "copy_calibration": {"kernel": copy_name[:120], "bytes": COPY_BYTES,
+                                "fetch_kib": max(fetch[copy_name]), "write_kib": max(write[copy_name]),
+                                "read_factor": round(f_read, 4), "write_factor": round(f_write, 4)},
+           "workloads": {}}
+    for wname, kname in TRAFFIC_KERNELS.items():
+        hits = [k for k in fetch if kname in k]
+        if not hits:
+            continue
+        fk = float(np.mean(fetch[hits[0]]))
+        wk = float(np.mean(write.get(hits[0], [0.0])))
+        out["workloads"][wname] = {"kernel": kname, "dispatches": len(fetch[hits[0]]),
+                                   "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+                                   "hbm_bytes_per_launch": int(round((fk * f_read + wk * f_write) * 1024))}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
 
 
 def cpu_baseline(lengths, seconds):

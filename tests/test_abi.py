@@ -175,6 +175,15 @@ def test_partial_and_merge_validation():
                                          0x8000, 16, 0.1, 1, 0x7000, need - 16, None) == -4
     assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 64, ctypes.byref(k), ctypes.byref(k),
                                          0x8000, 16, 0.1, 1, 0x7000, need, None) == -2
+    # a (sequence, head) region of 2^30 bytes or more is beyond 32-bit in-region offsets
+    rows = (1 << 30) // 48
+    huge = B.IQCacheC(0x4000, 0x5000, rows + 1)
+    fine = B.IQCacheC(0x4000, 0x5000, rows)
+    assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 32, ctypes.byref(huge), ctypes.byref(k),
+                                         0x8000, 16, 0.1, 1, 0x7000, need, None) == -2
+    assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 32, ctypes.byref(k), ctypes.byref(huge),
+                                         0x8000, 16, 0.1, 1, 0x7000, need, None) == -2
+    assert (1 << 30) - rows * 48 <= 48 and fine.capacity * 48 < (1 << 30)
     # merge: null out, bad dtype, misaligned argmax
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, None, 0, None, None, 0x7000, need, None) == -1
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 5, None, None, 0x7000, need, None) == -2
