@@ -360,35 +360,37 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
     }
     // V operand: column block nb holds dims (D/16) * n + nb of lane column
     // n = j; dword p is the pair of tokens (2p, 2p+1) of the lane's 8
-    // (code_a | code_b << BITS).
+    // (code_a | code_b << BITS).  Per group of 8 column blocks the two tokens'
+    // fields are interleaved first (SWAR): X[g][p][parity] holds the pair
+    // indices of the group's dims of that parity at 2*BITS-bit strides.
     uint32_t vbw[NB][4];
-    if constexpr (VX == 1 && NB == 8) {
-      // Interleave two tokens' fields (SWAR): X[p][parity] holds the pair
-      // indices of the dims of that parity at 2*BITS-bit strides.
+    {
+      constexpr int NGRP = NB / 8;
       constexpr uint32_t M = (1u << BITS) - 1u;
       constexpr uint32_t ME = M | (M << (2 * BITS)) | (M << (4 * BITS)) | (M << (6 * BITS));
-      uint32_t X[4][2];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t ca = vch[2 * p][0], cb = vch[2 * p + 1][0];
-        X[p][0] = (ca & ME) | ((cb & ME) << BITS);
-        X[p][1] = ((ca >> BITS) & ME) | (cb & (ME << BITS));
-      }
-      static_for<NB>([&](auto nb) {
-        constexpr int sh = (decltype(nb)::value >> 1) * 2 * BITS;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) vbw[nb][p] = pair(X[p][nb & 1], std::integral_constant<int, sh>{});
-      });
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
+      uint32_t X[NGRP][4][2];
+      static_for<NGRP>([&](auto gi) {
+        constexpr int bit0 = decltype(gi)::value * 8 * BITS, wd = bit0 >> 5, off = bit0 & 31;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t c0 = field(vch[2 * p], nb * BITS, BITS);
-          const uint32_t c1 = field(vch[2 * p + 1], nb * BITS, BITS);
-          vbw[nb][p] = pair(c0 | (c1 << BITS), std::integral_constant<int, 0>{});
+          uint32_t ca, cb;
+          if constexpr (off + 8 * BITS <= 32) {
+            ca = vch[2 * p][wd] >> off;
+            cb = vch[2 * p + 1][wd] >> off;
+          } else {
+            ca = __builtin_amdgcn_alignbit(vch[2 * p][wd + 1], vch[2 * p][wd], off);
+            cb = __builtin_amdgcn_alignbit(vch[2 * p + 1][wd + 1], vch[2 * p + 1][wd], off);
+          }
+          X[gi][p][0] = (ca & ME) | ((cb & ME) << BITS);
+          X[gi][p][1] = ((ca >> BITS) & ME) | (cb & (ME << BITS));
         }
-      }
+      });
+      static_for<NB>([&](auto nb) {
+        constexpr int nbv = decltype(nb)::value;
+        constexpr int sh = ((nbv % 8) >> 1) * 2 * BITS;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) vbw[nb][p] = pair(X[nbv / 8][p][nbv & 1], std::integral_constant<int, sh>{});
+      });
     }
 
     // scores for both tiles
