@@ -113,11 +113,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 
 // Layout of one wave's LDS stage: 32 packed K rows, 32 packed V rows, 32 K
-// norms, 32 V norms.
+// norms, 32 V norms.  Rows sit RS = ROWB + PAD bytes apart; PAD (0 or one
+// 16-byte granule) is chosen per shape so that the row reads of a wave
+// spread over the LDS banks.
 template <int D, int BITS>
 struct Stage {
   static constexpr int ROWB = D * BITS / 8;
-  static constexpr int ROWS_B = kDecodeStep * ROWB;           // bytes of 32 rows
+  static constexpr int PAD = (D == 128 && BITS == 3) ? 0 : 16;
+  static constexpr int RS = ROWB + PAD;
+  static constexpr int ROWS_B = kDecodeStep * RS;             // bytes of 32 rows in LDS
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = ROWS_B;
   static constexpr int KN_OFF = 2 * ROWS_B;
@@ -132,22 +136,35 @@ struct Stage {
 // memory.
 constexpr uint32_t kOutOfRange = 0x40000000u;
 
+// Byte offset inside a 32-row block of the cache of the 16-byte granule that
+// lane `lane` of row load c places in LDS (granule 64c + lane of the padded
+// stage rows), or kOutOfRange for a pad granule.
+template <int D, int BITS>
+__device__ __forceinline__ uint32_t granule_offset(int c, int lane) {
+  using S = Stage<D, BITS>;
+  const int g = 64 * c + lane;
+  const int r = g / (S::RS / 16), o = g % (S::RS / 16);
+  return o < S::ROWB / 16 ? (uint32_t)(r * S::ROWB + 16 * o) : kOutOfRange;
+}
+
 // Issue the asynchronous buffer->LDS loads of one 32-token stage starting at
-// token t0 (wave-uniform); stage_lds is the stage's LDS byte address.  The
-// token offset rides in the per-lane offset, which the buffer range check
-// always covers.  A stage that is not needed (valid false) is still issued,
-// pointing out of range, so that every stage counts the same number of loads.
+// token t0 (wave-uniform); stage_lds is the stage's LDS byte address and
+// goff[c] the lane's granule offsets.  The token offset rides in the per-lane
+// offset, which the buffer range check always covers.  A stage that is not
+// needed (valid false) is still issued, pointing out of range, so that every
+// stage counts the same number of loads.
 template <int D, int BITS>
 __device__ __forceinline__ void load_stage(uint32_t stage_lds, int32x4_t kr, int32x4_t vr, int32x4_t knr,
-                                           int32x4_t vnr, int t0, bool valid, int lane) {
+                                           int32x4_t vnr, int t0, bool valid, int lane,
+                                           const uint32_t (&goff)[Stage<D, BITS>::ROW_LOADS]) {
   using S = Stage<D, BITS>;
   const uint32_t row_off = valid ? (uint32_t)(t0 * S::ROWB) : kOutOfRange;
   const uint32_t norm_off = valid ? (uint32_t)(t0 * 2) : kOutOfRange;
 #pragma unroll
   for (int c = 0; c < S::ROW_LOADS; ++c) {
     if (c * 1024 + lane * 16 < S::ROWS_B) {
-      dma_to_lds<16>(kr, stage_lds + S::K_OFF + c * 1024, row_off + c * 1024 + lane * 16, 0);
-      dma_to_lds<16>(vr, stage_lds + S::V_OFF + c * 1024, row_off + c * 1024 + lane * 16, 0);
+      dma_to_lds<16>(kr, stage_lds + S::K_OFF + c * 1024, goff[c] + row_off, 0);
+      dma_to_lds<16>(vr, stage_lds + S::V_OFF + c * 1024, goff[c] + row_off, 0);
     }
   }
   if (lane < kDecodeStep / 2) {
@@ -193,6 +210,13 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   constexpr int NB = D / 16;                 // 16-column blocks of the value product
   constexpr int ROWB = D * BITS / 8;         // bytes per packed row
   constexpr int CW = ROWB / 16;              // dwords of a row held by one lane group (d/4 dims)
+  // K rows are read in units of UDW dwords holding whole code pairs (32 codes
+  // at 3 bits, one dword otherwise); lane group g4 holds units g4, g4+4, ...
+  // so that the four groups read neighbouring banks.  A unit covers SPU
+  // k-steps of 8 dims.
+  constexpr int UDW = BITS == 3 ? 3 : 1;
+  constexpr int SPU = UDW * 32 / BITS / 8;
+  static_assert(CW % UDW == 0 && KS % SPU == 0, "K row units");
   constexpr int VCB = (D / 16) * BITS;       // bits of the d/16 codes a lane owns in the value product
   constexpr int VW = (VCB + 31) / 32 + 1;    // dwords read to cover them at any bit offset
   constexpr int VX = (VCB + 31) / 32;        // dwords after extraction
@@ -260,13 +284,16 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   const bool lo_lane = live && j >= G;
   const int head = j % G;
 
-  // B operand of the score product: lane group g4 covers dims [g4*D/4, (g4+1)*D/4).
+  // B operand of the score product: k-step s of lane group g4 holds dims
+  // 8 (s mod SPU) .. +7 of row unit 4 (s / SPU) + g4 (the dims the K operand
+  // carries at the same k positions).
   half8 qB[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = live ? qs[head][g4 * (D / 4) + 8 * s + e] : 0.f;
+      const int dim = (4 * (s / SPU) + g4) * (8 * SPU) + 8 * (s % SPU) + e;
+      const float v = live ? qs[head][dim] : 0.f;
       const _Float16 hi = static_cast<_Float16>(v);
       qB[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
     }
@@ -288,8 +315,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   const int vbit = VCB * j;                  // bit offset of this lane's codes in a row
   const float lo_mask = lo_lane ? 1.f : 0.f;
   // per-lane LDS byte offsets inside a stage
-  const int k_off = S::K_OFF + j * ROWB + g4 * CW * 4;
-  const int v_off = S::V_OFF + 4 * g4 * ROWB + (vbit >> 5) * 4;
+  const int k_off = S::K_OFF + j * S::RS + g4 * UDW * 4;
+  const int v_off = S::V_OFF + 4 * g4 * S::RS + (vbit >> 5) * 4;
   const int n_off = (16 * my_tile + 4 * g4) * 2;
   // byte address of this lane's replica of table entry 0
   const uint32_t lut_base = lds_addr(lut) + (uint32_t)(lane % REPL) * 4u;
@@ -319,15 +346,17 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
     uint32_t kw[2][CW];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + k_off + tile * 16 * ROWB);
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + k_off + tile * 16 * S::RS);
 #pragma unroll
-      for (int i = 0; i < CW; ++i) kw[tile][i] = src[i];
+      for (int m = 0; m < CW / UDW; ++m)
+#pragma unroll
+        for (int t = 0; t < UDW; ++t) kw[tile][m * UDW + t] = src[4 * m * UDW + t];
     }
     // the 8 tokens of this lane in the operand/result layouts: 4*g4 + r of each tile
     uint32_t vch[8][VX];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + v_off + (16 * (r >> 2) + (r & 3)) * ROWB);
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + v_off + (16 * (r >> 2) + (r & 3)) * S::RS);
       uint32_t w[VW];
 #pragma unroll
       for (int i = 0; i < VW; ++i) w[i] = src[i];            // may read one dword past the row: still in LDS
@@ -348,7 +377,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
       static_for<KS>([&](auto s) {
         static_for<4>([&](auto p) {
           constexpr int W = 2 * BITS;
-          constexpr int pos = (8 * decltype(s)::value + 2 * decltype(p)::value) * BITS;
+          constexpr int sv = decltype(s)::value;
+          constexpr int pos = (sv / SPU) * UDW * 32 + (8 * (sv % SPU) + 2 * decltype(p)::value) * BITS;
           constexpr int wd = pos >> 5, off = pos & 31;
           if constexpr (off + W <= 32 || wd + 1 >= CW)
             ka[tile][s][p] = pair(kw[tile][wd], std::integral_constant<int, off>{});
@@ -489,6 +519,10 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
                                                      O[nb], 0, 0, 0);
   };
 
+  uint32_t goff[S::ROW_LOADS];
+#pragma unroll
+  for (int c = 0; c < S::ROW_LOADS; ++c) goff[c] = granule_offset<D, BITS>(c, lane);
+
   // Ring of NST stages per wave: the next NST - 1 tiles are in flight while
   // one is processed.  Every iteration issues one stage (out of range past
   // the wave's last tile), so one fixed wait finds the oldest stage landed.
@@ -496,14 +530,15 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   if (n_tiles > 0) {
 #pragma unroll
     for (int i = 0; i < NST - 1; ++i)
-      load_stage<D, BITS>(stages_lds + i * S::BYTES, kr, vr, knr, vnr, begin + i * kDecodeStep, i < n_tiles, lane);
+      load_stage<D, BITS>(stages_lds + i * S::BYTES, kr, vr, knr, vnr, begin + i * kDecodeStep, i < n_tiles, lane,
+                          goff);
     const int n_full = (end - begin) / kDecodeStep;
     int slot = 0;                            // stage of tile `it`
     for (int it = 0; it < n_full; ++it) {
       const int ahead = it + NST - 1;
       const int aslot = slot == 0 ? NST - 1 : slot - 1;     // (it + NST - 1) mod NST, processed last iteration
       load_stage<D, BITS>(stages_lds + aslot * S::BYTES, kr, vr, knr, vnr, begin + ahead * kDecodeStep,
-                          ahead < n_tiles, lane);
+                          ahead < n_tiles, lane, goff);
       wait_vmem<(NST - 1) * S::LOADS>();
       process(stages + slot * S::BYTES, begin + it * kDecodeStep, std::true_type{});
       slot = slot == NST - 1 ? 0 : slot + 1;
