@@ -2,9 +2,12 @@
 // launch geometry and kernel dispatch.  See include/iq.h for the contract.
 #include "iq.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <limits>
+#include <vector>
 
 #include "iq_internal.h"
 
@@ -89,6 +92,52 @@ Tables make_tables(const iq_config *cfg) {
     t.thr[k] = static_cast<float>(0.5 * (static_cast<double>(cfg->centroids[k]) +
                                          static_cast<double>(cfg->centroids[k + 1])));
   return t;
+}
+
+// Cell index of a value exactly as the quantize kernel computes it: fp32 fma
+// whose offset includes 2^23 (so the result is rounded to an integer),
+// clamped to [2^23, 2^23 + n - 1].
+constexpr float kCellMagic = 8388608.0f;  // 2^23
+uint32_t cell_of(float x, float scale, float offset, int n) {
+  float y = std::fma(x, scale, offset);
+  y = std::min(std::max(y, kCellMagic), kCellMagic + static_cast<float>(n - 1));
+  return static_cast<uint32_t>(y - kCellMagic);
+}
+
+// Smallest power-of-two cell table (8..kMaxCells cells) with at most one
+// threshold per cell; n = 0 when none exists.
+iq::CellTable make_cells(const Tables &t, int bits) {
+  iq::CellTable c;
+  std::memset(&c, 0, sizeof(c));
+  const int nthr = (1 << bits) - 1;
+  const float lo = t.thr[0], hi = t.thr[nthr - 1];
+  if (!(hi > lo)) return c;
+  for (int n = 8; n <= iq::kMaxCells; n *= 2) {
+    const float scale = static_cast<float>(n - 1) / (hi - lo);
+    const float offset = kCellMagic - lo * scale;
+    if (!std::isfinite(scale) || !std::isfinite(offset)) break;
+    std::vector<int> owner(n, -1);
+    bool ok = true;
+    for (int k = 0; k < nthr && ok; ++k) {
+      const uint32_t ci = cell_of(t.thr[k], scale, offset, n);
+      if (owner[ci] >= 0) ok = false;
+      owner[ci] = k;
+    }
+    if (!ok) continue;
+    uint32_t below = 0;
+    for (int ci = 0; ci < n; ++ci) {
+      const float th = owner[ci] >= 0 ? t.thr[owner[ci]] : std::numeric_limits<float>::infinity();
+      uint32_t bitsv;
+      std::memcpy(&bitsv, &th, 4);
+      c.e[ci] = make_uint2(bitsv, below);
+      if (owner[ci] >= 0) ++below;
+    }
+    c.scale = scale;
+    c.offset = offset;
+    c.n = n;
+    return c;
+  }
+  return c;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_HIP; }
@@ -203,6 +252,7 @@ int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype, int
   a.n = n_new;
   a.hkv = cfg->num_kv_heads;
   a.tab = make_tables(cfg);
+  a.cells = make_cells(a.tab, cfg->bits);
   return hip_status(iq::launch_quantize(cfg->head_dim, cfg->bits, cfg->variant, x_dtype == IQ_F16, a, stream));
 }
 

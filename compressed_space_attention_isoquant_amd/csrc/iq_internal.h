@@ -15,6 +15,21 @@ struct Tables {
   float thr[kMaxLevels];   // thr[k] = (cent[k] + cent[k+1]) / 2, k < 2^b - 1
 };
 
+// Lloyd-Max code lookup: a monotone cell index
+// c(x) = clamp(fma(x, scale, offset), 2^23, 2^23 + n - 1) - 2^23 over n cells
+// (offset includes 2^23, so the fp32 fma rounds onto the integers), each cell
+// holding at most one threshold: entry c = (bits of that threshold, or of
+// +inf; number of thresholds whose cell is below c).  The code of x is then
+// entry.y + (x > entry.x) -- the same count of thresholds strictly below x.
+// n = 0: no such table (thresholds too close); the kernel counts directly.
+constexpr int kMaxCells = 256;
+struct CellTable {
+  float scale, offset;
+  int n;
+  int pad_;
+  uint2 e[kMaxCells];
+};
+
 struct QuantArgs {
   const void *x;           // [batch][n][H_kv][d]
   const float *quats;      // [H_kv][d/4][2][4]
@@ -24,6 +39,7 @@ struct QuantArgs {
   long long capacity;
   int batch, n, hkv;
   Tables tab;
+  CellTable cells;
 };
 
 struct DequantArgs {

@@ -41,14 +41,14 @@ struct IO<float> {
 
 template <>
 struct IO<_Float16> {
-  __device__ static void load32(const _Float16 *p, float (&r)[32]) {
+  __device__ static void load32(const _Float16 *p, _Float16 (&r)[32]) {
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     const h8 *p8 = reinterpret_cast<const h8 *>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       h8 v = p8[i];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) r[8 * i + k] = static_cast<float>(v[k]);
+      for (int k = 0; k < 8; ++k) r[8 * i + k] = v[k];
     }
   }
   __device__ static void store32(_Float16 *p, const float (&r)[32]) {
@@ -64,9 +64,43 @@ struct IO<_Float16> {
   }
 };
 
+// Value of lane (lane ^ M) within groups of 32 lanes, M a power of two < 32.
+// DPP (a vector-ALU move, no latency) serves M = 1, 2 (quad permutes) and
+// M = 8 (row rotate by 8) when DPP is set; otherwise, and for M = 4 and 16,
+// ds_swizzle (bit-mask mode) goes through the LDS crossbar, which costs no
+// vector-ALU slot but has LDS latency.
+template <int M, bool DPP>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(M > 0 && M < 32 && (M & (M - 1)) == 0, "xor mask");
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (DPP && M == 1)
+    r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  else if constexpr (DPP && M == 2)
+    r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  else if constexpr (DPP && M == 8)
+    r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true);  // row_ror:8
+  else
+    r = __builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1F);
+  return __builtin_bit_cast(float, r);
+}
+
 // Unnormalised Walsh-Hadamard butterflies over d = 32 * LPV elements held as
 // r[0..31] in each of LPV consecutive lanes (lane j holds elements 32j..32j+31).
+// Across lanes the pair (a, b) of lanes (j, j ^ hl) becomes (a + b, a - b).
+// Lane j keeps its values multiplied by a sign sigma(j): the upper lane of a
+// pair stores b' = -(a - b) = b - a, so every lane does r += s(j) * other
+// with s(j) = -1 on upper lanes, one multiply-add per value.  The signs only
+// depend on the lane bits already exchanged, so partners always carry equal
+// signs, and after all stages lane j holds sigma(j) * (H x) with
+// sigma(j) = (-1)^popcount(j) (lane_sign); the caller multiplies by sigma(j)
+// after the transform.
 template <int LPV>
+__device__ __forceinline__ float lane_sign(int j) {
+  return (__builtin_popcount(j & (LPV - 1)) & 1) ? -1.f : 1.f;
+}
+
+template <int LPV, bool DPP>
 __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
@@ -79,15 +113,54 @@ __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
       }
     }
   }
+  static_for_pow2<LPV>([&](auto hl_c) {
+    constexpr int hl = decltype(hl_c)::value;
+    const float sign = (j & hl) ? -1.f : 1.f;
 #pragma unroll
-  for (int hl = 1; hl < LPV; hl <<= 1) {
-    const bool upper = (j & hl) != 0;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      float o = shfl_xor(r[k], hl);
-      r[k] = upper ? (o - r[k]) : (r[k] + o);
-    }
+    for (int k = 0; k < 32; ++k) r[k] = fmaf(lane_xor<hl, DPP>(r[k]), sign, r[k]);
+    // Finish the stage before the next: left to itself the scheduler runs
+    // each value through all stages in turn, one exchange latency at a time.
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// Columns of the 4x4 matrices of the forward block rotations: column c of
+// block gb = 8 j + blk (held by lane j of a vector) is so4_fwd(e_c), times
+// lane_sign(j) when SIGNED, stored at qm[blk][c][j] so that the lanes of a
+// vector read consecutive 16-byte words (no LDS bank conflicts).  The inverse
+// rotation is the transpose of the unsigned matrix.
+template <int LPV>
+using BlockMatrices = float4[8][4][LPV];
+
+template <int D, int VARIANT, bool SIGNED>
+__device__ __forceinline__ void load_block_matrices(BlockMatrices<D / 32> &qm, const float *quats) {
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
+    const int gb = i >> 2, c = i & 3;
+    const float4 *q = reinterpret_cast<const float4 *>(quats) + 2 * gb;
+    const float4 e = make_float4(c == 0, c == 1, c == 2, c == 3);
+    float4 col = so4_fwd<VARIANT>(e, q[0], q[1]);
+    if (SIGNED && lane_sign<D / 32>(gb >> 3) < 0.f) col = make_float4(-col.x, -col.y, -col.z, -col.w);
+    qm[gb & 7][c][gb >> 3] = col;
   }
+}
+
+// m0..m3: the columns
+__device__ __forceinline__ float4 mat_vec(float4 m0, float4 m1, float4 m2, float4 m3, float4 v) {
+  float4 t;
+  t.x = fmaf(m3.x, v.w, fmaf(m2.x, v.z, fmaf(m1.x, v.y, m0.x * v.x)));
+  t.y = fmaf(m3.y, v.w, fmaf(m2.y, v.z, fmaf(m1.y, v.y, m0.y * v.x)));
+  t.z = fmaf(m3.z, v.w, fmaf(m2.z, v.z, fmaf(m1.z, v.y, m0.z * v.x)));
+  t.w = fmaf(m3.w, v.w, fmaf(m2.w, v.z, fmaf(m1.w, v.y, m0.w * v.x)));
+  return t;
+}
+
+__device__ __forceinline__ float dot4(float4 a, float4 b) {
+  return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, a.x * b.x)));
+}
+
+// transpose of the matrix with columns m0..m3, times v
+__device__ __forceinline__ float4 mat_t_vec(float4 m0, float4 m1, float4 m2, float4 m3, float4 v) {
+  return make_float4(dot4(m0, v), dot4(m1, v), dot4(m2, v), dot4(m3, v));
 }
 
 template <int D, int BITS, int VARIANT, typename TIn>
@@ -99,67 +172,113 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   constexpr int ROWB = D * BITS / 8;     // packed row bytes
   const int h = blockIdx.y;
 
-  __shared__ float4 qs[D / 4][2];        // (q_L, q_R) of this head's blocks
-  for (int i = threadIdx.x; i < D / 2; i += kThreads)
-    qs[i >> 1][i & 1] = reinterpret_cast<const float4 *>(a.quats + (size_t)h * D * 2)[i];
+  __shared__ BlockMatrices<LPV> qm;      // block rotation matrices of this head
+  __shared__ uint2 cells[kMaxCells];
+  load_block_matrices<D, VARIANT, true>(qm, a.quats + (size_t)h * D * 2);
+  static_assert(kMaxCells <= kThreads, "one cell per thread");
+  if ((int)threadIdx.x < a.cells.n) cells[threadIdx.x] = a.cells.e[threadIdx.x];
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int j = lane % LPV;
   const long long nvec = (long long)a.batch * a.n;
-  const long long v = (long long)blockIdx.x * VPB + wave * VPW + lane / LPV;
-  const bool valid = v < nvec;
-  const long long vv = valid ? v : 0;    // inactive lanes still join the exchanges
+  const long long stride = (long long)gridDim.x * VPB;
+  // Lanes past the last vector work on vector 0 instead and store what its
+  // own lanes store, so that every memory access is unconditional.
+  auto clamp = [&](long long v) { return v < nvec ? v : 0; };
+  // input and append position of vector v
+  auto fetch = [&](long long v, TIn (&x)[32], int &sp) {
+    IO<TIn>::load32(static_cast<const TIn *>(a.x) + ((size_t)v * a.hkv + h) * D + 32 * j, x);
+    sp = a.start_pos[v / a.n];
+  };
+  // Workgroups stride over the vectors of one head, so the tables above are
+  // built once per workgroup.  The next vector's loads are issued before this
+  // one's stores (a load issued after a store cannot be waited for alone), and
+  // no branch skips a store or a load, so that the waits stay exact.
+  TIn xn[32];
+  int spn;
+  fetch(clamp((long long)blockIdx.x * VPB + wave * VPW + lane / LPV), xn, spn);
+  for (long long v0 = (long long)blockIdx.x * VPB; v0 < nvec; v0 += stride) {
+    const long long v = clamp(v0 + wave * VPW + lane / LPV);
+    TIn xin[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) xin[k] = xn[k];
+    const int sp = spn;
+    fetch(clamp(v0 + stride + wave * VPW + lane / LPV), xn, spn);
 
-  float r[32];
-  const TIn *src = static_cast<const TIn *>(a.x) + ((size_t)vv * a.hkv + h) * D + 32 * j;
-  IO<TIn>::load32(src, r);
+    // s = ||x||_2 (fp32 sum of squares, tree over the vector's lanes)
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) ss = fmaf((float)xin[k], (float)xin[k], ss);
+#pragma unroll
+    for (int m = 1; m < LPV; m <<= 1) ss += shfl_xor(ss, m);
+    const float s = sqrtf(ss);
+    // x^ = x / s folded with the 1/sqrt(d) of the normalised transform
+    const float inv = s > 0.f ? 1.0f / (s * sqrtf((float)D)) : 0.f;
+    float r[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) r[k] = (float)xin[k] * inv;
 
-  // s = ||x||_2 (fp32 sum of squares, tree over the vector's lanes)
-  float ss = 0.f;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) ss = fmaf(r[k], r[k], ss);
-#pragma unroll
-  for (int m = 1; m < LPV; m <<= 1) ss += shfl_xor(ss, m);
-  const float s = sqrtf(ss);
-  // x^ = x / s folded with the 1/sqrt(d) of the normalised transform
-  const float inv = s > 0.f ? 1.0f / (s * sqrtf((float)D)) : 0.f;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) r[k] *= inv;
+    // DPP exchanges measured faster except for d = 128, where the LDS
+    // swizzle relieves the vector ALU
+    wht_butterflies<LPV, (D > 128)>(r, j);
 
-  wht_butterflies<LPV>(r, j);
+    // block rotations; the matrices carry the butterflies' lane sign
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      float4 t = mat_vec(qm[blk][0][j], qm[blk][1][j], qm[blk][2][j], qm[blk][3][j],
+                         make_float4(r[4 * blk], r[4 * blk + 1], r[4 * blk + 2], r[4 * blk + 3]));
+      r[4 * blk] = t.x;
+      r[4 * blk + 1] = t.y;
+      r[4 * blk + 2] = t.z;
+      r[4 * blk + 3] = t.w;
+    }
 
+    // Lloyd-Max code = number of thresholds strictly below the value; packed
+    // LSB-first: code k of this lane occupies bits BITS*k .. BITS*k+BITS-1.
+    uint32_t w[BITS];
+    auto pack = [&](auto code_of) {
 #pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
-    const int gb = 8 * j + blk;
-    float4 t = so4_fwd<VARIANT>(make_float4(r[4 * blk], r[4 * blk + 1], r[4 * blk + 2], r[4 * blk + 3]),
-                                qs[gb][0], qs[gb][1]);
-    r[4 * blk] = t.x;
-    r[4 * blk + 1] = t.y;
-    r[4 * blk + 2] = t.z;
-    r[4 * blk + 3] = t.w;
-  }
+      for (int i = 0; i < BITS; ++i) w[i] = 0u;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const uint32_t code = code_of(r[k]);
+        const int bit = BITS * k;
+        w[bit >> 5] |= code << (bit & 31);
+        if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+      }
+    };
+    auto count_all = [&](float x) {
+      uint32_t code = 0;
+#pragma unroll
+      for (int t = 0; t < NLEV - 1; ++t) code += (x > a.tab.thr[t]) ? 1u : 0u;
+      return code;
+    };
+    if (a.cells.n > 0) {
+      // One threshold test per value through the cell table.  The cell index
+      // is rounded onto the integers by the fma itself (the offset holds 2^23,
+      // where the fp32 spacing is 1) and read from the low bits of the clamped
+      // result; the table address is those bits times 8 plus a base that
+      // cancels the exponent bits modulo 2^32.
+      const float cmin = 8388608.0f, cmax = 8388608.0f + (float)(a.cells.n - 1);
+      const float cs = a.cells.scale, co = a.cells.offset;
+      const uint32_t tbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)cells -
+                             (0x4B000000u << 3);
+      pack([&](float x) {
+        const float y = __builtin_amdgcn_fmed3f(fmaf(x, cs, co), cmin, cmax);
+        const uint32_t addr = (__float_as_uint(y) << 3) + tbase;
+        const uint64_t e = *reinterpret_cast<const __attribute__((address_space(3))) uint64_t *>(addr);
+        return (uint32_t)(e >> 32) + (x > __uint_as_float((uint32_t)e) ? 1u : 0u);
+      });
+    } else {
+      pack(count_all);
+    }
 
-  // Lloyd-Max code = number of thresholds strictly below the value; packed
-  // LSB-first: code k of this lane occupies bits BITS*k .. BITS*k+BITS-1.
-  uint32_t w[BITS];
-#pragma unroll
-  for (int i = 0; i < BITS; ++i) w[i] = 0u;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    uint32_t code = 0;
-#pragma unroll
-    for (int t = 0; t < NLEV - 1; ++t) code += (r[k] > a.tab.thr[t]) ? 1u : 0u;
-    const int bit = BITS * k;
-    w[bit >> 5] |= code << (bit & 31);
-    if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
-  }
-
-  if (valid) {
+    // every lane of the vector stores the (same) norm
     const int b = (int)(v / a.n);
     const int t = (int)(v % a.n);
-    const long long row = ((long long)b * a.hkv + h) * a.capacity + a.start_pos[b] + t;
+    const long long row = ((long long)b * a.hkv + h) * a.capacity + sp + t;
     uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + row * ROWB + 4 * BITS * j);
     if constexpr (BITS == 4) {
       *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -169,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 #pragma unroll
       for (int i = 0; i < BITS; ++i) dst[i] = w[i];
     }
-    if (j == 0) a.norms[row] = float_to_half_bits(s);
+    a.norms[row] = float_to_half_bits(s);
   }
 }
 
@@ -182,10 +301,9 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   constexpr int ROWB = D * BITS / 8;
   const int h = blockIdx.y;
 
-  __shared__ float4 qs[D / 4][2];
+  __shared__ BlockMatrices<LPV> qm;
   __shared__ float cent[NLEV];
-  for (int i = threadIdx.x; i < D / 2; i += kThreads)
-    qs[i >> 1][i & 1] = reinterpret_cast<const float4 *>(a.quats + (size_t)h * D * 2)[i];
+  load_block_matrices<D, VARIANT, false>(qm, a.quats + (size_t)h * D * 2);
   if (threadIdx.x < NLEV) cent[threadIdx.x] = a.tab.cent[threadIdx.x];
   __syncthreads();
 
@@ -193,55 +311,83 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   const int wave = threadIdx.x >> 6;
   const int j = lane % LPV;
   const long long nvec = (long long)a.batch * a.n;
-  const long long v = (long long)blockIdx.x * VPB + wave * VPW + lane / LPV;
-  const bool valid = v < nvec;
-  const int b = valid ? (int)(v / a.n) : 0;
-  const int t = valid ? (int)(v % a.n) : 0;
-  const long long row = ((long long)b * a.hkv + h) * a.capacity + a.start_pos[b] + t;
-
-  uint32_t w[BITS];
-  const uint32_t *src = reinterpret_cast<const uint32_t *>(a.codes + row * ROWB + 4 * BITS * j);
+  const long long stride = (long long)gridDim.x * VPB;
+  // Lanes past the last vector work on vector 0 instead and store what its
+  // own lanes store, so that every memory access is unconditional.
+  auto clamp = [&](long long v) { return v < nvec ? v : 0; };
+  // codes and norm of vector v, its batch's append position being sp
+  auto fetch = [&](long long v, int sp, uint32_t (&w)[BITS], uint16_t &nb) {
+    const int b = (int)(v / a.n), t = (int)(v % a.n);
+    const long long row = ((long long)b * a.hkv + h) * a.capacity + sp + t;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(a.codes + row * ROWB + 4 * BITS * j);
 #pragma unroll
-  for (int i = 0; i < BITS; ++i) w[i] = src[i];
-  const float s16 = half_bits_to_float(a.norms[row]);
-
-  float r[32];
+    for (int i = 0; i < BITS; ++i) w[i] = src[i];
+    nb = a.norms[row];
+  };
+  auto position = [&](long long v) { return a.start_pos[v / a.n]; };
+  // Workgroups stride over the vectors of one head, so the tables above are
+  // built once per workgroup.  Loads run ahead of the stores (a load issued
+  // after a store cannot be waited for alone): the codes one vector ahead,
+  // the append position, which the codes' address needs, two ahead.  No
+  // branch skips a load or a store, so that the waits stay exact.
+  const long long vlane = wave * VPW + lane / LPV;
+  const long long vfirst = clamp((long long)blockIdx.x * VPB + vlane);
+  uint32_t wn[BITS];
+  uint16_t nn;
+  fetch(vfirst, position(vfirst), wn, nn);
+  int spn = position(clamp((long long)blockIdx.x * VPB + stride + vlane));
+  for (long long v0 = (long long)blockIdx.x * VPB; v0 < nvec; v0 += stride) {
+    const long long v = clamp(v0 + vlane);
+    uint32_t w[BITS];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int bit = BITS * k;
-    uint32_t code = w[bit >> 5] >> (bit & 31);
-    if ((bit & 31) + BITS > 32) code |= w[(bit >> 5) + 1] << (32 - (bit & 31));
-    r[k] = cent[code & (NLEV - 1)];
+    for (int i = 0; i < BITS; ++i) w[i] = wn[i];
+    const float s16 = half_bits_to_float(nn);
+    fetch(clamp(v0 + stride + vlane), spn, wn, nn);
+    spn = position(clamp(v0 + 2 * stride + vlane));
+
+    float r[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int bit = BITS * k;
+      uint32_t code = w[bit >> 5] >> (bit & 31);
+      if ((bit & 31) + BITS > 32) code |= w[(bit >> 5) + 1] << (32 - (bit & 31));
+      r[k] = cent[code & (NLEV - 1)];
+    }
+
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      float4 u = mat_t_vec(qm[blk][0][j], qm[blk][1][j], qm[blk][2][j], qm[blk][3][j],
+                           make_float4(r[4 * blk], r[4 * blk + 1], r[4 * blk + 2], r[4 * blk + 3]));
+      r[4 * blk] = u.x;
+      r[4 * blk + 1] = u.y;
+      r[4 * blk + 2] = u.z;
+      r[4 * blk + 3] = u.w;
+    }
+
+    wht_butterflies<LPV, true>(r, j);
+
+    const float scale = lane_sign<LPV>(j) * s16 / sqrtf((float)D);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) r[k] *= scale;
+
+    IO<TOut>::store32(static_cast<TOut *>(a.out) + ((size_t)v * a.hkv + h) * D + 32 * j, r);
   }
+}
 
-#pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
-    const int gb = 8 * j + blk;
-    float4 u = so4_inv<VARIANT>(make_float4(r[4 * blk], r[4 * blk + 1], r[4 * blk + 2], r[4 * blk + 3]),
-                                qs[gb][0], qs[gb][1]);
-    r[4 * blk] = u.x;
-    r[4 * blk + 1] = u.y;
-    r[4 * blk + 2] = u.z;
-    r[4 * blk + 3] = u.w;
-  }
-
-  wht_butterflies<LPV>(r, j);
-
-  const float scale = s16 / sqrtf((float)D);
-#pragma unroll
-  for (int k = 0; k < 32; ++k) r[k] *= scale;
-
-  if (valid) {
-    TOut *dst = static_cast<TOut *>(a.out) + ((size_t)v * a.hkv + h) * D + 32 * j;
-    IO<TOut>::store32(dst, r);
-  }
+// Workgroups per head: one per VPB vectors, at most about 2048 in all
+// (8 per compute unit), each then looping over its share.
+unsigned stage1_groups(long long nvec, int vpb, int hkv) {
+  long long g = (nvec + vpb - 1) / vpb;
+  const long long cap = (2048 + hkv - 1) / hkv;
+  if (g > cap) g = cap;
+  return (unsigned)(g < 1 ? 1 : g);
 }
 
 template <int D, int BITS, int VARIANT>
 hipError_t quantize_dispatch_io(int in_f16, const QuantArgs &a, hipStream_t s) {
   constexpr int VPB = (64 / (D / 32)) * (kThreads / 64);
   const long long nvec = (long long)a.batch * a.n;
-  dim3 grid((unsigned)((nvec + VPB - 1) / VPB), (unsigned)a.hkv);
+  dim3 grid(stage1_groups(nvec, VPB, a.hkv), (unsigned)a.hkv);
   if (in_f16)
     hipLaunchKernelGGL((quantize_kernel<D, BITS, VARIANT, _Float16>), grid, dim3(kThreads), 0, s, a);
   else
@@ -253,7 +399,7 @@ template <int D, int BITS, int VARIANT>
 hipError_t dequantize_dispatch_io(int out_f16, const DequantArgs &a, hipStream_t s) {
   constexpr int VPB = (64 / (D / 32)) * (kThreads / 64);
   const long long nvec = (long long)a.batch * a.n;
-  dim3 grid((unsigned)((nvec + VPB - 1) / VPB), (unsigned)a.hkv);
+  dim3 grid(stage1_groups(nvec, VPB, a.hkv), (unsigned)a.hkv);
   if (out_f16)
     hipLaunchKernelGGL((dequantize_kernel<D, BITS, VARIANT, _Float16>), grid, dim3(kThreads), 0, s, a);
   else

@@ -86,6 +86,46 @@ def test_edge_vectors():
     check_stage1(one, O.FAST, 256, 2, np.float16, "single")
 
 
+def check_custom_codebook(cent, variant, d, dt, label):
+    """Quantize with caller-supplied centroids; codes and norms against the
+    oracle run on the same centroids."""
+    t = torch()
+    bits = int(np.log2(len(cent)))
+    cent = np.asarray(cent, np.float32)
+    quats = inputs.quaternions(1, d, seed=inputs.QUATERNION_SEED)
+    cfg = B.Config(d, bits, variant, 1, t.from_numpy(quats).to(DEV), cent)
+    x = inputs.unit_vectors(777, d, dt, seed=11 + bits)
+    cache = quantize_rows(cfg, x[None, :, None, :])
+    codes, norms = host_cache(cache)
+    ref = O.quantize(x, quats[0], cent.astype(np.float64), variant)
+    rc, nf, nfm = reconcile_codes(codes[0, 0], ref["codes"], ref["flags"], bits, d)
+    rn, _, _ = reconcile_norms(norms[0, 0], ref["norm16"], ref["norm_flags"])
+    got = dequantize_gpu(cfg, cache, 1, len(x), 1, d, np.float32)[0, :, 0]
+    want = O.dequantize_codes(rc, rn, quats[0], cent.astype(np.float64), variant)
+    err = float(np.max(np.abs(got - want)))
+    hist = np.bincount(rc.ravel(), minlength=len(cent))
+    say(f"{label}: flagged={nf} flagged_mismatch={nfm} dequant_maxabs={err:.3g} levels used={hist.tolist()}")
+    assert err <= 1e-5
+    return hist
+
+
+def test_custom_codebook_with_close_thresholds():
+    """Two decision thresholds 1e-6 apart (centroids 0, 2^-20, 2^-19): no
+    cell of the code-lookup table can separate them, so the kernel counts
+    thresholds directly; codes must still match."""
+    cent = [-0.25, -0.125, -0.0625, 0.0, 2.0 ** -20, 2.0 ** -19, 0.125, 0.25]
+    check_custom_codebook(cent, O.FULL, 128, np.float32, "close thresholds")
+
+
+def test_custom_codebook_asymmetric():
+    """An asymmetric 16-level codebook (fp16-exact levels) narrower than the
+    data: values beyond the outer thresholds land in the clamped end cells."""
+    k = np.arange(16) / 15.0
+    cent = np.float16(-0.09 + 0.15 * k ** 1.3).astype(np.float32)
+    hist = check_custom_codebook(cent, O.FAST, 256, np.float16, "asymmetric")
+    assert hist[0] > 0 and hist[-1] > 0
+
+
 def test_append_offsets_batches_and_heads():
     """batch 3, 4 KV heads, rows appended at different start positions."""
     t = torch()
