@@ -57,8 +57,8 @@ UNIFORM_32K = dict(batch=64, kv_len=32768, num_q_heads=32, num_kv_heads=4, head_
 KERNEL_SOURCES = ["compressed_space_attention_isoquant_amd/csrc/decode_kernels.h",
                   "compressed_space_attention_isoquant_amd/csrc/decode_256.hip",
                   "compressed_space_attention_isoquant_amd/csrc/decode_128.hip",
-                  "compressed_space_attention_isoquant_amd/csrc/iq_internal.h",
-                  "compressed_space_attention_isoquant_amd/csrc/api.cpp"]
+                  "compressed_space_attention_isoquant_amd/csrc/decode_args.h",
+                  "compressed_space_attention_isoquant_amd/csrc/iq_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_hbm_traffic.json")
 
 

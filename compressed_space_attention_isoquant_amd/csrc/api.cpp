@@ -142,29 +142,6 @@ iq::CellTable make_cells(const Tables &t, int bits) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_HIP; }
 
-// Split-K geometry of the decode kernels: enough workgroups to cover the
-// 256 compute units several times, each holding a whole number of
-// (waves x tile) token blocks.
-struct Geometry {
-  int chunk;
-  int n_split;
-};
-
-Geometry decode_geometry(int32_t batch, int32_t hkv, int64_t max_kv_len) {
-  const int64_t unit = (int64_t)iq::kDecodeWaves * iq::kDecodeStep;
-  const int64_t T = max_kv_len > 0 ? max_kv_len : 1;
-  const int64_t pairs = (int64_t)batch * hkv;
-  const int64_t target_groups = 1024;     // 4 resident workgroups on each of 256 CUs
-  int64_t want = (target_groups + pairs - 1) / pairs;
-  if (want < 1) want = 1;
-  int64_t chunk = (T + want - 1) / want;
-  chunk = (chunk + unit - 1) / unit * unit;
-  Geometry g;
-  g.chunk = (int)chunk;
-  g.n_split = (int)((T + chunk - 1) / chunk);
-  return g;
-}
-
 // Lloyd iteration for the minimum-MSE quantiser of N(0,1): thresholds are the
 // midpoints of neighbouring levels; levels are the conditional means of their
 // cells, (phi(a) - phi(b)) / P(a < X <= b).
@@ -285,7 +262,7 @@ size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch, int32_t nu
   if (check_config(cfg) != IQ_OK) return 0;
   if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return 0;
   if (num_q_heads % cfg->num_kv_heads) return 0;
-  const Geometry g = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
+  const iq::Geometry g = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
   return (size_t)batch * num_q_heads * g.n_split * (cfg->head_dim + iq::kRecHeader) * sizeof(float);
 }
 
@@ -326,7 +303,7 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
   if (k->capacity * rb >= (int64_t(1) << 30) || v->capacity * rb >= (int64_t(1) << 30)) return IQ_ERR_UNSUPPORTED;
   if (!aligned16(q)) return IQ_ERR_MISALIGNED;
 
-  const Geometry geo = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
+  const iq::Geometry geo = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
   const int e = centroid_exponent(cfg);
   iq::DecodeArgs a;
   a.q = q;
@@ -365,7 +342,7 @@ int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q
   if (!valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
   if (!aligned16(out)) return IQ_ERR_MISALIGNED;
   if ((lse_out && !aligned16(lse_out)) || (argmax_out && !aligned16(argmax_out))) return IQ_ERR_MISALIGNED;
-  const Geometry geo = decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
+  const iq::Geometry geo = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
   iq::MergeArgs m;
   m.ws = static_cast<const float *>(workspace);
   m.quats = cfg->quats;

@@ -1,8 +1,6 @@
 // Device-side helpers for the IsoQuant kernels (gfx950, wave64).
 #pragma once
 
-#include <type_traits>
-
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,15 +36,6 @@ __device__ __forceinline__ float4 so4_inv(float4 w, float4 qL, float4 qR) {
 }
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
-
-// f(std::integral_constant<int, m>) for m = 1, 2, 4, ... < N.
-template <int N, int M = 1, class F>
-__device__ __forceinline__ void static_for_pow2(F &&f) {
-  if constexpr (M < N) {
-    f(std::integral_constant<int, M>{});
-    static_for_pow2<N, 2 * M>(f);
-  }
-}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

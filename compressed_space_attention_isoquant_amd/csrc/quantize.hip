@@ -7,6 +7,8 @@
 // lane-xor exchanges.  Each SO(4) block (4 consecutive elements) is in one
 // lane, and the 32 codes of a lane form exactly b whole dwords of the packed
 // row (32 * b bits), so packing needs no cross-lane traffic.
+#include <type_traits>
+
 #include "iq_device.h"
 #include "iq_internal.h"
 
@@ -14,6 +16,15 @@ namespace iq {
 namespace {
 
 constexpr int kThreads = 256;
+
+// f(std::integral_constant<int, m>) for m = 1, 2, 4, ... < N.
+template <int N, int M = 1, class F>
+__device__ __forceinline__ void static_for_pow2(F &&f) {
+  if constexpr (M < N) {
+    f(std::integral_constant<int, M>{});
+    static_for_pow2<N, 2 * M>(f);
+  }
+}
 
 template <typename T>
 struct IO;
