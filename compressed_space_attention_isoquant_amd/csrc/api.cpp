@@ -82,6 +82,11 @@ int check_cache(const iq_cache *c) {
 
 bool valid_dtype(int32_t t) { return t == IQ_F32 || t == IQ_F16; }
 
+// The stage-1 kernels index the vectors of a call with 32-bit integers.
+bool vector_count_ok(int32_t batch, int32_t n) {
+  return static_cast<int64_t>(batch) * n < (int64_t(1) << 31) - (int64_t(1) << 20);
+}
+
 Tables make_tables(const iq_config *cfg) {
   Tables t;
   std::memset(&t, 0, sizeof(t));
@@ -213,7 +218,7 @@ int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype, int
   if (st != IQ_OK) return st;
   if (!x || !start_pos) return IQ_ERR_INVALID_ARG;
   if (!valid_dtype(x_dtype)) return IQ_ERR_UNSUPPORTED;
-  if (batch < 1 || n_new < 1) return IQ_ERR_INVALID_ARG;
+  if (batch < 1 || n_new < 1 || !vector_count_ok(batch, n_new)) return IQ_ERR_INVALID_ARG;
   st = check_cache(out);
   if (st != IQ_OK) return st;
   if (n_new > out->capacity) return IQ_ERR_INVALID_ARG;
@@ -241,7 +246,7 @@ int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch, const
   if (st != IQ_OK) return st;
   if (!out || !start_pos) return IQ_ERR_INVALID_ARG;
   if (!valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
-  if (batch < 1 || n < 1 || n > in->capacity) return IQ_ERR_INVALID_ARG;
+  if (batch < 1 || n < 1 || n > in->capacity || !vector_count_ok(batch, n)) return IQ_ERR_INVALID_ARG;
   if (!aligned16(out)) return IQ_ERR_MISALIGNED;
   iq::DequantArgs a;
   a.codes = in->codes;

@@ -26,6 +26,23 @@ __device__ __forceinline__ void static_for_pow2(F &&f) {
   }
 }
 
+// Position (batch b, row t) of vector v = b * n + t of a [batch][n] set of
+// vectors, stepped by a fixed stride (= sq * n + sr, 0 <= sr < n) without a
+// division per step.
+struct VecPos {
+  int b, t;
+  __device__ void init(int v, int n) {
+    b = v / n;
+    t = v - b * n;
+  }
+  __device__ void advance(int sq, int sr, int n) {
+    t += sr;
+    const bool wrap = t >= n;
+    t = wrap ? t - n : t;
+    b += sq + (wrap ? 1 : 0);
+  }
+};
+
 template <typename T>
 struct IO;
 
@@ -193,30 +210,41 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int j = lane % LPV;
-  const long long nvec = (long long)a.batch * a.n;
-  const long long stride = (long long)gridDim.x * VPB;
-  // Lanes past the last vector work on vector 0 instead and store what its
-  // own lanes store, so that every memory access is unconditional.
-  auto clamp = [&](long long v) { return v < nvec ? v : 0; };
-  // input and append position of vector v
-  auto fetch = [&](long long v, TIn (&x)[32], int &sp) {
-    IO<TIn>::load32(static_cast<const TIn *>(a.x) + ((size_t)v * a.hkv + h) * D + 32 * j, x);
-    sp = a.start_pos[v / a.n];
+  const long long nvec = (long long)a.batch * a.n;   // < 2^31 (checked by the host)
+  const int n = a.n;
+  const int stride = (int)gridDim.x * VPB;
+  const int sq = stride / n, sr = stride - sq * n;
+  // Lanes past the last vector (b >= batch) work on vector 0 instead and store
+  // what its own lanes store, so that every memory access is unconditional.
+  auto clamp = [&](const VecPos &p, int &b, int &t) {
+    const bool ok = p.b < a.batch;
+    b = ok ? p.b : 0;
+    t = ok ? p.t : 0;
+  };
+  // input and append position of the vector at p
+  auto fetch = [&](const VecPos &p, TIn (&x)[32], int &sp) {
+    int b, t;
+    clamp(p, b, t);
+    IO<TIn>::load32(static_cast<const TIn *>(a.x) + ((size_t)(b * n + t) * a.hkv + h) * D + 32 * j, x);
+    sp = a.start_pos[b];
   };
   // Workgroups stride over the vectors of one head, so the tables above are
   // built once per workgroup.  The next vector's loads are issued before this
   // one's stores (a load issued after a store cannot be waited for alone), and
   // no branch skips a store or a load, so that the waits stay exact.
+  VecPos cur, nxt;
+  cur.init((int)blockIdx.x * VPB + wave * VPW + lane / LPV, n);
+  nxt = cur;
+  nxt.advance(sq, sr, n);
   TIn xn[32];
   int spn;
-  fetch(clamp((long long)blockIdx.x * VPB + wave * VPW + lane / LPV), xn, spn);
+  fetch(cur, xn, spn);
   for (long long v0 = (long long)blockIdx.x * VPB; v0 < nvec; v0 += stride) {
-    const long long v = clamp(v0 + wave * VPW + lane / LPV);
     TIn xin[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) xin[k] = xn[k];
     const int sp = spn;
-    fetch(clamp(v0 + stride + wave * VPW + lane / LPV), xn, spn);
+    fetch(nxt, xn, spn);
 
     // s = ||x||_2 (fp32 sum of squares, tree over the vector's lanes)
     float ss = 0.f;
@@ -287,8 +315,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     }
 
     // every lane of the vector stores the (same) norm
-    const int b = (int)(v / a.n);
-    const int t = (int)(v % a.n);
+    int b, t;
+    clamp(cur, b, t);
     const long long row = ((long long)b * a.hkv + h) * a.capacity + sp + t;
     uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + row * ROWB + 4 * BITS * j);
     if constexpr (BITS == 4) {
@@ -300,6 +328,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
       for (int i = 0; i < BITS; ++i) dst[i] = w[i];
     }
     a.norms[row] = float_to_half_bits(s);
+    cur = nxt;
+    nxt.advance(sq, sr, n);
   }
 }
 
@@ -312,6 +342,15 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   constexpr int ROWB = D * BITS / 8;
   const int h = blockIdx.y;
 
+  // output staging: each lane's 32 values (one padded segment per lane, so
+  // the segment writes do not collide in LDS banks), read back in output
+  // order so that a store instruction writes whole contiguous rows
+  constexpr int SZ = (int)sizeof(TOut);
+  constexpr int CPL = 32 * SZ / 16;        // 16-byte chunks per lane
+  constexpr int SEGP = 32 * SZ + 16;       // padded segment bytes
+  constexpr int CPV = D * SZ / 16;         // chunks per output row
+  __shared__ uint4 obuf[kThreads / 64][64 * SEGP / 16];
+
   __shared__ BlockMatrices<LPV> qm;
   __shared__ float cent[NLEV];
   load_block_matrices<D, VARIANT, false>(qm, a.quats + (size_t)h * D * 2);
@@ -321,40 +360,54 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int j = lane % LPV;
-  const long long nvec = (long long)a.batch * a.n;
-  const long long stride = (long long)gridDim.x * VPB;
-  // Lanes past the last vector work on vector 0 instead and store what its
-  // own lanes store, so that every memory access is unconditional.
-  auto clamp = [&](long long v) { return v < nvec ? v : 0; };
-  // codes and norm of vector v, its batch's append position being sp
-  auto fetch = [&](long long v, int sp, uint32_t (&w)[BITS], uint16_t &nb) {
-    const int b = (int)(v / a.n), t = (int)(v % a.n);
+  const long long nvec = (long long)a.batch * a.n;   // < 2^31 (checked by the host)
+  const int n = a.n;
+  const int stride = (int)gridDim.x * VPB;
+  const int sq = stride / n, sr = stride - sq * n;
+  // Lanes past the last vector (b >= batch) work on vector 0 instead and store
+  // what its own lanes store, so that every memory access is unconditional.
+  auto clamp = [&](const VecPos &p, int &b, int &t) {
+    const bool ok = p.b < a.batch;
+    b = ok ? p.b : 0;
+    t = ok ? p.t : 0;
+  };
+  // codes and norm of the vector at p, its batch's append position being sp
+  auto fetch = [&](const VecPos &p, int sp, uint32_t (&w)[BITS], uint16_t &nb) {
+    int b, t;
+    clamp(p, b, t);
     const long long row = ((long long)b * a.hkv + h) * a.capacity + sp + t;
     const uint32_t *src = reinterpret_cast<const uint32_t *>(a.codes + row * ROWB + 4 * BITS * j);
 #pragma unroll
     for (int i = 0; i < BITS; ++i) w[i] = src[i];
     nb = a.norms[row];
   };
-  auto position = [&](long long v) { return a.start_pos[v / a.n]; };
+  auto position = [&](const VecPos &p) {
+    int b, t;
+    clamp(p, b, t);
+    return a.start_pos[b];
+  };
   // Workgroups stride over the vectors of one head, so the tables above are
   // built once per workgroup.  Loads run ahead of the stores (a load issued
   // after a store cannot be waited for alone): the codes one vector ahead,
   // the append position, which the codes' address needs, two ahead.  No
   // branch skips a load or a store, so that the waits stay exact.
-  const long long vlane = wave * VPW + lane / LPV;
-  const long long vfirst = clamp((long long)blockIdx.x * VPB + vlane);
+  VecPos p0, p1, p2;                         // this vector, the next, the one after
+  p0.init((int)blockIdx.x * VPB + wave * VPW + lane / LPV, n);
+  p1 = p0;
+  p1.advance(sq, sr, n);
+  p2 = p1;
+  p2.advance(sq, sr, n);
   uint32_t wn[BITS];
   uint16_t nn;
-  fetch(vfirst, position(vfirst), wn, nn);
-  int spn = position(clamp((long long)blockIdx.x * VPB + stride + vlane));
+  fetch(p0, position(p0), wn, nn);
+  int spn = position(p1);
   for (long long v0 = (long long)blockIdx.x * VPB; v0 < nvec; v0 += stride) {
-    const long long v = clamp(v0 + vlane);
     uint32_t w[BITS];
 #pragma unroll
     for (int i = 0; i < BITS; ++i) w[i] = wn[i];
     const float s16 = half_bits_to_float(nn);
-    fetch(clamp(v0 + stride + vlane), spn, wn, nn);
-    spn = position(clamp(v0 + 2 * stride + vlane));
+    fetch(p1, spn, wn, nn);
+    spn = position(p2);
 
     float r[32];
 #pragma unroll
@@ -381,7 +434,29 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
 #pragma unroll
     for (int k = 0; k < 32; ++k) r[k] *= scale;
 
-    IO<TOut>::store32(static_cast<TOut *>(a.out) + ((size_t)v * a.hkv + h) * D + 32 * j, r);
+    int b, t;
+    clamp(p0, b, t);
+    const int f = b * n + t;                 // row of the output
+    char *seg = reinterpret_cast<char *>(obuf[wave]) + lane * SEGP;
+    // (the asm statements keep the compiler from moving LDS accesses across
+    // them; one wave's LDS accesses complete in issue order)
+    asm volatile("" ::: "memory");
+    IO<TOut>::store32(reinterpret_cast<TOut *>(seg), r);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = 64 * i + lane;           // chunk of the wave's rows, in output order
+      const int src = c / CPL;               // the lane that computed it
+      const uint4 val = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(obuf[wave]) +
+                                                         src * SEGP + 16 * (c % CPL));
+      const int frow = __shfl(f, (src / LPV) * LPV, 64);
+      char *dst = static_cast<char *>(a.out) + ((size_t)frow * a.hkv + h) * (D * SZ) + 16 * (c % CPV);
+      *reinterpret_cast<uint4 *>(dst) = val;
+    }
+    asm volatile("" ::: "memory");
+    p0 = p1;
+    p1 = p2;
+    p2.advance(sq, sr, n);
   }
 }
 

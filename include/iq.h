@@ -107,6 +107,8 @@ int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out);
  *   start_pos: DEVICE int32 [batch]; vector t of sequence b is written to row
  *              start_pos[b] + t of `out`.  The library does not advance it.
  *   out:       the packed tensor written (codes and norms).
+ * batch * n_new must stay below 2^31 - 2^20 (IQ_ERR_INVALID_ARG otherwise;
+ * an input that large would not fit in device memory anyway).
  * K and V are two calls on two caches that share one iq_config. */
 int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype,
                        int32_t batch, int32_t n_new, const int32_t *start_pos,
@@ -116,7 +118,8 @@ int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype,
  * (the stage-1 return path of the IsoQuant abstract; inverse of RotaryQuant
  * eq. (2) as in §3.4):  out[b][t][h][:] = fp16(s) * R^T c[codes].
  *   start_pos: DEVICE int32 [batch].
- *   out:       [batch][n][H_kv][d] of out_dtype. */
+ *   out:       [batch][n][H_kv][d] of out_dtype.
+ * batch * n must stay below 2^31 - 2^20 (IQ_ERR_INVALID_ARG otherwise). */
 int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch,
                   const int32_t *start_pos, int32_t n, void *out,
                   int32_t out_dtype, hipStream_t stream);

@@ -104,6 +104,8 @@ def test_quantize_validation():
     assert call_quant(cfg(), codes=0) == -1
     assert call_quant(cfg(), norms=0x5002) == -3
     assert call_quant(cfg(), cap=0) == -1
+    # batch * n_new must fit the kernels' 32-bit vector indices
+    assert call_quant(cfg(), batch=1 << 16, n=1 << 15, cap=1 << 15) == -1
     bad = O.codebook(3, 128).copy()
     bad[3], bad[4] = bad[4], bad[3]
     assert call_quant(cfg(centroids=bad)) == -1
@@ -160,6 +162,8 @@ def test_dequantize_validation():
     assert L.iq_dequantize(ctypes.byref(cc), ctypes.byref(cache), 1, 0x3000, 4, 0x6002, 0, None) == -3
     assert L.iq_dequantize(ctypes.byref(cc), ctypes.byref(cache), 1, 0x3000, 4, 0x6000, 9, None) == -2
     assert L.iq_dequantize(ctypes.byref(cc), None, 1, 0x3000, 4, 0x6000, 0, None) == -1
+    huge = B.IQCacheC(0x4000, 0x5000, 1 << 15)
+    assert L.iq_dequantize(ctypes.byref(cc), ctypes.byref(huge), 1 << 16, 0x3000, 1 << 15, 0x6000, 0, None) == -1
 
 
 def test_partial_and_merge_validation():
