@@ -262,10 +262,13 @@ int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch, const
   return hip_status(iq::launch_dequantize(cfg->head_dim, cfg->bits, cfg->variant, out_dtype == IQ_F16, a, stream));
 }
 
+// The decode grids carry the sequence index in their second dimension.
+constexpr int32_t kMaxDecodeBatch = 65535;
+
 size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
                                  int64_t max_kv_len) {
   if (check_config(cfg) != IQ_OK) return 0;
-  if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return 0;
+  if (batch < 1 || batch > kMaxDecodeBatch || num_q_heads < 1 || max_kv_len < 0) return 0;
   if (num_q_heads % cfg->num_kv_heads) return 0;
   const iq::Geometry g = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
   return (size_t)batch * num_q_heads * g.n_split * (cfg->head_dim + iq::kRecHeader) * sizeof(float);
@@ -278,6 +281,7 @@ static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_
   if (st != IQ_OK) return st;
   if (!workspace) return IQ_ERR_INVALID_ARG;
   if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return IQ_ERR_INVALID_ARG;
+  if (batch > kMaxDecodeBatch) return IQ_ERR_UNSUPPORTED;
   if (num_q_heads % cfg->num_kv_heads) return IQ_ERR_INVALID_ARG;
   *group = num_q_heads / cfg->num_kv_heads;
   if (*group != 1 && *group != 2 && *group != 4 && *group != 8) return IQ_ERR_UNSUPPORTED;

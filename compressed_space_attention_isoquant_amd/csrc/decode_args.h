@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace iq {
 
 // Split-K decode.  Each workgroup (4 waves) of the partial kernel covers
@@ -51,9 +53,12 @@ struct MergeArgs {
   float oscale;            // 2^-cexp
 };
 
-// Split-K geometry of the decode kernels: enough workgroups to cover the
-// 256 compute units several times, each holding a whole number of
-// (waves x tile) token blocks.
+// Split-K geometry of the decode kernels.  About 2048 workgroups (8 per
+// compute unit, two resident at a time): with ragged context lengths the
+// extra, shorter workgroups even out the compute units' loads.  Chunks are
+// kept at 8192 tokens or more while that still gives 1024 workgroups, since
+// each workgroup costs a fixed prologue and epilogue.  Chunks are whole
+// numbers of (waves x tile) token blocks.
 struct Geometry {
   int chunk;
   int n_split;
@@ -63,10 +68,14 @@ inline Geometry decode_geometry(int32_t batch, int32_t hkv, int64_t max_kv_len) 
   const int64_t unit = (int64_t)kDecodeWaves * kDecodeStep;
   const int64_t T = max_kv_len > 0 ? max_kv_len : 1;
   const int64_t pairs = (int64_t)batch * hkv;
-  const int64_t target_groups = 1024;     // 4 resident workgroups on each of 256 CUs
-  int64_t want = (target_groups + pairs - 1) / pairs;
-  if (want < 1) want = 1;
-  int64_t chunk = (T + want - 1) / want;
+  auto chunk_for = [&](int64_t groups) {
+    int64_t want = (groups + pairs - 1) / pairs;
+    if (want < 1) want = 1;
+    return (T + want - 1) / want;
+  };
+  int64_t chunk = chunk_for(2048);
+  const int64_t floor_chunk = std::min<int64_t>(8192, chunk_for(1024));
+  if (chunk < floor_chunk) chunk = floor_chunk;
   chunk = (chunk + unit - 1) / unit * unit;
   Geometry g;
   g.chunk = (int)chunk;

@@ -197,9 +197,9 @@ constexpr int ilog2() {
 // per CU can hold alongside each other next to their pair tables, at least 2
 // (double buffering).
 template <int D, int BITS>
-constexpr int stage_count() {
-  constexpr int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
-  constexpr int n = (80 * 1024 - table) / (kDecodeWaves * Stage<D, BITS>::BYTES);
+constexpr int stage_count(int extra) {
+  const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
+  const int n = (80 * 1024 - table - extra) / (kDecodeWaves * Stage<D, BITS>::BYTES);
   return n > 4 ? 4 : (n < 2 ? 2 : n);
 }
 
@@ -223,15 +223,19 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   constexpr int NROW = 2 * G;                // live rows/columns (hi + lo)
   using S = Stage<D, BITS>;
   constexpr int PRO_B = G * D * 4;                                  // prologue q~ staging
-  constexpr int NST = stage_count<D, BITS>();
+  constexpr int NST = stage_count<D, BITS>(PRO_B);
   static_assert((NST - 1) * S::LOADS < 64, "in-flight loads exceed the vmcnt range");
   constexpr int STG_B = kDecodeWaves * NST * S::BYTES;              // ring of stages per wave
   constexpr int RED_B = kDecodeWaves * G * (D + 4) * 4;             // wave states at the end
-  constexpr int MAIN_B = (PRO_B > STG_B ? (PRO_B > RED_B ? PRO_B : RED_B) : (STG_B > RED_B ? STG_B : RED_B));
+  constexpr int MAIN_B = STG_B > RED_B ? STG_B : RED_B;
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // Grid (KV head, sequence, split), KV head fastest: workgroups are handed to
+  // the 8 dies (XCDs) in turn by linear index, so each die gets an even mix
+  // of heads and sequences, and every die starts with the first, always
+  // fullest, context split of each pair (longest work first).
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
@@ -240,7 +244,43 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   constexpr int LSH = ilog2<REPL * 4>();     // table entry -> byte offset shift
   __shared__ uint32_t lut[NLEV * NLEV * REPL];
   __shared__ __attribute__((aligned(16))) char smem[MAIN_B];
-  float (*qs)[D] = reinterpret_cast<float (*)[D]>(smem);
+  // q~ staging in LDS of its own where it fits (then the first stages load
+  // during the prologue), else in the stage memory (loads after it)
+  constexpr bool EARLY = MAIN_B + NLEV * NLEV * REPL * 4 + PRO_B <= 160 * 1024;
+  __shared__ float qs_own[EARLY ? G : 1][EARLY ? D : 1];
+  float (*qs)[D] = EARLY ? reinterpret_cast<float (*)[D]>(&qs_own[0][0]) : reinterpret_cast<float (*)[D]>(smem);
+
+  // The workgroup's tokens [base, end) are dealt to the waves tile by tile
+  // (tile i to wave i mod 4), so that its waves finish together whatever the
+  // length: the workgroup holds its compute unit until its slowest wave ends.
+  const int base = split * a.chunk;
+  const int end = min(T, base + a.chunk);
+  const int len = end > base ? end - base : 0;
+  auto tile_t0 = [&](int k) { return base + (wave + kDecodeWaves * k) * kDecodeStep; };
+  const long long hrow = (long long)b * a.hkv + kvh;
+  const int32x4_t kr = make_rsrc(a.kc + hrow * a.kcap * ROWB, (uint32_t)(a.kcap * ROWB));
+  const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
+  const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
+  const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
+  char *stages = smem + wave * NST * S::BYTES;
+  const uint32_t stages_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(stages));
+  uint32_t goff[S::ROW_LOADS];
+#pragma unroll
+  for (int c = 0; c < S::ROW_LOADS; ++c) goff[c] = granule_offset<D, BITS>(c, lane);
+  // this wave's tiles k = 0, 1, ...: workgroup tiles wave + 4k
+  auto count = [&](int tiles) { return tiles > wave ? (tiles - wave + kDecodeWaves - 1) / kDecodeWaves : 0; };
+  const int n_tiles = count((len + kDecodeStep - 1) / kDecodeStep);
+  const int n_full = count(len / kDecodeStep);
+  // The first NST - 1 stages are requested before the prologue, whose work
+  // then overlaps their memory latency.
+  auto first_stages = [&] {
+    if (n_tiles > 0) {
+#pragma unroll
+      for (int i = 0; i < NST - 1; ++i)
+        load_stage<D, BITS>(stages_lds + i * S::BYTES, kr, vr, knr, vnr, tile_t0(i), i < n_tiles, lane, goff);
+    }
+  };
+  if constexpr (EARLY) first_stages();
 
   // ---- prologue: q~ = R q for this KV head's query heads --------------------
   for (int i = threadIdx.x; i < NLEV * NLEV * REPL; i += kThreads) lut[i] = a.lut[i / REPL];
@@ -298,19 +338,12 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
       qB[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
     }
   }
-  __syncthreads();                           // qs is reused as stage memory below
+  if constexpr (!EARLY) {
+    __syncthreads();                         // qs is reused as stage memory
+    first_stages();
+  }
 
   // ---- main loop ---------------------------------------------------------------
-  const int sub = a.chunk / kDecodeWaves;
-  const int begin = split * a.chunk + wave * sub;
-  const int end = min(T, begin + sub);
-  const long long hrow = (long long)b * a.hkv + kvh;
-  const int32x4_t kr = make_rsrc(a.kc + hrow * a.kcap * ROWB, (uint32_t)(a.kcap * ROWB));
-  const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
-  const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
-  const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
-  char *stages = smem + wave * NST * S::BYTES;
-  const uint32_t stages_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(stages));
   const int my_tile = lo_lane ? 1 : 0;
   const int vbit = VCB * j;                  // bit offset of this lane's codes in a row
   const float lo_mask = lo_lane ? 1.f : 0.f;
@@ -519,33 +552,23 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
                                                      O[nb], 0, 0, 0);
   };
 
-  uint32_t goff[S::ROW_LOADS];
-#pragma unroll
-  for (int c = 0; c < S::ROW_LOADS; ++c) goff[c] = granule_offset<D, BITS>(c, lane);
-
   // Ring of NST stages per wave: the next NST - 1 tiles are in flight while
   // one is processed.  Every iteration issues one stage (out of range past
   // the wave's last tile), so one fixed wait finds the oldest stage landed.
-  const int n_tiles = end > begin ? (end - begin + kDecodeStep - 1) / kDecodeStep : 0;
   if (n_tiles > 0) {
-#pragma unroll
-    for (int i = 0; i < NST - 1; ++i)
-      load_stage<D, BITS>(stages_lds + i * S::BYTES, kr, vr, knr, vnr, begin + i * kDecodeStep, i < n_tiles, lane,
-                          goff);
-    const int n_full = (end - begin) / kDecodeStep;
     int slot = 0;                            // stage of tile `it`
     for (int it = 0; it < n_full; ++it) {
       const int ahead = it + NST - 1;
       const int aslot = slot == 0 ? NST - 1 : slot - 1;     // (it + NST - 1) mod NST, processed last iteration
-      load_stage<D, BITS>(stages_lds + aslot * S::BYTES, kr, vr, knr, vnr, begin + ahead * kDecodeStep,
-                          ahead < n_tiles, lane, goff);
+      load_stage<D, BITS>(stages_lds + aslot * S::BYTES, kr, vr, knr, vnr, tile_t0(ahead), ahead < n_tiles, lane,
+                          goff);
       wait_vmem<(NST - 1) * S::LOADS>();
-      process(stages + slot * S::BYTES, begin + it * kDecodeStep, std::true_type{});
+      process(stages + slot * S::BYTES, tile_t0(it), std::true_type{});
       slot = slot == NST - 1 ? 0 : slot + 1;
     }
     wait_vmem<0>();                          // also drains the out-of-range stages before LDS is reused
     if (n_full < n_tiles)                    // the last, partial tile
-      process(stages + slot * S::BYTES, begin + n_full * kDecodeStep, std::false_type{});
+      process(stages + slot * S::BYTES, tile_t0(n_full), std::false_type{});
   }
   __syncthreads();                           // stage memory is reused for the wave states below
   float (*red_o)[G][D + 4] = reinterpret_cast<float (*)[G][D + 4]>(smem);
@@ -697,7 +720,7 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
 
 template <int D, int BITS, bool ARGMAX>
 hipError_t partial_dispatch_group(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)a.n_split, (unsigned)a.hkv, (unsigned)a.batch);
+  dim3 grid((unsigned)a.hkv, (unsigned)a.batch, (unsigned)a.n_split);
   switch (a.group) {
     case 1: hipLaunchKernelGGL((partial_kernel<D, BITS, 1, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((partial_kernel<D, BITS, 2, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;

@@ -133,7 +133,8 @@ size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch,
 /* Decode attention on packed K/V (RotaryQuant §3.4 Table 2, Appendix A).
  * Equivalent to iq_decode_attention_partial followed by
  * iq_decode_attention_merge on the same stream and workspace.
- * One query token per sequence; query head h reads KV head h / (Hq / H_kv).
+ * One query token per sequence; query head h reads KV head h / (Hq / H_kv);
+ * batch at most 65535 (IQ_ERR_UNSUPPORTED otherwise).
  *   q:          [batch][Hq][d] of q_dtype.
  *   k, v:       packed caches written by iq_quantize_append with this cfg.
  *   kv_len:     DEVICE int32 [batch]; attends rows [0, kv_len[b]) (includes a

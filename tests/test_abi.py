@@ -150,6 +150,8 @@ def test_decode_validation():
     assert call_decode(c, kv=0) == -1
     assert call_decode(c, scale=float("inf")) == -1
     assert call_decode(c, batch=0) == -1
+    assert call_decode(c, batch=65536) == -2                # grid limit
+    assert L.iq_decode_workspace_bytes(ctypes.byref(cc), 65536, 32, 16) == 0
     assert call_decode(cfg(d=64)) == -2
 
 
