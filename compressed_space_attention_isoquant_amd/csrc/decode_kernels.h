@@ -242,7 +242,9 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
 
   constexpr int REPL = lut_repl<BITS>();
   constexpr int LSH = ilog2<REPL * 4>();     // table entry -> byte offset shift
-  __shared__ uint32_t lut[NLEV * NLEV * REPL];
+  // aligned to its own size, so that the entry offset can be OR-ed into the
+  // lane's replica offset (pair below)
+  __shared__ __attribute__((aligned(NLEV * NLEV * REPL * 4))) uint32_t lut[NLEV * NLEV * REPL];
   __shared__ __attribute__((aligned(16))) char smem[MAIN_B];
   // q~ staging in LDS of its own where it fits (then the first stages load
   // during the prologue), else in the stage memory (loads after it)
@@ -352,18 +354,16 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   const int v_off = S::V_OFF + 4 * g4 * S::RS + (vbit >> 5) * 4;
   const int n_off = (16 * my_tile + 4 * g4) * 2;
   // byte address of this lane's replica of table entry 0
-  const uint32_t lut_base = lds_addr(lut) + (uint32_t)(lane % REPL) * 4u;
-  // table entry at the 2*BITS-bit field at bit `pos` of w: bit-field extract
-  // plus one shift-add for the address
+  const uint32_t lut_base = lds_addr(lut) | (uint32_t)(lane % REPL) * 4u;
+  // table entry at the 2*BITS-bit field at bit `pos` of w: the field is
+  // shifted to bit LSH and masked, and the lane's replica offset OR-ed in
+  // (the table is aligned to its size): a shift and one three-input bit
+  // operation, or the bit operation alone where pos = LSH
   auto pair = [&](uint32_t w, auto pos) -> uint32_t {
-    uint32_t idx = __builtin_amdgcn_ubfe(w, decltype(pos)::value, 2 * BITS);
-    // The empty asm keeps the extract a v_bfe_u32 followed by one shift-add
-    // (left alone, the compiler folds it into shift, and, add).  It emits no
-    // instruction: a real instruction written in asm here would escape the
-    // compiler's matrix-core hazard tracking (a VALU write to a register an
-    // in-flight MFMA still writes needs wait states that asm does not get).
-    asm("" : "+v"(idx));
-    const uint32_t addr = (idx << LSH) + lut_base;
+    constexpr int P = decltype(pos)::value;
+    constexpr uint32_t M = ((1u << (2 * BITS)) - 1u) << LSH;
+    const uint32_t f = P >= LSH ? (w >> (P - LSH)) : (w << (LSH - P));
+    const uint32_t addr = (f & M) | lut_base;
     return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
   };
 
