@@ -271,7 +271,7 @@ size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch, int32_t nu
   if (batch < 1 || batch > kMaxDecodeBatch || num_q_heads < 1 || max_kv_len < 0) return 0;
   if (num_q_heads % cfg->num_kv_heads) return 0;
   const iq::Geometry g = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
-  return (size_t)batch * num_q_heads * g.n_split * (cfg->head_dim + iq::kRecHeader) * sizeof(float);
+  return iq::decode_workspace_total(batch, num_q_heads, g.n_split, cfg->head_dim);
 }
 
 static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
@@ -335,6 +335,10 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
   a.qmul = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634 * std::ldexp(1.0, -e));
   a.argmax = track_argmax != 0;
   a.ws = static_cast<float *>(workspace);
+  a.order = iq::decode_ordered(batch, geo.n_split)
+                ? reinterpret_cast<int2 *>(static_cast<char *>(workspace) +
+                                           iq::decode_order_offset(batch, num_q_heads, geo.n_split, cfg->head_dim))
+                : nullptr;
   std::memset(a.lut, 0, sizeof(a.lut));
   fill_pair_table(cfg, e, a.lut);
   return hip_status(iq::launch_decode(cfg->head_dim, cfg->bits, a, stream));

@@ -38,6 +38,10 @@ struct DecodeArgs {
   float qmul;              // softmax_scale * log2(e) / 2^cexp, applied to R q
   int argmax;              // track the position of the largest score
   float *ws;               // records [batch][Hq][n_split][d + kRecHeader]
+  // Nullable.  Entry P (workgroup (kvh, P mod batch, P / batch)) holds the
+  // (sequence, split) it processes, (split << 16 | sequence, kv_len), in
+  // longest-first order of the splits' token counts.
+  int2 *order;
   uint32_t lut[256];       // fp16 pairs (c_i 2^cexp | c_k 2^cexp << 16) at index i | k << bits
 };
 
@@ -52,6 +56,25 @@ struct MergeArgs {
   int n_part;              // records per (sequence, query head)
   float oscale;            // 2^-cexp
 };
+
+// Workspace of the decode path: the split records, then (256-byte aligned)
+// the workgroup order when batch * n_split is at most kMaxOrderedPairs.
+constexpr int kMaxOrderedPairs = 4096;
+
+inline size_t decode_record_bytes(int32_t batch, int32_t hq, int n_split, int d) {
+  return (size_t)batch * hq * n_split * (d + kRecHeader) * sizeof(float);
+}
+inline size_t decode_order_offset(int32_t batch, int32_t hq, int n_split, int d) {
+  return (decode_record_bytes(batch, hq, n_split, d) + 255) / 256 * 256;
+}
+inline bool decode_ordered(int32_t batch, int n_split) {
+  return (int64_t)batch * n_split <= kMaxOrderedPairs;
+}
+inline size_t decode_workspace_total(int32_t batch, int32_t hq, int n_split, int d) {
+  return decode_ordered(batch, n_split)
+             ? decode_order_offset(batch, hq, n_split, d) + (size_t)batch * n_split * sizeof(int2)
+             : decode_record_bytes(batch, hq, n_split, d);
+}
 
 // Split-K geometry of the decode kernels.  About 2048 workgroups (8 per
 // compute unit, two resident at a time): with ragged context lengths the

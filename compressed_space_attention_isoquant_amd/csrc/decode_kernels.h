@@ -229,16 +229,26 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
   constexpr int RED_B = kDecodeWaves * G * (D + 4) * 4;             // wave states at the end
   constexpr int MAIN_B = STG_B > RED_B ? STG_B : RED_B;
 
-  // Grid (KV head, sequence, split), KV head fastest: workgroups are handed to
-  // the 8 dies (XCDs) in turn by linear index, so each die gets an even mix
-  // of heads and sequences, and every die starts with the first, always
-  // fullest, context split of each pair (longest work first).
+  // Grid (KV head, rank): workgroups are handed to the 8 dies (XCDs) in turn
+  // by linear index, KV head fastest, so every die gets an even mix.  With an
+  // order table (a.order) rank P runs the (sequence, split) of P-th most
+  // tokens, so each die works longest-first; without one, rank
+  // (sequence + batch * split) runs that pair (first splits, the fullest,
+  // first).
   const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
-  const int split = blockIdx.z;
+  int b, split, T;
+  if (a.order) {
+    const int2 o = a.order[blockIdx.y + gridDim.y * blockIdx.z];
+    b = __builtin_amdgcn_readfirstlane(o.x & 0xffff);
+    split = __builtin_amdgcn_readfirstlane(o.x >> 16);
+    T = __builtin_amdgcn_readfirstlane(o.y);
+  } else {
+    b = blockIdx.y;
+    split = blockIdx.z;
+    T = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int T = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
 
   constexpr int REPL = lut_repl<BITS>();
   constexpr int LSH = ilog2<REPL * 4>();     // table entry -> byte offset shift

@@ -125,7 +125,8 @@ int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch,
                   int32_t out_dtype, hipStream_t stream);
 
 /* Bytes of workspace iq_decode_attention needs for these sizes.  Returns 0 if
- * the arguments are invalid.  O(batch * Hq * splits * d) floats: never
+ * the arguments are invalid.  O(batch * Hq * splits * d) floats of split
+ * records plus 8 bytes per (sequence, split) for the work order: never
  * O(T * d) -- the decode path writes no dequantized K or V. */
 size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch,
                                  int32_t num_q_heads, int64_t max_kv_len);
