@@ -190,6 +190,32 @@ def test_split_geometry_invariance():
         check_outputs(f"split max_len={max_len}", got, lse, arg, ref, rlse, rarg, 2e-3)
 
 
+def test_many_short_sequences():
+    """4200 short ragged sequences (0..40 tokens): more (sequence, split)
+    pairs than the device-side longest-first ordering handles, so the
+    workgroups take their pairs in grid order.  Sampled sequences (first,
+    last, empty ones and a spread) against the oracle."""
+    d, bits, hq, hkv, batch, cap = 128, 3, 2, 1, 4200, 40
+    rng = np.random.default_rng(21)
+    lens = rng.integers(0, cap + 1, size=batch)
+    lens[0], lens[-1] = cap, 1
+    cfg, quats = make_config(d, bits, O.FAST, hkv)
+    k = rng.standard_normal((batch, cap, hkv, d)).astype(np.float16)
+    v = rng.standard_normal((batch, cap, hkv, d)).astype(np.float16)
+    q = rng.standard_normal((batch, hq, d)).astype(np.float16)
+    kc = quantize_rows(cfg, k)
+    vc = quantize_rows(cfg, v)
+    got, lse, arg = run_decode(cfg, q, kc, vc, lens, cap)
+    hk, hv = host_cache(kc), host_cache(vc)
+    idx = np.unique(np.concatenate([[0, batch - 1], np.flatnonzero(lens == 0)[:3],
+                                    rng.choice(batch, 12, replace=False)]))
+    ref, rlse, rarg = oracle_decode(q[idx], k[idx], v[idx], quats, cfg, lens[idx],
+                                    (hk[0][idx], hk[1][idx]), (hv[0][idx], hv[1][idx]))
+    check_outputs(f"many short sequences ({len(idx)} sampled)", got[idx], lse[idx], arg[idx], ref, rlse, rarg,
+                  2e-3)
+    assert np.all(got[lens == 0] == 0)
+
+
 def test_c5_batched_append_decode():
     """64 sequences, lengths U[1024, 32768], Hq=16, H_kv=8, d=256, 3-bit, Fast:
     each step appends one K and one V token per sequence then attends over
