@@ -123,6 +123,7 @@ def main():
     extras = {}
     if not args.no_extras:
         extras["uniform_32k"] = run_uniform_32k(torch, dev, max(10, args.steps // 5), args.warmup)
+        extras["prefill_compress"] = run_prefill_compress(torch, dev)
         if not args.no_stage1:
             extras["stage1"] = run_stage1(torch, dev)
     cpu = None
@@ -330,6 +331,49 @@ def run_uniform_32k(torch, dev, steps, warmup):
             "unit": "GB/s", "partial_kernel_ms": round(partial_ms, 5),
             "partial_achieved_gbs": round(achieved, 2), "frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("uniform_32k")}
+
+
+def run_prefill_compress(torch, dev, reps=5):
+    """Supplementary: bulk compression of a finished prefill (deferred
+    prefill, [RQ] Appendix C): 28 layers x (K, V) of [1][2048][8][128] fp16
+    appended with one quantize call each (n_new = 2048), 3-bit Full."""
+    from compressed_space_attention_isoquant_amd import binding as B
+    from compressed_space_attention_isoquant_amd import inputs
+
+    layers, T, hkv, d, bits = 28, 2048, 8, 128, 3
+    quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
+    cfg = B.Config(d, bits, B.IQ_FULL, hkv, quats, B.iq_codebook(bits, d))
+    rng = np.random.default_rng(6)
+    xs, caches = [], []
+    for layer in range(layers):
+        for idx in range(2):
+            ch = inputs.outlier_channels(rng, hkv, d)
+            xs.append(inputs.device_kv(60 + idx, layer, T, ch, d, dev).view(1, T, hkv, d))
+            caches.append(B.new_cache(1, hkv, T, d, bits, dev))
+    zero = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def run_all():
+        for x, c in zip(xs, caches):
+            B.iq_quantize_append(cfg, x, zero, c)
+
+    run_all()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = _events(torch)
+    e0.record(stream)
+    for _ in range(reps):
+        run_all()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nvec = layers * 2 * T * hkv
+    moved = nvec * (d * 2 + row_bytes(d, bits) + 2)
+    print(f"[bench] prefill compression {ms:.3f} ms for {layers} layers x K,V of {T}x{hkv}x{d} fp16",
+          file=sys.stderr, flush=True)
+    return {"workload": f"deferred-prefill compression: {layers} layers x (K, V) [1][{T}][{hkv}][{d}] fp16, "
+                        f"{bits}-bit Full, one append call of {T} tokens each",
+            "ms": round(ms, 4), "input_mib": round(nvec * d * 2 / 2 ** 20, 1),
+            "mvec_s": round(nvec / (ms * 1e-3) / 1e6, 1), "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
 
 
 def run_stage1(torch, dev):

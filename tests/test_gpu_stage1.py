@@ -159,6 +159,36 @@ def test_append_offsets_batches_and_heads():
             assert np.max(np.abs(got[b, :, h] - want)) <= 1e-5 * max(1.0, np.max(np.abs(want)))
 
 
+def test_prefill_bulk_compression():
+    """Deferred-prefill compression ([RQ] Appendix C): two sequences' 2,048
+    prefill tokens x 8 KV heads appended in one call each (n_new = 2048) at
+    different start rows; sampled (sequence, head) pairs against the oracle,
+    rows outside the appended ranges untouched."""
+    t = torch()
+    d, bits, hkv, batch, n, cap = 128, 3, 8, 2, 2048, 2100
+    cfg, quats = make_config(d, bits, O.FULL, hkv)
+    rng = np.random.default_rng(17)
+    ch = inputs.outlier_channels(rng, hkv, d)
+    scale = np.ones((hkv, d))
+    for h in range(hkv):
+        scale[h, ch[h]] = inputs.OUTLIER_SCALE
+    x = (rng.standard_normal((batch, n, hkv, d)) * scale).astype(np.float16)
+    starts = np.array([0, 52], np.int32)
+    cache = B.new_cache(batch, hkv, cap, d, bits, DEV)
+    B.iq_quantize_append(cfg, t.from_numpy(x).to(DEV), t.from_numpy(starts).to(DEV), cache)
+    codes, norms = host_cache(cache)
+    cb = O.codebook(bits, d)
+    for b, h in ((0, 0), (0, 7), (1, 3), (1, 6)):
+        ref = O.quantize(x[b, :, h], quats[h], cb, O.FULL)
+        rows = slice(starts[b], starts[b] + n)
+        _, nf, nfm = reconcile_codes(codes[b, h, rows], ref["codes"], ref["flags"], bits, d)
+        reconcile_norms(norms[b, h, rows], ref["norm16"], ref["norm_flags"])
+        untouched = np.ones(cap, bool)
+        untouched[rows] = False
+        assert not codes[b, h, untouched].any() and not norms[b, h, untouched].any()
+        say(f"prefill (b={b}, h={h}): flagged={nf} flagged_mismatch={nfm}")
+
+
 @pytest.mark.parametrize("idx,setting", list(enumerate(SETTINGS)))
 def test_c2_full_size_sampled(idx, setting):
     """2^20 unit vectors per setting quantized and dequantized on the GPU; the
