@@ -16,7 +16,9 @@ constexpr int kOrderThreads = 1024;
 
 // Longest-first order of the (sequence, split) pairs by token count
 // (min(chunk, kv_len - split * chunk), at least 0), ties in (split, sequence)
-// order: one workgroup, bitonic sort of 64-bit keys in LDS.
+// order: one workgroup.  The 64-bit keys (distinct) are ranked by counting
+// up to kOrderThreads pairs (one pass, one barrier), else sorted with a
+// bitonic network in LDS.
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *kv_len, int batch, int n_split,
                                                               int chunk, int2 *order) {
   __shared__ unsigned long long key[kMaxOrderedPairs];
@@ -34,6 +36,17 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *kv_
     key[i] = k;
   }
   __syncthreads();
+  if (n <= kOrderThreads) {
+    const int i = threadIdx.x;
+    if (i < n) {
+      const unsigned long long k = key[i];
+      int r = 0;
+      for (int m = 0; m < n; ++m) r += key[m] < k ? 1 : 0;
+      const int sp = i / batch, b = i - sp * batch;
+      order[r] = make_int2((sp << 16) | b, kv_len[b]);
+    }
+    return;
+  }
   for (int size = 2; size <= npad; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = threadIdx.x; i < npad; i += kOrderThreads) {
