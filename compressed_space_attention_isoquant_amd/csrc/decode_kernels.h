@@ -193,18 +193,42 @@ constexpr int ilog2() {
   return N <= 1 ? 0 : 1 + ilog2<N / 2>();
 }
 
-// Stages per wave: as many as fit (up to 4) in the LDS that two workgroups
-// per CU can hold alongside each other next to their pair tables, at least 2
-// (double buffering).
+// LDS layout: workgroups per CU (each holds one wave per SIMD) and stages
+// per wave.  Three workgroups per CU where each can still keep 3 stages per
+// wave next to its pair table and `extra` bytes (more waves hide latency
+// better than a deeper ring), else two; then as many stages as fit, up to 4,
+// at least 2 (double buffering).
+template <int D, int BITS>
+constexpr int stages_fitting(int budget, int extra) {
+  const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
+  return (budget - table - extra) / (kDecodeWaves * Stage<D, BITS>::BYTES);
+}
+
+template <int D, int BITS>
+constexpr int resident_groups(int extra) {
+  return stages_fitting<D, BITS>(160 * 1024 / 3, extra) >= 3 ? 3 : 2;
+}
+
 template <int D, int BITS>
 constexpr int stage_count(int extra) {
-  const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
-  const int n = (80 * 1024 - table - extra) / (kDecodeWaves * Stage<D, BITS>::BYTES);
+  const int n = stages_fitting<D, BITS>(160 * 1024 / resident_groups<D, BITS>(extra), extra);
   return n > 4 ? 4 : (n < 2 ? 2 : n);
 }
 
+// Waves per SIMD the register allocation is held to, matching the LDS
+// layout: three where three workgroups share a CU (at most 168 registers per
+// lane), two where the LDS of two fits (head_dim <= 256; 256 registers),
+// else no constraint.
+template <int D, int BITS>
+constexpr int partial_waves(int extra) {
+  const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
+  const int lds = table + extra + kDecodeWaves * stage_count<D, BITS>(extra) * Stage<D, BITS>::BYTES;
+  return resident_groups<D, BITS>(extra) == 3 ? 3 : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
+}
+
 template <int D, int BITS, int G, bool ARGMAX>
-__global__ __launch_bounds__(kThreads) void partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(partial_waves<D, BITS>(G * D * 4))))
+void partial_kernel(DecodeArgs a) {
   constexpr int NLEV = 1 << BITS;
   constexpr int KS = D / 32;                 // k-steps of the score product
   constexpr int NB = D / 16;                 // 16-column blocks of the value product
