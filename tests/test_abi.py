@@ -195,3 +195,38 @@ def test_partial_and_merge_validation():
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 5, None, None, 0x7000, need, None) == -2
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 0, None, 0x9002, 0x7000, need, None) == -3
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 0, None, None, 0x7000, need - 4, None) == -4
+
+
+def expected_workspace(batch, hq, hkv, d, max_len):
+    """Workspace bytes from the documented split rule: about 2048 workgroups,
+    chunks of at least 8192 tokens while that still gives 1024 workgroups,
+    whole 128-token blocks; records of d + 4 floats per (sequence, query
+    head, split), then (256-byte aligned) 8 bytes per (sequence, split) of
+    work order when there are at most 4096 such pairs."""
+    T = max(max_len, 1)
+    pairs = batch * hkv
+
+    def chunk_for(groups):
+        want = max(1, -(-groups // pairs))
+        return -(-T // want)
+
+    chunk = max(chunk_for(2048), min(8192, chunk_for(1024)))
+    chunk = -(-chunk // 128) * 128
+    n_split = -(-T // chunk)
+    rec = batch * hq * n_split * (d + 4) * 4
+    if batch * n_split <= 4096:
+        return -(-rec // 256) * 256 + batch * n_split * 8
+    return rec
+
+
+@pytest.mark.parametrize("batch,hq,hkv,d,max_len", [
+    (64, 16, 8, 256, 32768), (64, 32, 4, 128, 32768), (1, 32, 4, 128, 8192), (1, 8, 8, 128, 131072),
+    (4200, 2, 1, 128, 40), (3, 8, 2, 512, 1), (256, 8, 8, 256, 32768), (2, 4, 4, 128, 0)])
+def test_decode_workspace_geometry(batch, hq, hkv, d, max_len):
+    """The host's split geometry, observed through the workspace size."""
+    L = B.lib()
+    c = cfg(d=d, hkv=hkv)
+    cc = c.c()
+    got = L.iq_decode_workspace_bytes(ctypes.byref(cc), batch, hq, max_len)
+    assert got == expected_workspace(batch, hq, hkv, d, max_len)
+
