@@ -2,11 +2,13 @@
 // split-K over the context, scores and value accumulation on fp16 matrix
 // cores (v_mfma_f32_16x16x32_f16) directly from the packed codes.
 //
-// partial kernel: one workgroup of 4 waves per (split, KV head, sequence).
+// partial kernel: one workgroup of 4 waves per (split, KV head, sequence);
+//   the order kernel (decode.hip) may assign the (sequence, split) pairs
+//   longest-first.
 //   Prologue: q~ = R q for the G query heads of the KV head (WHT butterflies
 //   and SO(4) blocks in LDS), scaled, split into fp16 hi + lo parts and held
 //   in registers as the B operand of the score product.
-//   Each wave walks its token range 32 tokens at a time:
+//   The split's 32-token tiles are dealt to the waves round-robin; per tile:
 //     scores  S^T (16 tokens x 16 columns) = C_K (16 x d) . Q~^T (d x 16) for
 //             two 16-token tiles; column j < G holds q~_hi of head j, column
 //             G + j holds q~_lo of head j, so S_hi + S_lo is the full-precision
