@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-stage1", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="headline and uniform 32K decode only (the profiled command)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.summarize_counters:
@@ -123,8 +125,10 @@ def main():
     extras = {}
     if not args.no_extras:
         extras["uniform_32k"] = run_uniform_32k(torch, dev, max(10, args.steps // 5), args.warmup)
-        extras["prefill_compress"] = run_prefill_compress(torch, dev)
-        if not args.no_stage1:
+        if not args.decode_only:
+            extras["c3_latency"] = run_c3_latency(torch, dev)
+            extras["prefill_compress"] = run_prefill_compress(torch, dev)
+        if not args.no_stage1 and not args.decode_only:
             extras["stage1"] = run_stage1(torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
@@ -157,6 +161,8 @@ def main():
         },
         "pct_hbm_peak": round(100.0 * head["value"] / HBM_PEAK_GBS, 2),
         "partial_kernel_ms": round(head["partial_ms"], 5),
+        "partial_kernel_ms_spread": {"std": round(head["partial_ms_std"], 5), "min": round(head["partial_ms_min"], 5),
+                                     "cv": round(head["partial_ms_std"] / head["partial_ms"], 4)},
         "roofline": {
             "bound": "hbm",
             "achieved": round(head["achieved"], 2),
@@ -248,7 +254,8 @@ def run_headline(torch, dev, args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    per_step = np.array([a.elapsed_time(b) for a, b in events])
+    partial_ms = float(per_step.mean())
     kv = np.array([float((lens + g).sum()) * hkv * 2 * (rb + 2) for g in range(args.warmup, n_total)])
     qo = batch * hq * d * 2
     attn_bytes = kv + 2 * qo                 # packed K/V with norms read, q read, o written
@@ -259,7 +266,8 @@ def run_headline(torch, dev, args):
           f"{achieved:.1f} GB/s", file=sys.stderr, flush=True)
     return dict(value=value, ms_per_step=ms_per_step, partial_ms=partial_ms, achieved=achieved,
                 attn_bytes_per_step=attn_bytes.mean(), partial_bytes_per_launch=partial_bytes.mean(),
-                lengths=lens)
+                lengths=lens, partial_ms_std=float(per_step.std()),
+                partial_ms_min=float(per_step.min()))
 
 
 def run_uniform_32k(torch, dev, steps, warmup):
@@ -331,6 +339,55 @@ def run_uniform_32k(torch, dev, steps, warmup):
             "unit": "GB/s", "partial_kernel_ms": round(partial_ms, 5),
             "partial_achieved_gbs": round(achieved, 2), "frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("uniform_32k")}
+
+
+def run_c3_latency(torch, dev, reps=20):
+    """Supplementary: one sequence of 8,192 tokens, 32 query / 4 KV heads,
+    d=128, 3-bit Full (3.3 MB of packed K/V: it fits the 256 MB last-level
+    cache).  Latency of one decode call (order, partial, merge), warm (back
+    to back) and cold (512 MiB written between calls, events around the
+    call only)."""
+    from compressed_space_attention_isoquant_amd import binding as B
+    from compressed_space_attention_isoquant_amd import inputs
+
+    T, hq, hkv, d, bits = 8192, 32, 4, 128, 3
+    quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
+    cfg = B.Config(d, bits, B.IQ_FULL, hkv, quats, B.iq_codebook(bits, d))
+    rng = np.random.default_rng(3)
+    kc = B.new_cache(1, hkv, T, d, bits, dev)
+    vc = B.new_cache(1, hkv, T, d, bits, dev)
+    zero = torch.zeros((1,), dtype=torch.int32, device=dev)
+    for cache, idx in ((kc, 0), (vc, 1)):
+        ch = inputs.outlier_channels(rng, hkv, d)
+        B.iq_quantize_append(cfg, inputs.device_kv(70 + idx, 0, T, ch, d, dev).view(1, T, hkv, d), zero, cache)
+    q = inputs.device_normal(72, 0, (1, hq, d), dev, torch.float16)
+    kv_len = torch.full((1,), T, dtype=torch.int32, device=dev)
+    out = torch.empty((1, hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty((B.iq_decode_workspace_bytes(cfg, 1, hq, T),), dtype=torch.uint8, device=dev)
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(cold):
+        ts = []
+        for _ in range(reps):
+            if cold:
+                flush.fill_(1)
+            e0, e1 = _events(torch)
+            e0.record(stream)
+            B.iq_decode_attention(cfg, q, kc, vc, kv_len, T, 1.0 / math.sqrt(d), out, None, None, ws)
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+
+    timed(False)
+    warm, cold = timed(False), timed(True)
+    del flush
+    print(f"[bench] C3 decode latency warm {warm:.1f} us, cold {cold:.1f} us", file=sys.stderr, flush=True)
+    return {"workload": "one sequence of 8192 tokens, 32 query / 4 KV heads, d=128, 3-bit Full, fp16 q, "
+                        "fp32 out; median of 20 calls",
+            "warm_us": round(warm, 1), "cold_us": round(cold, 1),
+            "packed_kv_bytes": int(T * hkv * 2 * (row_bytes(d, bits) + 2))}
 
 
 def run_prefill_compress(torch, dev, reps=5):
@@ -454,9 +511,9 @@ def summarize_counters(fetch_csv, write_csv):
     out = {"commands": [
                "export TMPDIR=/tmp",
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o f -- python3 bench.py "
-               "--steps 3 --warmup 1 --no-cpu-baseline --no-stage1 --calibrate-copy",
+               "--steps 3 --warmup 1 --no-cpu-baseline --decode-only --calibrate-copy",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o w -- python3 bench.py "
-               "--steps 3 --warmup 1 --no-cpu-baseline --no-stage1 --calibrate-copy",
+               "--steps 3 --warmup 1 --no-cpu-baseline --decode-only --calibrate-copy",
                "python3 bench.py --summarize-counters gpurun_out/pmc_fetch/f_counter_collection.csv "
                "gpurun_out/pmc_write/w_counter_collection.csv"],
            "kernel_source_hash": kernel_source_hash(),
