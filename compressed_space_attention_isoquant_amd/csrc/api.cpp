@@ -335,7 +335,9 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
   a.qmul = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634 * std::ldexp(1.0, -e));
   a.argmax = track_argmax != 0;
   a.ws = static_cast<float *>(workspace);
-  a.order = iq::decode_ordered(batch, geo.n_split)
+  // One sequence: split order is already longest first (only the last split
+  // can be short), so the ranking launch is skipped.
+  a.order = batch > 1 && iq::decode_ordered(batch, geo.n_split)
                 ? reinterpret_cast<int2 *>(static_cast<char *>(workspace) +
                                            iq::decode_order_offset(batch, num_q_heads, geo.n_split, cfg->head_dim))
                 : nullptr;
