@@ -37,18 +37,6 @@ __device__ __forceinline__ float4 so4_inv(float4 w, float4 qL, float4 qR) {
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
