@@ -9,6 +9,8 @@ FP64 and cast with round-to-nearest-even):
 
 * quaternions: seed 0 for every workload; q = g / ||g|| with g ~ N(0, I_4)
   drawn as an array of shape (H_kv, d/4, 2, 4), cast to fp32 (uniform on S^3).
+* planar pair rotations: seed 0; z = g / |g| with g ~ N(0, I_2) drawn as an
+  array of shape (H_kv, d/2, 2), cast to fp32 (uniform angle).
 * stage-1 vectors: entries N(0, 1), each vector L2-normalised in FP64, cast
   to the I/O dtype.
 * decode K/V: entries N(0, 1) with, per KV head, 4 channels drawn without
@@ -37,6 +39,26 @@ def quaternions(num_kv_heads: int, head_dim: int, seed: int = QUATERNION_SEED) -
     g = rng.standard_normal((num_kv_heads, head_dim // 4, 2, 4))
     q = g / np.linalg.norm(g, axis=-1, keepdims=True)
     return q.astype(np.float32)
+
+
+def planar_rotations(num_kv_heads: int, head_dim: int, seed: int = QUATERNION_SEED) -> np.ndarray:
+    """(H_kv, d/2, 2) fp32 unit complex numbers (cos, sin), one per pair of
+    coordinates: z = g / |g| with g ~ N(0, I_2), i.e. a uniform angle."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((num_kv_heads, head_dim // 2, 2))
+    z = g / np.linalg.norm(g, axis=-1, keepdims=True)
+    return z.astype(np.float32)
+
+
+PLANAR = 2
+
+
+def rotation_params(num_kv_heads: int, head_dim: int, variant: int, seed: int = QUATERNION_SEED) -> np.ndarray:
+    """The block-rotation parameters a variant reads: quaternion pairs for
+    Full (0) and Fast (1), pair rotations for Planar (2)."""
+    if variant == PLANAR:
+        return planar_rotations(num_kv_heads, head_dim, seed)
+    return quaternions(num_kv_heads, head_dim, seed)
 
 
 def unit_vectors(n: int, head_dim: int, dtype, seed: int) -> np.ndarray:

@@ -16,6 +16,11 @@ design notes of the repository):
   q_R`` in (w, x, y, z) order.  Full: v -> q_L v conj(q_R); Fast keeps the left
   isoclinic factor only: v -> q_L v.  The FP32 quaternions given as input are
   re-normalised in FP64 here.
+* Planar (the 2-D special case): 0-based contiguous pairs x[2i : 2i+2], each
+  read as the complex number x[2i] + x[2i+1] i and multiplied by the unit
+  complex number stored at ``params[h, i] = (cos, sin)`` (re-normalised in
+  FP64).  In two dimensions the left and right factors commute, so one
+  rotation per pair is all there is; the WHT comes first as for SO(4).
 * Quantiser: thresholds t_k = (c_k + c_{k+1}) / 2 computed in FP64 from the
   FP32 centroids; code = number of thresholds strictly below the value (a tie
   takes the lower code).  Elements within 1e-6 of a threshold are flagged.
@@ -35,6 +40,7 @@ import numpy as np
 __all__ = [
     "FULL",
     "FAST",
+    "PLANAR",
     "BOUNDARY_BAND",
     "lloyd_max_gaussian",
     "codebook",
@@ -46,6 +52,8 @@ __all__ = [
     "unit_quaternions",
     "so4_forward",
     "so4_inverse",
+    "planar_forward",
+    "planar_inverse",
     "rotate",
     "rotate_inverse",
     "rotate_scalar",
@@ -63,6 +71,7 @@ __all__ = [
 
 FULL = 0
 FAST = 1
+PLANAR = 2
 
 # Width of the decision-boundary band: an element whose rotated value lies
 # closer than this to a threshold may legitimately take either neighbouring
@@ -235,14 +244,56 @@ def so4_inverse(w: np.ndarray, quats: np.ndarray, variant: int) -> np.ndarray:
     return out.reshape(w.shape)
 
 
+def _unit_complex(params: np.ndarray) -> np.ndarray:
+    """Stored (cos, sin) pairs promoted to FP64 unit complex numbers."""
+    p = np.asarray(params, dtype=np.float64)
+    z = p[..., 0] + 1j * p[..., 1]
+    return z / np.abs(z)
+
+
+def planar_forward(y: np.ndarray, params: np.ndarray) -> np.ndarray:
+    """Block-diagonal SO(2) rotation of the last axis (the 2-D special case
+    of the IsoQuant framework, IsoQuant abstract): pair i, read as the
+    complex number y[2i] + y[2i+1] i, is multiplied by z_i.
+
+    ``params`` has shape (d/2, 2) (one head) and broadcasts over leading axes.
+    """
+    z = _unit_complex(params)
+    y = np.asarray(y, dtype=np.float64)
+    v = y[..., 0::2] + 1j * y[..., 1::2]
+    w = z * v
+    out = np.empty(y.shape, dtype=np.float64)
+    out[..., 0::2] = w.real
+    out[..., 1::2] = w.imag
+    return out
+
+
+def planar_inverse(w: np.ndarray, params: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`planar_forward`: multiplication by conj(z_i)."""
+    z = _unit_complex(params)
+    w = np.asarray(w, dtype=np.float64)
+    v = w[..., 0::2] + 1j * w[..., 1::2]
+    u = np.conj(z) * v
+    out = np.empty(w.shape, dtype=np.float64)
+    out[..., 0::2] = u.real
+    out[..., 1::2] = u.imag
+    return out
+
+
 def rotate(x: np.ndarray, quats: np.ndarray, variant: int) -> np.ndarray:
-    """R x = R_SO(4)(H_d x) (RotaryQuant eq. (2))."""
+    """R x = R_blocks(H_d x) (RotaryQuant eq. (2)); the block rotation is
+    SO(4) (Full, Fast; ``quats`` (d/4, 2, 4)) or planar (``quats`` holding
+    the (d/2, 2) pair rotations)."""
+    if variant == PLANAR:
+        return planar_forward(wht(x), quats)
     return so4_forward(wht(x), quats, variant)
 
 
 def rotate_inverse(x: np.ndarray, quats: np.ndarray, variant: int) -> np.ndarray:
-    """R^T x = H_d (R_SO(4)^T x): the same butterfly plus the block transpose
+    """R^T x = H_d (R_blocks^T x): the same butterfly plus the block transpose
     (RotaryQuant §3.4)."""
+    if variant == PLANAR:
+        return wht(planar_inverse(x, quats))
     return wht(so4_inverse(x, quats, variant))
 
 
@@ -251,7 +302,7 @@ def rotate_scalar(x, quats, variant):
 
     Counts one operation per addition/subtraction in the WHT butterflies, the
     1/sqrt(d) scalings separately, and one per real multiplication in the
-    quaternion products of the SO(4) stage.  Returns (Rx as FP64 array,
+    quaternion products of the SO(4) stage (in the 2x2 rotations, Planar).  Returns (Rx as FP64 array,
     counts dict).  Used to pin the per-vector cost figures the pages print.
     """
     counts = {"wht_addsub": 0, "wht_scale_mul": 0, "so4_mul": 0, "so4_addsub": 0}
@@ -281,6 +332,17 @@ def rotate_scalar(x, quats, variant):
         j = products[0][2] - products[1][3] + products[2][0] + products[3][1]
         k = products[0][3] + products[1][2] - products[2][1] + products[3][0]
         return [w, i, j, k]
+
+    if variant == PLANAR:
+        z = _unit_complex(quats)
+        out = []
+        for i in range(d // 2):
+            a, b = float(z[i].real), float(z[i].imag)
+            x0, x1 = y[2 * i], y[2 * i + 1]
+            out.extend([a * x0 - b * x1, b * x0 + a * x1])
+            counts["so4_mul"] += 4
+            counts["so4_addsub"] += 2
+        return np.array(out), counts
 
     q = unit_quaternions(quats)
     out = []
@@ -319,7 +381,9 @@ def quantize(x, quats, centroids, variant):
     """Algorithm 1 (RotaryQuant §3.2) on vectors along the last axis.
 
     ``x``: (..., d) fp16/fp32/FP64 input, promoted exactly to FP64.
-    ``quats``: (d/4, 2, 4) for the head these vectors belong to.
+    ``quats``: the block-rotation parameters of the head these vectors
+    belong to: (d/4, 2, 4) quaternion pairs (Full, Fast) or (d/2, 2) pair
+    rotations (Planar).
     ``centroids``: FP32 codebook (2**b values, ascending).
 
     Returns a dict with ``codes`` (int64, (..., d)), ``norm16`` (uint16 fp16

@@ -22,6 +22,15 @@ from compressed_space_attention_isoquant_amd import inputs
 
 
 def dense_rotation(quats_head, variant):
+    if variant == O.PLANAR:
+        d = quats_head.shape[0] * 2
+        H = np.array([[(-1.0) ** bin(i & j).count("1") for j in range(d)] for i in range(d)]) / math.sqrt(d)
+        z = quats_head.astype(np.float64)
+        z = z / np.linalg.norm(z, axis=-1, keepdims=True)
+        B = np.zeros((d, d))
+        for i in range(d // 2):
+            B[2 * i:2 * i + 2, 2 * i:2 * i + 2] = [[z[i, 0], -z[i, 1]], [z[i, 1], z[i, 0]]]
+        return B @ H
     d = quats_head.shape[0] * 4
     H = np.array([[(-1.0) ** bin(i & j).count("1") for j in range(d)] for i in range(d)]) / math.sqrt(d)
     q = quats_head.astype(np.float64)
@@ -40,7 +49,7 @@ def dense_rotation(quats_head, variant):
 
 def make_case(seed, T, hq, hkv, d, bits, variant, scale_kv=1.0):
     rng = np.random.default_rng(seed)
-    quats = inputs.quaternions(hkv, d, seed=seed)
+    quats = inputs.rotation_params(hkv, d, variant, seed=seed)
     cb = O.codebook(bits, d)
     k = (rng.standard_normal((hkv, T, d)) * scale_kv).astype(np.float16)
     v = (rng.standard_normal((hkv, T, d)) * scale_kv).astype(np.float16)
@@ -65,7 +74,7 @@ def run(case, fn=O.attend, kv_len=None, scale=None):
               case["cb"], case["bits"], case["variant"], scale, kv_len)
 
 
-@pytest.mark.parametrize("variant", [O.FULL, O.FAST])
+@pytest.mark.parametrize("variant", [O.FULL, O.FAST, O.PLANAR])
 @pytest.mark.parametrize("T", [1, 2, 5, 8])
 def test_brute_force_tiny(variant, T):
     d, hq, hkv, bits = 32, 4, 2, 3
@@ -143,7 +152,7 @@ def test_empty_context_and_prefix_length():
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("variant", [O.FULL, O.FAST])
+@pytest.mark.parametrize("variant", [O.FULL, O.FAST, O.PLANAR])
 @pytest.mark.parametrize("d,hq,hkv", [(128, 32, 4), (256, 16, 8)])
 def test_rotated_space_equals_reconstruct_then_compute(variant, d, hq, hkv):
     c = make_case(5 + d, 300, hq, hkv, d, 3, variant, scale_kv=4.0)

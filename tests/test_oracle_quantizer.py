@@ -168,10 +168,10 @@ def quant_mse_closed_form(d, c):
 
 @pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("variant", [O.FULL, O.FAST])
+@pytest.mark.parametrize("variant", [O.FULL, O.FAST, O.PLANAR])
 def test_stage1_mse_matches_closed_form(d, bits, variant):
     n = 4096
-    q = inputs.quaternions(1, d)[0]
+    q = inputs.rotation_params(1, d, variant)[0]
     c = O.codebook(bits, d)
     x = inputs.unit_vectors(n, d, np.float32, seed=100 + d + bits)
     r = O.quantize(x, q, c, variant)

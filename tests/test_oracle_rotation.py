@@ -1,9 +1,11 @@
-"""Pins for the oracle's rotation R = R_SO(4) o H_d (CPU only).
+"""Pins for the oracle's rotation R = R_blocks o H_d (CPU only).
 
 Each check compares the oracle with something other than itself: the explicit
 Sylvester matrix, scipy's Hadamard routine, the quaternion multiplication
 table, textbook left/right multiplication matrices, group identities, and the
 operation counts printed on the pages (RotaryQuant §3.2, IsoQuant abstract).
+The planar (2-D) blocks are pinned as the SO(2) x SO(2) subgroup of the SO(4)
+blocks, through the already pinned Hamilton product, and by angle addition.
 """
 
 import math
@@ -162,17 +164,20 @@ def test_identity_quaternions_and_known_rotation():
     assert np.allclose(O.so4_forward(J, rot, O.FAST), [0, 0, math.cos(th), math.sin(th)], atol=1e-15)
 
 
-@pytest.mark.parametrize("variant", [O.FULL, O.FAST])
+@pytest.mark.parametrize("variant", [O.FULL, O.FAST, O.PLANAR])
 @pytest.mark.parametrize("d", [128, 256, 512])
 def test_rotation_inverse_and_inner_products(variant, d):
-    q = inputs.quaternions(1, d)[0]
+    q = inputs.rotation_params(1, d, variant)[0]
     rng = np.random.default_rng(d + variant)
     x = rng.standard_normal((64, d))
     y = rng.standard_normal((64, d))
     rx = O.rotate(x, q, variant)
     ry = O.rotate(y, q, variant)
     assert np.max(np.abs(O.rotate_inverse(rx, q, variant) - x)) < 1e-12
-    assert np.max(np.abs(O.so4_inverse(O.so4_forward(x, q, variant), q, variant) - x)) < 1e-12
+    if variant == O.PLANAR:
+        assert np.max(np.abs(O.planar_inverse(O.planar_forward(x, q), q) - x)) < 1e-12
+    else:
+        assert np.max(np.abs(O.so4_inverse(O.so4_forward(x, q, variant), q, variant) - x)) < 1e-12
     # RotaryQuant Appendix A: <Rq, Rk> = <q, k>
     assert np.allclose(np.sum(rx * ry, axis=-1), np.sum(x * y, axis=-1), rtol=0, atol=1e-12 * d)
     assert np.allclose(np.linalg.norm(rx, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
@@ -227,3 +232,70 @@ def test_stored_parameter_count(golden):
     q = inputs.quaternions(1, 128)[0]
     assert q.size == g["stored_quaternion_floats_d128"]["value"]
     assert (128 // 4) * 6 == g["dof_d128"]["value"]
+
+
+def planar_params(angles):
+    return np.stack([np.cos(angles), np.sin(angles)], axis=-1)
+
+
+def test_planar_is_the_so2_x_so2_subgroup_of_so4():
+    """Turning the pairs (0, 1) and (2, 3) of a block by th0 and th1 is the
+    Full SO(4) map with q_L = cos a + i sin a, q_R = cos b + i sin b,
+    a = (th0 + th1) / 2, b = (th1 - th0) / 2: left multiplication by q_L
+    turns both pairs by a, right multiplication by conj(q_R) turns them by -b
+    and +b.  Equal angles give the Fast map with q_L = cos th + i sin th."""
+    rng = np.random.default_rng(31)
+    for _ in range(50):
+        th = rng.uniform(-math.pi, math.pi, 2)
+        a, b = (th[0] + th[1]) / 2, (th[1] - th[0]) / 2
+        qp = np.array([[[math.cos(a), math.sin(a), 0, 0], [math.cos(b), math.sin(b), 0, 0]]])
+        v = rng.standard_normal((6, 4))
+        w = O.planar_forward(v, planar_params(th))
+        assert np.max(np.abs(w - O.so4_forward(v, qp, O.FULL))) < 1e-14
+        same = planar_params(np.array([th[0], th[0]]))
+        qf = np.array([[[math.cos(th[0]), math.sin(th[0]), 0, 0], [1, 0, 0, 0]]])
+        assert np.max(np.abs(O.planar_forward(v, same) - O.so4_forward(v, qf, O.FAST))) < 1e-14
+        assert np.max(np.abs(O.planar_inverse(w, planar_params(th)) - O.so4_inverse(w, qp, O.FULL))) < 1e-14
+
+
+def test_planar_known_rotations_and_angle_addition():
+    v = np.random.default_rng(32).standard_normal((5, 8))
+    # angle 0: identity; a quarter turn maps (x, y) to (-y, x) exactly
+    assert np.array_equal(O.planar_forward(v, planar_params(np.zeros(4))), v)
+    quarter = O.planar_forward(v, np.tile([0.0, 1.0], (4, 1)))
+    assert np.array_equal(quarter[:, 0::2], -v[:, 1::2]) and np.array_equal(quarter[:, 1::2], v[:, 0::2])
+    # e_0 goes to (cos th, sin th); rotations compose by adding angles
+    th = np.array([0.3, -1.1, 2.0, 0.7])
+    e0 = np.zeros(8)
+    e0[0] = 1.0
+    assert np.allclose(O.planar_forward(e0, planar_params(th))[:2], [math.cos(0.3), math.sin(0.3)], atol=1e-16)
+    ph = np.array([1.4, 0.2, -0.6, -2.5])
+    two = O.planar_forward(O.planar_forward(v, planar_params(th)), planar_params(ph))
+    assert np.max(np.abs(two - O.planar_forward(v, planar_params(th + ph)))) < 1e-14
+    # unnormalised stored pairs are re-normalised
+    assert np.max(np.abs(O.planar_forward(v, 3.0 * planar_params(th)) - O.planar_forward(v, planar_params(th)))) < 1e-15
+
+
+def test_planar_rotation_as_explicit_dense_matrix():
+    d = 32
+    z = inputs.planar_rotations(1, d, seed=9)[0].astype(np.float64)
+    z /= np.linalg.norm(z, axis=-1, keepdims=True)
+    B = np.zeros((d, d))
+    for i in range(d // 2):
+        c, s = z[i]
+        B[2 * i:2 * i + 2, 2 * i:2 * i + 2] = [[c, -s], [s, c]]
+    assert abs(np.linalg.det(B) - 1.0) < 1e-12
+    R = B @ sylvester(d)
+    x = np.random.default_rng(2).standard_normal((8, d))
+    assert np.max(np.abs(O.rotate(x, z, O.PLANAR) - x @ R.T)) < 1e-13
+    assert np.max(np.abs(O.rotate_inverse(x, z, O.PLANAR) - x @ R)) < 1e-13
+
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_planar_multiply_count(d):
+    # a 2x2 rotation per pair: 4 real products, i.e. 2 per coordinate (2d)
+    z = inputs.planar_rotations(1, d)[0]
+    x = np.random.default_rng(d).standard_normal(d)
+    y, c = O.rotate_scalar(x, z, O.PLANAR)
+    assert c["so4_mul"] == 2 * d and c["wht_addsub"] == d * int(math.log2(d))
+    assert np.max(np.abs(y - O.rotate(x, z, O.PLANAR))) < 1e-13
