@@ -443,10 +443,11 @@ def run_stage1(torch, dev):
     stream = torch.cuda.current_stream()
     rates = {}
     for d in (128, 256, 512):
-        quats = torch.from_numpy(inputs.quaternions(1, d)).to(dev)
+        params = {v: torch.from_numpy(inputs.rotation_params(1, d, v)).to(dev)
+                  for v in (B.IQ_FULL, B.IQ_FAST, B.IQ_PLANAR)}
         for bits in (2, 3, 4):
-            for variant, vname in ((B.IQ_FULL, "full"), (B.IQ_FAST, "fast")):
-                cfg = B.Config(d, bits, variant, 1, quats, B.iq_codebook(bits, d))
+            for variant, vname in ((B.IQ_FULL, "full"), (B.IQ_FAST, "fast"), (B.IQ_PLANAR, "planar")):
+                cfg = B.Config(d, bits, variant, 1, params[variant], B.iq_codebook(bits, d))
                 c1 = B.new_cache(1, 1, n, d, bits, dev)
                 sp = torch.zeros((1,), dtype=torch.int32, device=dev)
                 for dt, dname in ((torch.float16, "fp16"), (torch.float32, "fp32")):
@@ -474,11 +475,12 @@ def run_stage1(torch, dev):
                         "dequantize_gbs": round(io / (dms * 1e-3) / 1e9, 1)}
                     del x, o
                 del c1
-    head = rates["d128_b3_full_fp16"]
-    print(f"[bench] stage-1 d=128 b=3 Full fp16: quantize {head['quantize_mvec_s']} Mvec/s, "
-          f"dequantize {head['dequantize_mvec_s']} Mvec/s", file=sys.stderr, flush=True)
+    for vname in ("full", "fast", "planar"):
+        r = rates[f"d128_b3_{vname}_fp16"]
+        print(f"[bench] stage-1 d=128 b=3 {vname} fp16: quantize {r['quantize_mvec_s']} Mvec/s, "
+              f"dequantize {r['dequantize_mvec_s']} Mvec/s", file=sys.stderr, flush=True)
     return {"workload": "2^20 unit vectors per setting, d in {128,256,512} x bits in {2,3,4} x "
-                        "{Full,Fast} x {fp16,fp32} I/O", "rates": rates}
+                        "{Full,Fast,Planar} x {fp16,fp32} I/O", "rates": rates}
 
 
 # Kernels whose HBM traffic is recorded, by the workload they run in.

@@ -16,7 +16,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libiq.so")
 
 IQ_OK = 0
-IQ_FULL, IQ_FAST = 0, 1
+IQ_FULL, IQ_FAST, IQ_PLANAR = 0, 1, 2
 IQ_F32, IQ_F16 = 0, 1
 
 _LIB = None
@@ -101,8 +101,10 @@ def iq_codebook(bits: int, head_dim: int) -> np.ndarray:
 
 @dataclass
 class Config:
-    """Mirror of iq_config.  ``quats``: device fp32 tensor (H_kv, d/4, 2, 4);
-    ``centroids``: host fp32 array of 2**bits values."""
+    """Mirror of iq_config.  ``quats``: device fp32 tensor of block-rotation
+    parameters, (H_kv, d/4, 2, 4) quaternion pairs for Full and Fast or
+    (H_kv, d/2, 2) pair rotations for Planar; ``centroids``: host fp32 array
+    of 2**bits values."""
 
     head_dim: int
     bits: int

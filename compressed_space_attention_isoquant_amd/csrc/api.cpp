@@ -21,7 +21,7 @@ int check_config(const iq_config *cfg) {
   if (!cfg || !cfg->quats || !cfg->centroids) return IQ_ERR_INVALID_ARG;
   if (cfg->head_dim != 128 && cfg->head_dim != 256 && cfg->head_dim != 512) return IQ_ERR_UNSUPPORTED;
   if (cfg->bits < 2 || cfg->bits > 4) return IQ_ERR_UNSUPPORTED;
-  if (cfg->variant != IQ_FULL && cfg->variant != IQ_FAST) return IQ_ERR_INVALID_ARG;
+  if (cfg->variant != IQ_FULL && cfg->variant != IQ_FAST && cfg->variant != IQ_PLANAR) return IQ_ERR_INVALID_ARG;
   if (cfg->num_kv_heads < 1) return IQ_ERR_INVALID_ARG;
   if (!aligned16(cfg->quats)) return IQ_ERR_MISALIGNED;
   const int n = 1 << cfg->bits;

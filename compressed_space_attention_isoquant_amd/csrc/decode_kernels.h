@@ -341,13 +341,13 @@ void partial_kernel(DecodeArgs a) {
   }
   {
     const float scale = a.qmul / sqrtf((float)D);
-    const float4 *qg = reinterpret_cast<const float4 *>(a.quats) + (size_t)kvh * (D / 4) * 2;
+    const float *pg = a.quats + (size_t)kvh * (D / 4) * block_param_floats(a.variant);
     for (int p = threadIdx.x; p < G * D / 4; p += kThreads) {
       const int hh = p / (D / 4), blk = p % (D / 4);
       float4 v = make_float4(qs[hh][4 * blk] * scale, qs[hh][4 * blk + 1] * scale,
                              qs[hh][4 * blk + 2] * scale, qs[hh][4 * blk + 3] * scale);
-      const float4 qL = qg[2 * blk], qR = qg[2 * blk + 1];
-      float4 t = a.variant == 0 ? so4_fwd<0>(v, qL, qR) : so4_fwd<1>(v, qL, qR);
+      float4 t = a.variant == 0 ? block_fwd<0>(v, pg, blk)
+                 : a.variant == 1 ? block_fwd<1>(v, pg, blk) : block_fwd<kPlanar>(v, pg, blk);
       qs[hh][4 * blk] = t.x;
       qs[hh][4 * blk + 1] = t.y;
       qs[hh][4 * blk + 2] = t.z;
@@ -717,9 +717,8 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
   y[i] = L > 0.f ? o * a.oscale / L : 0.f;
   __syncthreads();
   if (i < D / 4) {
-    const float4 *qg = reinterpret_cast<const float4 *>(a.quats) + (size_t)g * (D / 4) * 2;
-    float4 u = so4_inv<VARIANT>(make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]),
-                                qg[2 * i], qg[2 * i + 1]);
+    const float *pg = a.quats + (size_t)g * (D / 4) * block_param_floats(VARIANT);
+    float4 u = block_inv<VARIANT>(make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]), pg, i);
     y[4 * i] = u.x;
     y[4 * i + 1] = u.y;
     y[4 * i + 2] = u.z;
@@ -780,10 +779,12 @@ hipError_t partial_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
 template <int D>
 hipError_t merge_dispatch(int variant, const MergeArgs &a, hipStream_t s) {
   dim3 grid((unsigned)a.hq, (unsigned)a.batch);
-  if (variant == 0)
-    hipLaunchKernelGGL((merge_kernel<D, 0>), grid, dim3(D), 0, s, a);
-  else
-    hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(D), 0, s, a);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((merge_kernel<D, 0>), grid, dim3(D), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(D), 0, s, a); break;
+    case kPlanar: hipLaunchKernelGGL((merge_kernel<D, kPlanar>), grid, dim3(D), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

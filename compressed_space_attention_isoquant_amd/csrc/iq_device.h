@@ -35,6 +35,41 @@ __device__ __forceinline__ float4 so4_inv(float4 w, float4 qL, float4 qR) {
   return t;
 }
 
+// 2-D special case (IsoQuant abstract): the pairs (v.x, v.y) and (v.z, v.w)
+// of a 4-D block, read as complex numbers, times z0 = (z.x, z.y) and
+// z1 = (z.z, z.w), each stored as (cos, sin).
+__device__ __forceinline__ float4 planar_fwd(float4 v, float4 z) {
+  return make_float4(z.x * v.x - z.y * v.y, z.y * v.x + z.x * v.y, z.z * v.z - z.w * v.w,
+                     z.w * v.z + z.z * v.w);
+}
+
+// Inverse: times the conjugates.
+__device__ __forceinline__ float4 planar_inv(float4 w, float4 z) {
+  return make_float4(z.x * w.x + z.y * w.y, z.x * w.y - z.y * w.x, z.z * w.z + z.w * w.w,
+                     z.z * w.w - z.w * w.z);
+}
+
+constexpr int kPlanar = 2;
+
+// Floats of rotation parameters per 4-D block: a quaternion pair (Full,
+// Fast) or two unit complex numbers (Planar).
+__host__ __device__ constexpr int block_param_floats(int variant) { return variant == kPlanar ? 4 : 8; }
+
+// Block rotation of 4-D block blk of a head whose parameters start at p.
+template <int VARIANT>
+__device__ __forceinline__ float4 block_fwd(float4 v, const float *p, int blk) {
+  const float4 *q = reinterpret_cast<const float4 *>(p);
+  if constexpr (VARIANT == kPlanar) return planar_fwd(v, q[blk]);
+  else return so4_fwd<VARIANT>(v, q[2 * blk], q[2 * blk + 1]);
+}
+
+template <int VARIANT>
+__device__ __forceinline__ float4 block_inv(float4 w, const float *p, int blk) {
+  const float4 *q = reinterpret_cast<const float4 *>(p);
+  if constexpr (VARIANT == kPlanar) return planar_inv(w, q[blk]);
+  else return so4_inv<VARIANT>(w, q[2 * blk], q[2 * blk + 1]);
+}
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {

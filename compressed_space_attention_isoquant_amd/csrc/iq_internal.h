@@ -34,7 +34,7 @@ struct CellTable {
 
 struct QuantArgs {
   const void *x;           // [batch][n][H_kv][d]
-  const float *quats;      // [H_kv][d/4][2][4]
+  const float *quats;      // [H_kv][d/4][2][4] (Full, Fast) or [H_kv][d/2][2] (Planar)
   const int32_t *start_pos;
   uint8_t *codes;          // [batch][H_kv][cap][row]
   uint16_t *norms;         // [batch][H_kv][cap]

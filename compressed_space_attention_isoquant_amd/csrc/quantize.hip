@@ -153,7 +153,7 @@ __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
 }
 
 // Columns of the 4x4 matrices of the forward block rotations: column c of
-// block gb = 8 j + blk (held by lane j of a vector) is so4_fwd(e_c), times
+// block gb = 8 j + blk (held by lane j of a vector) is block_fwd(e_c), times
 // lane_sign(j) when SIGNED, stored at qm[blk][c][j] so that the lanes of a
 // vector read consecutive 16-byte words (no LDS bank conflicts).  The inverse
 // rotation is the transpose of the unsigned matrix.
@@ -161,20 +161,27 @@ template <int LPV>
 using BlockMatrices = float4[8][4][LPV];
 
 template <int D, int VARIANT, bool SIGNED>
-__device__ __forceinline__ void load_block_matrices(BlockMatrices<D / 32> &qm, const float *quats) {
+__device__ __forceinline__ void load_block_matrices(BlockMatrices<D / 32> &qm, const float *params) {
   for (int i = threadIdx.x; i < D; i += blockDim.x) {
     const int gb = i >> 2, c = i & 3;
-    const float4 *q = reinterpret_cast<const float4 *>(quats) + 2 * gb;
     const float4 e = make_float4(c == 0, c == 1, c == 2, c == 3);
-    float4 col = so4_fwd<VARIANT>(e, q[0], q[1]);
+    float4 col = block_fwd<VARIANT>(e, params, gb);
     if (SIGNED && lane_sign<D / 32>(gb >> 3) < 0.f) col = make_float4(-col.x, -col.y, -col.z, -col.w);
     qm[gb & 7][c][gb >> 3] = col;
   }
 }
 
 // m0..m3: the columns
+template <int VARIANT>
 __device__ __forceinline__ float4 mat_vec(float4 m0, float4 m1, float4 m2, float4 m3, float4 v) {
   float4 t;
+  if constexpr (VARIANT == kPlanar) {   // two 2x2 diagonal blocks
+    t.x = fmaf(m1.x, v.y, m0.x * v.x);
+    t.y = fmaf(m1.y, v.y, m0.y * v.x);
+    t.z = fmaf(m3.z, v.w, m2.z * v.z);
+    t.w = fmaf(m3.w, v.w, m2.w * v.z);
+    return t;
+  }
   t.x = fmaf(m3.x, v.w, fmaf(m2.x, v.z, fmaf(m1.x, v.y, m0.x * v.x)));
   t.y = fmaf(m3.y, v.w, fmaf(m2.y, v.z, fmaf(m1.y, v.y, m0.y * v.x)));
   t.z = fmaf(m3.z, v.w, fmaf(m2.z, v.z, fmaf(m1.z, v.y, m0.z * v.x)));
@@ -187,7 +194,11 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
 }
 
 // transpose of the matrix with columns m0..m3, times v
+template <int VARIANT>
 __device__ __forceinline__ float4 mat_t_vec(float4 m0, float4 m1, float4 m2, float4 m3, float4 v) {
+  if constexpr (VARIANT == kPlanar)
+    return make_float4(fmaf(m0.y, v.y, m0.x * v.x), fmaf(m1.y, v.y, m1.x * v.x), fmaf(m2.w, v.w, m2.z * v.z),
+                       fmaf(m3.w, v.w, m3.z * v.z));
   return make_float4(dot4(m0, v), dot4(m1, v), dot4(m2, v), dot4(m3, v));
 }
 
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 
   __shared__ BlockMatrices<LPV> qm;      // block rotation matrices of this head
   __shared__ uint2 cells[kMaxCells];
-  load_block_matrices<D, VARIANT, true>(qm, a.quats + (size_t)h * D * 2);
+  load_block_matrices<D, VARIANT, true>(qm, a.quats + (size_t)h * (D / 4) * block_param_floats(VARIANT));
   static_assert(kMaxCells <= kThreads, "one cell per thread");
   if ((int)threadIdx.x < a.cells.n) cells[threadIdx.x] = a.cells.e[threadIdx.x];
   __syncthreads();
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     // block rotations; the matrices carry the butterflies' lane sign
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
-      float4 t = mat_vec(qm[blk][0][j], qm[blk][1][j], qm[blk][2][j], qm[blk][3][j],
+      float4 t = mat_vec<VARIANT>(qm[blk][0][j], qm[blk][1][j], qm[blk][2][j], qm[blk][3][j],
                          make_float4(r[4 * blk], r[4 * blk + 1], r[4 * blk + 2], r[4 * blk + 3]));
       r[4 * blk] = t.x;
       r[4 * blk + 1] = t.y;
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
 
   __shared__ BlockMatrices<LPV> qm;
   __shared__ float cent[NLEV];
-  load_block_matrices<D, VARIANT, false>(qm, a.quats + (size_t)h * D * 2);
+  load_block_matrices<D, VARIANT, false>(qm, a.quats + (size_t)h * (D / 4) * block_param_floats(VARIANT));
   if (threadIdx.x < NLEV) cent[threadIdx.x] = a.tab.cent[threadIdx.x];
   __syncthreads();
 
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
 
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
-      float4 u = mat_t_vec(qm[blk][0][j], qm[blk][1][j], qm[blk][2][j], qm[blk][3][j],
+      float4 u = mat_t_vec<VARIANT>(qm[blk][0][j], qm[blk][1][j], qm[blk][2][j], qm[blk][3][j],
                            make_float4(r[4 * blk], r[4 * blk + 1], r[4 * blk + 2], r[4 * blk + 3]));
       r[4 * blk] = u.x;
       r[4 * blk + 1] = u.y;
@@ -495,14 +506,22 @@ hipError_t dequantize_dispatch_io(int out_f16, const DequantArgs &a, hipStream_t
 
 template <int D, int BITS>
 hipError_t quantize_dispatch_variant(int variant, int in_f16, const QuantArgs &a, hipStream_t s) {
-  return variant == 0 ? quantize_dispatch_io<D, BITS, 0>(in_f16, a, s)
-                      : quantize_dispatch_io<D, BITS, 1>(in_f16, a, s);
+  switch (variant) {
+    case 0: return quantize_dispatch_io<D, BITS, 0>(in_f16, a, s);
+    case 1: return quantize_dispatch_io<D, BITS, 1>(in_f16, a, s);
+    case kPlanar: return quantize_dispatch_io<D, BITS, kPlanar>(in_f16, a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D, int BITS>
 hipError_t dequantize_dispatch_variant(int variant, int out_f16, const DequantArgs &a, hipStream_t s) {
-  return variant == 0 ? dequantize_dispatch_io<D, BITS, 0>(out_f16, a, s)
-                      : dequantize_dispatch_io<D, BITS, 1>(out_f16, a, s);
+  switch (variant) {
+    case 0: return dequantize_dispatch_io<D, BITS, 0>(out_f16, a, s);
+    case 1: return dequantize_dispatch_io<D, BITS, 1>(out_f16, a, s);
+    case kPlanar: return dequantize_dispatch_io<D, BITS, kPlanar>(out_f16, a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D>

@@ -68,7 +68,12 @@ typedef enum {
   IQ_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
 } iq_status;
 
-typedef enum { IQ_FULL = 0, IQ_FAST = 1 } iq_variant;
+/* Block rotation applied after the WHT (IsoQuant abstract): Full is the SO(4)
+ * map v -> q_L v conj(q_R) on 4-D blocks, Fast keeps the left factor
+ * v -> q_L v, Planar is the framework's 2-D special case: each coordinate
+ * pair (x[2i], x[2i+1]), read as a complex number, is multiplied by a unit
+ * complex number (one SO(2) rotation per pair). */
+typedef enum { IQ_FULL = 0, IQ_FAST = 1, IQ_PLANAR = 2 } iq_variant;
 typedef enum { IQ_F32 = 0, IQ_F16 = 1 } iq_dtype;
 
 /* Per-layer quantiser configuration (a HOST struct). */
@@ -77,7 +82,11 @@ typedef struct {
   int32_t bits;            /* b: 2, 3 or 4 */
   int32_t variant;         /* iq_variant; Fast reads q_L only */
   int32_t num_kv_heads;    /* H_kv >= 1 */
-  const float *quats;      /* DEVICE [H_kv][d/4][2][4] fp32 unit quaternions */
+  const float *quats;      /* DEVICE fp32 block-rotation parameters, used as
+                              given (no renormalisation): Full and Fast
+                              [H_kv][d/4][2][4] unit quaternions (q_L, q_R),
+                              each (w, x, y, z); Planar [H_kv][d/2][2] unit
+                              complex numbers (cos, sin) */
   const float *centroids;  /* HOST [2^b] fp32, strictly ascending, finite, each
                               with at most 11 significant bits (fp16 precision,
                               as iq_codebook produces) and max/min nonzero

@@ -28,7 +28,7 @@ def say(msg):
 
 def make_config(d, bits, variant, hkv, quat_seed=inputs.QUATERNION_SEED):
     t = torch()
-    quats = inputs.quaternions(hkv, d, seed=quat_seed)
+    quats = inputs.rotation_params(hkv, d, variant, seed=quat_seed)
     qdev = t.from_numpy(quats).to(DEV)
     cfg = B.Config(d, bits, variant, hkv, qdev, B.iq_codebook(bits, d))
     return cfg, quats

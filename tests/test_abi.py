@@ -92,7 +92,8 @@ def call_quant(c, x=0x2000, xdt=0, batch=1, n=1, sp=0x3000, codes=0x4000, norms=
 def test_quantize_validation():
     assert call_quant(cfg(d=96)) == -2
     assert call_quant(cfg(bits=5)) == -2
-    assert call_quant(cfg(variant=2)) == -1
+    assert call_quant(cfg(variant=3)) == -1      # Full, Fast and Planar are 0, 1, 2
+    assert call_quant(cfg(variant=-1)) == -1
     assert call_quant(cfg(hkv=0)) == -1
     assert call_quant(cfg(quats=0x1004)) == -3
     assert call_quant(cfg(), x=0) == -1

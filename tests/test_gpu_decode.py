@@ -94,7 +94,7 @@ def decode_case_gpu(case, d, bits, variant, hkv):
     return cfg, quats, kc, vc
 
 
-@pytest.mark.parametrize("variant", [O.FULL, O.FAST])
+@pytest.mark.parametrize("variant", [O.FULL, O.FAST, O.PLANAR])
 def test_c3_decode_8k(variant):
     d, bits, hq, hkv, T = 128, 3, 32, 4, 8192
     case = inputs.decode_case(seed=3, kv_len=T, num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
@@ -135,6 +135,7 @@ SHAPES = [  # (d, bits, hq, hkv, variant)
     (128, 3, 32, 4, O.FULL), (128, 2, 8, 8, O.FAST), (128, 4, 16, 4, O.FULL),
     (256, 3, 16, 8, O.FAST), (256, 2, 4, 2, O.FULL), (256, 4, 8, 8, O.FAST),
     (512, 3, 8, 1, O.FULL), (512, 2, 16, 4, O.FAST), (512, 4, 4, 2, O.FULL),
+    (128, 3, 32, 4, O.PLANAR), (256, 3, 16, 8, O.PLANAR), (512, 4, 8, 2, O.PLANAR),
 ]
 
 

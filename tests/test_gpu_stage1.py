@@ -25,6 +25,10 @@ pytestmark = pytest.mark.gpu
 TOL = {np.float32: 1e-5, np.float16: 2e-3}
 SETTINGS = [(v, d, b, dt) for v in (O.FULL, O.FAST) for d in (128, 256, 512) for b in (2, 3, 4)
             for dt in (np.float16, np.float32)]
+# the 2-D special case: every width and bit count on ragged counts, full size at b = 3
+PLANAR_SETTINGS = [(O.PLANAR, d, b, dt) for d in (128, 256, 512) for b in (2, 3, 4)
+                   for dt in (np.float16, np.float32)]
+PLANAR_FULL_SIZE = [s for s in PLANAR_SETTINGS if s[2] == 3]
 
 
 def dequantize_gpu(cfg, cache, batch, n, hkv, d, out_dtype, start=0):
@@ -67,7 +71,7 @@ def test_c1_full_d128_b3_fp32():
     assert abs(np.mean(err) - expect) < 4 * se
 
 
-@pytest.mark.parametrize("variant,d,bits,dt", SETTINGS)
+@pytest.mark.parametrize("variant,d,bits,dt", SETTINGS + PLANAR_SETTINGS)
 def test_stage1_settings_ragged(variant, d, bits, dt):
     # a count that is not a multiple of the per-workgroup vector count
     x = inputs.unit_vectors(1037, d, dt, seed=7 + d + bits)
@@ -189,7 +193,8 @@ def test_prefill_bulk_compression():
         say(f"prefill (b={b}, h={h}): flagged={nf} flagged_mismatch={nfm}")
 
 
-@pytest.mark.parametrize("idx,setting", list(enumerate(SETTINGS)))
+@pytest.mark.parametrize("idx,setting", list(enumerate(SETTINGS)) +
+                         [(100 + i, s) for i, s in enumerate(PLANAR_FULL_SIZE)])
 def test_c2_full_size_sampled(idx, setting):
     """2^20 unit vectors per setting quantized and dequantized on the GPU; the
     oracle checks 2,048 sampled vectors (the last ones included) element by
