@@ -257,9 +257,21 @@ def test_c5_batched_append_decode():
         B.iq_decode_attention(cfg, q, kc, vc, pos, max_len, scale_for(d), out, lse, arg, ws)
         appended_k.append(knew.cpu().numpy())
         appended_v.append(vnew.cpu().numpy())
+    # the benchmark's launch configuration on the same last step: split phase
+    # without argmax tracking, merge into fp16 output
+    out16 = t.empty((batch, hq, d), dtype=t.float16, device=DEV)
+    lse2 = t.empty((batch, hq), dtype=t.float32, device=DEV)
+    B.iq_decode_attention_partial(cfg, q, kc, vc, pos, max_len, scale_for(d), ws, track_argmax=False)
+    B.iq_decode_attention_merge(cfg, batch, hq, max_len, out16, lse2, None, ws)
     t.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     glse = lse.cpu().numpy()
+    # the same arithmetic with and without argmax tracking, up to fp32 rounding
+    # order; fp16 output within one fp16 step of the fp32 result
+    g16 = out16.cpu().numpy().astype(np.float64)
+    step = np.abs(np.spacing(got.astype(np.float16)).astype(np.float64))
+    assert np.all(np.abs(g16 - got) <= step + 1e-6 * np.abs(got)), float(np.max(np.abs(g16 - got) - step))
+    assert np.max(np.abs(lse2.cpu().numpy() - glse)) <= 1e-5 * max(1.0, float(np.max(np.abs(glse))))
     qh = q.cpu().numpy()
     L = pos.cpu().numpy()
     cb = O.codebook(bits, d)
