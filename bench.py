@@ -101,12 +101,17 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="headline and uniform 32K decode only (the profiled command)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--stage1-only", action="store_true", help="the stage-1 sweep only (the profiled command)")
+    ap.add_argument("--summarize-stage1", metavar="COUNTER_CSV",
+                    help="VALU / HBM summary of the stage-1 kernels from a rocprofv3 --pmc run")
     ap.add_argument("--fresh-runs", type=int, default=2,
                     help="extra independent headline runs, each in a fresh process")
     ap.add_argument("--headline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
+    if args.summarize_stage1:
+        return summarize_stage1(args.summarize_stage1)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU only; runs on several GPUs are not "
                                    "part of it", "n_gpus": args.gpus}))
@@ -115,7 +120,7 @@ def main():
     # independent runs of the headline in fresh processes, started before this
     # process touches the GPU
     fresh = []
-    if not (args.headline_child or args.no_extras or args.decode_only):
+    if not (args.headline_child or args.no_extras or args.decode_only or args.stage1_only):
         for _ in range(max(0, args.fresh_runs)):
             fresh.append(run_fresh_headline(args.steps, args.warmup))
 
@@ -131,6 +136,9 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    if args.stage1_only:
+        print(json.dumps(run_stage1(torch, dev)))
+        return 0
     head = run_headline(torch, dev, args)
     if args.headline_child:
         print(json.dumps({"value": head["value"], "ms_per_step": head["ms_per_step"],
@@ -574,6 +582,80 @@ def summarize_counters(fetch_csv, write_csv):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+    return 0
+
+
+# read + write rate of a plain device-to-device copy measured on the GPU
+# (torch copy_ of 4 GiB): the practical HBM ceiling for kernels that both
+# read and write
+COPY_CEILING_GBS = 4880.0
+STAGE1_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "stage1_valu_and_hbm.md")
+
+
+def summarize_stage1(counter_csv):
+    """Per stage-1 kernel (d, bits, variant, I/O type): from one rocprofv3
+    --pmc pass with SQ_INSTS_VALU and GRBM_GUI_ACTIVE, the VALU instructions
+    per vector and the VALU issue utilisation (wave64 instructions x 4 cycles
+    over the SIMD cycles of the dispatch: 1024 SIMDs, GRBM_GUI_ACTIVE being
+    counted per XCD, 8 XCDs), next to the HBM rate of the algorithmic bytes
+    over the dispatch's duration.  The larger fraction names the binding
+    roofline."""
+    import csv
+    import re
+
+    n = 1 << 20
+    disp = {}
+    for r in csv.DictReader(open(counter_csv)):
+        # mangled (the _Float16 instantiations) or demangled (float) names
+        m = (re.search(r"(quantize|dequantize)_kernelILi(\d+)ELi(\d)ELi(\d)E(DF16_|f)E", r["Kernel_Name"]) or
+             re.search(r"(quantize|dequantize)_kernel<(\d+), (\d), (\d), (_Float16|float)>", r["Kernel_Name"]))
+        if not m:
+            continue
+        io = "fp16" if m.group(5) in ("DF16_", "_Float16") else "fp32"
+        e = disp.setdefault(r["Dispatch_Id"], {"key": (m.group(1), int(m.group(2)), int(m.group(3)),
+                                                        int(m.group(4)), io),
+                                                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+    agg = {}
+    for e in disp.values():
+        if "SQ_INSTS_VALU" in e and "GRBM_GUI_ACTIVE" in e:
+            agg.setdefault(e["key"], []).append(e)
+    vname = {0: "Full", 1: "Fast", 2: "Planar"}
+    lines = ["# Stage-1 kernels: VALU and HBM fractions", "",
+             "Commands (from the repository root, on one MI355X):", "", "```", "export TMPDIR=/tmp",
+             "rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_s1 "
+             "-o s -- python3 bench.py --stage1-only",
+             "python3 bench.py --summarize-stage1 gpurun_out/pmc_s1/s_counter_collection.csv", "```", "",
+             f"2^20 vectors per dispatch; medians over the dispatches of each kernel.  VALU: wave64 VALU "
+             f"instructions per vector x 64 lanes (lane-ops per vector), and the issue ratio = "
+             f"SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x the dispatch's cycles, GRBM_GUI_ACTIVE / 8 being "
+             f"the cycles of one XCD); it exceeds 1 where part of the instructions take fewer than four "
+             f"cycles, and near or above 1 the VALU issues without pause.  HBM: (d x input bytes + "
+             f"d x b / 8 + 2) bytes per vector for quantize, the reverse for dequantize, over the dispatch's "
+             f"duration (counter collection serialises dispatches, so the durations are those of a lone "
+             f"kernel), as a fraction of 8 TB/s.  Bound: HBM where the rate reaches 90% of what a plain "
+             f"device-to-device copy moves on this GPU (read + write, {COPY_CEILING_GBS / 1e3:.2f} TB/s), "
+             f"VALU where the issue ratio reaches 0.9, else neither (issue stalls).", "",
+             "| kernel | d | b | variant | I/O | us | G vec/s | VALU lane-ops / vec | VALU issue ratio | HBM GB/s | HBM frac | bound |",
+             "|---|---:|---:|---|---|---:|---:|---:|---:|---:|---:|---|"]
+    for key in sorted(agg, key=lambda k: (k[0] != "quantize", k[1], k[2], k[3], k[4])):
+        kind, d, b, v, io = key
+        es = agg[key]
+        ns = float(np.median([e["ns"] for e in es]))
+        valu = float(np.median([e["SQ_INSTS_VALU"] for e in es]))
+        util = float(np.median([e["SQ_INSTS_VALU"] * 4 / (128.0 * e["GRBM_GUI_ACTIVE"]) for e in es]))
+        nbytes = n * (d * (2 if io == "fp16" else 4) + row_bytes(d, b) + 2)
+        gbs = nbytes / ns
+        frac = gbs / HBM_PEAK_GBS
+        hbm_bound, valu_bound = gbs >= 0.9 * COPY_CEILING_GBS, util >= 0.9
+        bound = ("HBM + VALU" if valu_bound else "HBM") if hbm_bound else ("VALU" if valu_bound else "neither")
+        lines.append(f"| {kind} | {d} | {b} | {vname[v]} | {io} | {ns / 1e3:.1f} | {n / ns:.2f} | "
+                     f"{valu * 64 / n:.0f} | {util:.2f} | {gbs:.0f} | {frac:.2f} | {bound} |")
+    text = "\n".join(lines) + "\n"
+    os.makedirs(os.path.dirname(STAGE1_FILE), exist_ok=True)
+    with open(STAGE1_FILE, "w") as f:
+        f.write(text)
+    print(text)
     return 0
 
 
