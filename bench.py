@@ -224,7 +224,7 @@ def run_headline(torch, dev, args):
     batch, hq, hkv, d, bits = (w[k] for k in ("batch", "num_q_heads", "num_kv_heads", "head_dim", "bits"))
     lengths = inputs.batch_lengths(w["length_seed"], batch, w["len_lo"], w["len_hi"])
     n_total = args.warmup + args.steps
-    cap = int(lengths.max()) + n_total
+    cap = (int(lengths.max()) + n_total + 1) // 2 * 2       # decode needs an even capacity
     quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
     cfg = B.Config(d, bits, B.IQ_FAST, hkv, quats, B.iq_codebook(bits, d))
     rng = np.random.default_rng(46)

@@ -310,6 +310,9 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
   // offsets and use offsets from 2^30 up as out of range
   const int64_t rb = int64_t(cfg->head_dim) * cfg->bits / 8;
   if (k->capacity * rb >= (int64_t(1) << 30) || v->capacity * rb >= (int64_t(1) << 30)) return IQ_ERR_UNSUPPORTED;
+  // norms are streamed as 4-byte words (two rows each) that must lie inside
+  // the region, so a region holds an even number of rows
+  if ((k->capacity & 1) || (v->capacity & 1)) return IQ_ERR_UNSUPPORTED;
   if (!aligned16(q)) return IQ_ERR_MISALIGNED;
 
   const iq::Geometry geo = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);

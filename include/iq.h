@@ -152,8 +152,9 @@ size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch,
  *               lse = -inf, argmax = -1.
  *   max_kv_len: HOST upper bound of kv_len, used for the grid only; every
  *               kv_len[b] must be <= max_kv_len (rows at and past kv_len[b]
- *               do not affect the results).  Each cache's capacity * d*b/8
- *               must stay below 2^30 bytes (IQ_ERR_UNSUPPORTED otherwise).
+ *               do not affect the results).  Each cache's capacity must
+ *               be even and capacity * d*b/8 below 2^30 bytes
+ *               (IQ_ERR_UNSUPPORTED otherwise).
  *   softmax_scale: multiplies q.k (1/sqrt(d) in Appendix A).
  *   out:        [batch][Hq][d] of out_dtype, in the original (un-rotated)
  *               domain.

@@ -191,6 +191,12 @@ def test_partial_and_merge_validation():
     assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 32, ctypes.byref(k), ctypes.byref(huge),
                                          0x8000, 16, 0.1, 1, 0x7000, need, None) == -2
     assert (1 << 30) - rows * 48 <= 48 and fine.capacity * 48 < (1 << 30)
+    # an odd capacity: the last row's norm would straddle the region's end
+    odd = B.IQCacheC(0x4000, 0x5000, 17)
+    assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 32, ctypes.byref(odd), ctypes.byref(k),
+                                         0x8000, 16, 0.1, 1, 0x7000, need, None) == -2
+    assert L.iq_decode_attention_partial(ctypes.byref(cc), 0x2000, 1, 1, 32, ctypes.byref(k), ctypes.byref(odd),
+                                         0x8000, 16, 0.1, 1, 0x7000, need, None) == -2
     # merge: null out, bad dtype, misaligned argmax
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, None, 0, None, None, 0x7000, need, None) == -1
     assert L.iq_decode_attention_merge(ctypes.byref(cc), 1, 32, 16, 0x6000, 5, None, None, 0x7000, need, None) == -2

@@ -217,6 +217,63 @@ def test_many_short_sequences():
     assert np.all(got[lens == 0] == 0)
 
 
+def test_max_decode_batch():
+    """The largest batch a decode call takes (65535 sequences of 0..4
+    tokens): sampled sequences against the oracle, the empty ones exact."""
+    d, bits, hq, hkv, batch, cap = 128, 3, 2, 1, 65535, 4
+    rng = np.random.default_rng(23)
+    lens = rng.integers(0, cap + 1, size=batch)
+    lens[-1] = cap
+    cfg, quats = make_config(d, bits, O.FAST, hkv)
+    k = rng.standard_normal((batch, cap, hkv, d)).astype(np.float16)
+    v = rng.standard_normal((batch, cap, hkv, d)).astype(np.float16)
+    q = rng.standard_normal((batch, hq, d)).astype(np.float16)
+    kc = quantize_rows(cfg, k)
+    vc = quantize_rows(cfg, v)
+    got, lse, arg = run_decode(cfg, q, kc, vc, lens, cap)
+    hk, hv = host_cache(kc), host_cache(vc)
+    idx = np.unique(np.concatenate([[0, batch - 1], rng.choice(batch, 16, replace=False)]))
+    ref, rlse, rarg = oracle_decode(q[idx], k[idx], v[idx], quats, cfg, lens[idx],
+                                    (hk[0][idx], hk[1][idx]), (hv[0][idx], hv[1][idx]))
+    check_outputs(f"batch {batch} ({len(idx)} sampled)", got[idx], lse[idx], arg[idx], ref, rlse, rarg, 2e-3,
+                  check_arg=True)
+    empty = lens == 0
+    assert np.all(got[empty] == 0) and np.all(np.isneginf(lse[empty])) and np.all(arg[empty] == -1)
+
+
+def test_largest_cache_region_periodic_context():
+    """A context as long as one cache region may be (capacity x row bytes just
+    below 2^30): a 4096-token block of K/V repeated R times.  Attention over
+    R identical copies equals attention over one copy (every weight is
+    divided among R equal scores), with lse larger by ln R and the argmax in
+    the first copy (ties go to the lowest position); the oracle computes the
+    single copy."""
+    t = torch()
+    d, bits, hq, hkv, P = 128, 3, 8, 1, 4096
+    row = d * bits // 8
+    cap = ((1 << 30) - 1) // row // 2 * 2      # the largest even capacity
+    R = cap // P
+    T = P * R
+    rng = np.random.default_rng(24)
+    cfg, quats = make_config(d, bits, O.FULL, hkv)
+    k = (rng.standard_normal((1, P, hkv, d)) * 2).astype(np.float16)
+    v = rng.standard_normal((1, P, hkv, d)).astype(np.float16)
+    q = rng.standard_normal((1, hq, d)).astype(np.float16)
+    kp, vp = quantize_rows(cfg, k), quantize_rows(cfg, v)
+    big = []
+    for small in (kp, vp):
+        c = B.new_cache(1, hkv, cap, d, bits, DEV)
+        c.codes[0, 0, :T].view(R, P, row).copy_(small.codes[0, 0].unsqueeze(0).expand(R, P, row))
+        c.norms[0, 0, :T].view(R, P).copy_(small.norms[0, 0].unsqueeze(0).expand(R, P))
+        big.append(c)
+    got, lse, arg = run_decode(cfg, q, big[0], big[1], [T], T)
+    ref, rlse, rarg = oracle_decode(q, k, v, quats, cfg, [P], host_cache(kp), host_cache(vp))
+    say(f"periodic context T={T} ({R} x {P}, {T * row / 2**30:.4f} GiB per K/V region)")
+    check_outputs("largest region", got, lse - math.log(R), arg, ref, rlse, rarg, 2e-3, check_arg=True)
+    del big
+    t.cuda.empty_cache()
+
+
 def test_c5_batched_append_decode():
     """64 sequences, lengths U[1024, 32768], Hq=16, H_kv=8, d=256, 3-bit, Fast:
     each step appends one K and one V token per sequence then attends over
