@@ -274,6 +274,78 @@ def test_largest_cache_region_periodic_context():
     t.cuda.empty_cache()
 
 
+def test_distinct_k_and_v_capacities():
+    """K and V caches with different capacities (each region addressed with
+    its own row count), lengths up to the smaller one."""
+    t = torch()
+    d, bits, hq, hkv, batch = 256, 3, 8, 2, 3
+    kcap, vcap = 640, 1000
+    lens = [640, 17, 333]
+    rng = np.random.default_rng(26)
+    cfg, quats = make_config(d, bits, O.FULL, hkv)
+    k = (rng.standard_normal((batch, kcap, hkv, d)) * 2).astype(np.float16)
+    v = (rng.standard_normal((batch, vcap, hkv, d)) * 2).astype(np.float16)
+    q = rng.standard_normal((batch, hq, d)).astype(np.float16)
+    kc = quantize_rows(cfg, k)
+    vc = quantize_rows(cfg, v)
+    assert kc.capacity == kcap and vc.capacity == vcap
+    got, lse, arg = run_decode(cfg, q, kc, vc, lens, max(lens))
+    ref, rlse, rarg = oracle_decode(q, k, v[:, :kcap], quats, cfg, lens, host_cache(kc), host_cache(vc))
+    check_outputs("distinct K/V capacities", got, lse, arg, ref, rlse, rarg, 2e-3, check_arg=True)
+    del t
+
+
+def test_sorted_work_order_batch():
+    """300 ragged sequences up to 32K tokens, one KV head: 4 splits each, so
+    1200 (sequence, split) pairs, which the order kernel sorts (more than
+    1024 pairs: the sorting network rather than the counting rank).  Every
+    pair must run exactly once: sampled sequences against the oracle."""
+    t = torch()
+    d, bits, hq, hkv, batch, cap = 128, 3, 2, 1, 300, 32768
+    lens = inputs.batch_lengths(25, batch, 1, cap)
+    T = int(lens.max())
+    # the split rule (about 2048 workgroups, chunks of at least 8192 tokens
+    # while that still gives 1024, whole 128-token blocks)
+    chunk = max(-(-T // -(-2048 // batch)), min(8192, -(-T // -(-1024 // batch))))
+    n_split = -(-T // (-(-chunk // 128) * 128))
+    assert 1024 < batch * n_split <= 4096, batch * n_split
+    rng = np.random.default_rng(25)
+    ch_k = inputs.outlier_channels(rng, hkv, d)
+    ch_v = inputs.outlier_channels(rng, hkv, d)
+    cfg, quats = make_config(d, bits, O.FAST, hkv)
+    kc = B.new_cache(batch, hkv, cap, d, bits, DEV)
+    vc = B.new_cache(batch, hkv, cap, d, bits, DEV)
+    zero = t.zeros((1,), dtype=t.int32, device=DEV)
+    for b in range(batch):
+        n = int(lens[b])
+        for cache, idx, ch in ((kc, 2 * b, ch_k), (vc, 2 * b + 1, ch_v)):
+            x = inputs.device_kv(25, idx, n, ch, d, DEV)
+            B.iq_quantize_append(cfg, x[None], zero, B.PackedCache(cache.codes[b:b + 1], cache.norms[b:b + 1]))
+    q = inputs.device_normal(25, 99_999, (batch, hq, d), DEV, t.float16)
+    lens_dev = t.from_numpy(lens.astype(np.int32)).to(DEV)
+    ws = t.empty((B.iq_decode_workspace_bytes(cfg, batch, hq, T),), dtype=t.uint8, device=DEV)
+    out = t.empty((batch, hq, d), dtype=t.float32, device=DEV)
+    lse = t.empty((batch, hq), dtype=t.float32, device=DEV)
+    arg = t.empty((batch, hq), dtype=t.int32, device=DEV)
+    B.iq_decode_attention(cfg, q, kc, vc, lens_dev, T, scale_for(d), out, lse, arg, ws)
+    t.cuda.synchronize()
+    got, glse, garg = out.cpu().numpy().astype(np.float64), lse.cpu().numpy(), arg.cpu().numpy()
+    qh = q.cpu().numpy()
+    cb = O.codebook(bits, d)
+    sample = sorted({int(np.argmax(lens)), int(np.argmin(lens)), *rng.choice(batch, 3, replace=False).tolist()})
+    for b in sample:
+        n = int(lens[b])
+        kx = inputs.device_kv(25, 2 * b, n, ch_k, d, DEV).cpu().numpy()
+        vx = inputs.device_kv(25, 2 * b + 1, n, ch_v, d, DEV).cpu().numpy()
+        gk = (kc.codes[b, :, :n].cpu().numpy(), kc.norms[b, :, :n].cpu().numpy().view(np.uint16))
+        gv = (vc.codes[b, :, :n].cpu().numpy(), vc.norms[b, :, :n].cpu().numpy().view(np.uint16))
+        kr, kn, _ = oracle_cache(kx, quats, cb, O.FAST, bits, gk[0], gk[1])
+        vr, vn, _ = oracle_cache(vx, quats, cb, O.FAST, bits, gv[0], gv[1])
+        ro, rl, ra = O.attend(qh[b], kr, kn, vr, vn, quats, cb, bits, O.FAST, scale_for(d))
+        check_outputs(f"sorted order: sequence {b} (T={n})", got[b], glse[b], garg[b], ro, rl, ra, 2e-3,
+                      check_arg=True)
+
+
 def test_c5_batched_append_decode():
     """64 sequences, lengths U[1024, 32768], Hq=16, H_kv=8, d=256, 3-bit, Fast:
     each step appends one K and one V token per sequence then attends over
