@@ -29,6 +29,13 @@ design notes of the repository):
 * BitPack_b: bit r of code i is bit (b*i + r) of the row, bytes little-endian
   (LSB-first bitstream), d*b/8 bytes per vector.
 * Zero-length attention (kv_len = 0): output 0, lse = -inf, argmax = -1.
+* RoPE sub-block split (for MLA-style keys, which the pages name as a
+  limitation): a key is (content, positional) with the r positional (RoPE)
+  coordinates last.  Only the content part goes through Algorithm 1 (its
+  own norm, rotation, codes); the positional part is neither rotated nor
+  quantised and is kept in fp16 (round to nearest even).  Scores add the
+  positional dot product, unscaled by the content norm; values carry no
+  positional part.
 """
 
 from __future__ import annotations
@@ -67,6 +74,8 @@ __all__ = [
     "attend",
     "attend_rotated",
     "attend_dense",
+    "quantize_rope",
+    "attend_rope",
 ]
 
 FULL = 0
@@ -529,3 +538,52 @@ def attend_dense(q, k, v, softmax_scale):
     scores = softmax_scale * np.sum(np.asarray(k, dtype=np.float64) * q, axis=-1)
     alpha, _, _ = _softmax_stats(scores)
     return alpha @ np.asarray(v, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# RoPE sub-block split (RotaryQuant §5, the MLA/RoPE limitation: positional
+# coordinates must be neither rotated nor quantised).
+# ---------------------------------------------------------------------------
+
+def quantize_rope(x, quats, centroids, variant, rope_dim):
+    """Keys (..., d + r) with the r RoPE coordinates last: the content part
+    (..., d) is quantised as in :func:`quantize`; the RoPE part is returned
+    as fp16 bits (round to nearest even), untouched otherwise
+    (``rope16``, uint16 (..., r))."""
+    x = np.asarray(x)
+    r = quantize(x[..., :-rope_dim], quats, centroids, variant)
+    r["rope16"] = np.asarray(x[..., -rope_dim:], dtype=np.float64).astype(np.float16).view(np.uint16)
+    return r
+
+
+def attend_rope(q, k_rows, k_norm16, k_rope16, v_rows, v_norm16, quats, centroids, bits, variant,
+                softmax_scale, kv_len=None):
+    """Dequantize-then-attend with a RoPE sub-block (FP64), one sequence.
+
+    ``q``: (Hq, d + r), RoPE coordinates last.  ``k_rope16``: (H_kv, T, r)
+    fp16 bits of the keys' RoPE coordinates.  Score of token j for head h:
+    softmax_scale * (q_content . k'_j + q_rope . k_rope_j), with k'_j the
+    dequantised content key; the output is the weighted sum of the
+    dequantised values (d coordinates).  Other arguments as :func:`attend`.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    hq = q.shape[0]
+    rope_dim = k_rope16.shape[-1]
+    d = q.shape[1] - rope_dim
+    hkv = k_rows.shape[0]
+    group = hq // hkv
+    T = k_rows.shape[1] if kv_len is None else int(kv_len)
+    out = np.zeros((hq, d))
+    lse = np.full(hq, -np.inf)
+    arg = np.full(hq, -1, dtype=np.int64)
+    if T == 0:
+        return out, lse, arg
+    for g in range(hkv):
+        kp = dequantize(k_rows[g, :T], k_norm16[g, :T], quats[g], centroids, bits, variant, d)
+        kr = np.asarray(k_rope16[g, :T], dtype=np.uint16).view(np.float16).astype(np.float64)
+        vp = dequantize(v_rows[g, :T], v_norm16[g, :T], quats[g], centroids, bits, variant, d)
+        for h in range(g * group, (g + 1) * group):
+            scores = softmax_scale * (np.sum(kp * q[h, :d], axis=-1) + np.sum(kr * q[h, d:], axis=-1))
+            alpha, lse[h], arg[h] = _softmax_stats(scores)
+            out[h] = alpha @ vp
+    return out, lse, arg

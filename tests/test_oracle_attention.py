@@ -207,3 +207,118 @@ def test_needles_are_argmax_and_cosine_report():
         ref = O.attend_dense(case["q"][h], case["k"][:, g], case["v"][:, g], 1 / math.sqrt(d))
         cos = out[h] @ ref / (np.linalg.norm(out[h]) * np.linalg.norm(ref))
         assert cos > 0.95
+
+
+# ---- RoPE sub-block split -------------------------------------------------
+
+def make_rope_case(seed, T, hq, hkv, d, r, bits, variant):
+    rng = np.random.default_rng(seed)
+    quats = inputs.rotation_params(hkv, d, variant, seed=seed)
+    cb = O.codebook(bits, d)
+    k = (rng.standard_normal((hkv, T, d + r)) * 2).astype(np.float16)
+    v = (rng.standard_normal((hkv, T, d)) * 2).astype(np.float16)
+    q = rng.standard_normal((hq, d + r)).astype(np.float16)
+    kr = np.empty((hkv, T, d * bits // 8), np.uint8)
+    vr = np.empty_like(kr)
+    kn = np.empty((hkv, T), np.uint16)
+    vn = np.empty_like(kn)
+    kp = np.empty((hkv, T, r), np.uint16)
+    for g in range(hkv):
+        rk = O.quantize_rope(k[g], quats[g], cb, variant, r)
+        rv = O.quantize(v[g], quats[g], cb, variant)
+        kr[g], kn[g], kp[g] = O.pack(rk["codes"], bits), rk["norm16"], rk["rope16"]
+        vr[g], vn[g] = O.pack(rv["codes"], bits), rv["norm16"]
+    return dict(q=q, kr=kr, kn=kn, kp=kp, vr=vr, vn=vn, quats=quats, cb=cb, bits=bits, variant=variant,
+                d=d, r=r, k=k, v=v)
+
+
+def run_rope(c, q=None, kp=None, scale=0.125):
+    return O.attend_rope(c["q"] if q is None else q, c["kr"], c["kn"], c["kp"] if kp is None else kp, c["vr"],
+                         c["vn"], c["quats"], c["cb"], c["bits"], c["variant"], scale)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_rope_brute_force_tiny(T):
+    """Scores written out term by term: content keys through the dense
+    rotation matrix, RoPE keys as stored fp16, both dotted with the query."""
+    d, r, hq, hkv, bits = 32, 8, 4, 2, 3
+    c = make_rope_case(40 + T, T, hq, hkv, d, r, bits, O.FULL)
+    out, lse, arg = run_rope(c)
+    cb = c["cb"].astype(np.float64)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        R = dense_rotation(c["quats"][g], O.FULL)
+        qh = c["q"][h].astype(np.float64)
+        scores, vals = [], []
+        for j in range(T):
+            sk = float(np.array([c["kn"][g, j]], np.uint16).view(np.float16)[0])
+            sv = float(np.array([c["vn"][g, j]], np.uint16).view(np.float16)[0])
+            key = sk * (R.T @ cb[O.unpack(c["kr"][g, j], bits, d)])
+            rope = c["kp"][g, j].view(np.float16).astype(np.float64)
+            s = sum(qh[i] * key[i] for i in range(d)) + sum(qh[d + i] * rope[i] for i in range(r))
+            scores.append(0.125 * s)
+            vals.append(sv * (R.T @ cb[O.unpack(c["vr"][g, j], bits, d)]))
+        m = max(scores)
+        w = [math.exp(s - m) for s in scores]
+        ref = sum((w[j] / sum(w)) * vals[j] for j in range(T))
+        assert np.max(np.abs(out[h] - ref)) < 1e-12
+        assert abs(lse[h] - (m + math.log(sum(w)))) < 1e-12
+        assert arg[h] == scores.index(m)
+
+
+def test_rope_reduces_to_plain_attention():
+    """A zero RoPE query part gives plain attention over the content; a RoPE
+    key that is the same for every token shifts every score by one constant:
+    same output and argmax, lse larger by that constant."""
+    d, r, hq, hkv = 128, 64, 8, 2
+    c = make_rope_case(50, 200, hq, hkv, d, r, 3, O.FAST)
+    plain = O.attend(c["q"][:, :d], c["kr"], c["kn"], c["vr"], c["vn"], c["quats"], c["cb"], 3, O.FAST, 0.125)
+    q0 = c["q"].copy()
+    q0[:, d:] = 0
+    o0, l0, a0 = run_rope(c, q=q0)
+    assert np.max(np.abs(o0 - plain[0])) < 1e-12 and np.max(np.abs(l0 - plain[1])) < 1e-12
+    assert np.array_equal(a0, plain[2])
+    const = np.broadcast_to(c["kp"][:, :1], c["kp"].shape).copy()
+    o1, l1, a1 = run_rope(c, kp=const)
+    kr0 = const[:, 0].view(np.float16).astype(np.float64)            # (hkv, r)
+    shift = np.array([0.125 * np.dot(c["q"][h, d:].astype(np.float64), kr0[h // (hq // hkv)]) for h in range(hq)])
+    assert np.max(np.abs(o1 - plain[0])) < 1e-12
+    assert np.max(np.abs(l1 - (plain[1] + shift))) < 1e-11
+    assert np.array_equal(a1, plain[2])
+
+
+def test_rope_only_scores():
+    """A zero content query: the weights are the softmax of the RoPE dot
+    products alone (content norms and codes play no part)."""
+    d, r, hq, hkv = 128, 64, 4, 1
+    c = make_rope_case(51, 64, hq, hkv, d, r, 3, O.FULL)
+    q = c["q"].copy()
+    q[:, :d] = 0
+    out, lse, arg = run_rope(c, q=q)
+    kr = c["kp"][0].view(np.float16).astype(np.float64)
+    vp = O.dequantize(c["vr"][0], c["vn"][0], c["quats"][0], c["cb"], 3, O.FULL, d)
+    for h in range(hq):
+        s = 0.125 * (kr @ q[h, d:].astype(np.float64))
+        w = np.exp(s - s.max())
+        assert np.max(np.abs(out[h] - (w / w.sum()) @ vp)) < 1e-12
+        assert arg[h] == int(np.argmax(s))
+
+
+def test_rope_split_keeps_positional_coordinates():
+    """The content part is quantised on its own (its norm, its codes); the
+    RoPE part is only rounded to fp16, to nearest with ties to even."""
+    d, r = 128, 8
+    quats = inputs.quaternions(1, d)[0]
+    cb = O.codebook(3, d)
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal((5, d + r))
+    x[0, d:d + 5] = [1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -1 - 2.0 ** -11, 0.1, 65504.0 + 1.0]
+    a = O.quantize_rope(x, quats, cb, O.FULL, r)
+    b = O.quantize(x[:, :d], quats, cb, O.FULL)
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["norm16"], b["norm16"])
+    x2 = x.copy()
+    x2[:, d:] *= 0.5
+    assert np.array_equal(O.quantize_rope(x2, quats, cb, O.FULL, r)["norm16"], b["norm16"])
+    # ties to even: 1 + 2^-11 -> 1 (0x3C00), 1 + 3 * 2^-11 -> 1 + 2^-9 (0x3C02), -(1 + 2^-11) -> -1 (0xBC00);
+    # 0.1 -> 0x2E66; 65505 -> 65504 (0x7BFF)
+    assert a["rope16"][0, :5].tolist() == [0x3C00, 0x3C02, 0xBC00, 0x2E66, 0x7BFF]
