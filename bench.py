@@ -148,6 +148,7 @@ def main():
     if not args.no_extras:
         extras["uniform_32k"] = run_uniform_32k(torch, dev, max(10, args.steps // 5), args.warmup)
         if not args.decode_only:
+            extras["rope_32k"] = run_rope_32k(torch, dev)
             extras["c3_latency"] = run_c3_latency(torch, dev)
             extras["prefill_compress"] = run_prefill_compress(torch, dev)
         if not args.no_stage1 and not args.decode_only:
@@ -385,6 +386,64 @@ def run_uniform_32k(torch, dev, steps, warmup):
             "unit": "GB/s", "partial_kernel_ms": round(partial_ms, 5),
             "partial_achieved_gbs": round(achieved, 2), "frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("uniform_32k")}
+
+
+def run_rope_32k(torch, dev, reps=20):
+    """Supplementary: the uniform 32K shape with a RoPE sub-block: keys of
+    128 content coordinates (3-bit Full) plus 64 fp16 RoPE coordinates,
+    values of 128; 64 sequences x 32,768 tokens, 32 query / 4 KV heads.
+    Times the fused decode call (split + merge)."""
+    from compressed_space_attention_isoquant_amd import binding as B
+    from compressed_space_attention_isoquant_amd import inputs
+
+    batch, T, hq, hkv, d, bits, r = 64, 32768, 32, 4, 128, 3, 64
+    quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
+    cfg = B.Config(d, bits, B.IQ_FULL, hkv, quats, B.iq_codebook(bits, d))
+    rng = np.random.default_rng(7)
+    ch_k = inputs.outlier_channels(rng, hkv, d)
+    ch_v = inputs.outlier_channels(rng, hkv, d)
+    kc = B.new_cache(batch, hkv, T, d, bits, dev)
+    vc = B.new_cache(batch, hkv, T, d, bits, dev)
+    rope = torch.empty((batch, hkv, T, r), dtype=torch.int16, device=dev)
+    sb = 8
+    zero = torch.zeros((sb,), dtype=torch.int32, device=dev)
+    for b0 in range(0, batch, sb):
+        kx = torch.cat([inputs.device_kv(70, b0, sb * T, ch_k, d, dev),
+                        inputs.device_normal(71, b0, (sb * T, hkv, r), dev, torch.float16)], dim=-1)
+        B.iq_quantize_append_rope(cfg, kx.view(sb, T, hkv, d + r), r, zero,
+                                  B.PackedCache(kc.codes[b0:b0 + sb], kc.norms[b0:b0 + sb]), rope[b0:b0 + sb])
+        vx = inputs.device_kv(72, b0, sb * T, ch_v, d, dev)
+        B.iq_quantize_append(cfg, vx.view(sb, T, hkv, d), zero, B.PackedCache(vc.codes[b0:b0 + sb], vc.norms[b0:b0 + sb]))
+        del kx, vx
+    q = inputs.device_normal(73, 0, (batch, hq, d + r), dev, torch.float16)
+    kv_len = torch.full((batch,), T, dtype=torch.int32, device=dev)
+    out = torch.empty((batch, hq, d), dtype=torch.float16, device=dev)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    ws = torch.empty((B.iq_decode_workspace_bytes(cfg, batch, hq, T),), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d + r)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        B.iq_decode_attention_rope(cfg, q, kc, rope, vc, kv_len, T, scale, out, lse, None, ws)
+
+    for _ in range(3):
+        call()
+    e0, e1 = _events(torch)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    kv = batch * hkv * T * (2 * (row_bytes(d, bits) + 2) + 2 * r)
+    qo = batch * hq * (d + r) * 2 + batch * hq * d * 2
+    gbs = (kv + qo) / (ms * 1e-3) / 1e9
+    print(f"[bench] RoPE 32K decode {ms:.4f} ms, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+    del kc, vc, rope
+    return {"workload": "64 sequences x 32768 tokens, 32 query / 4 KV heads, keys of 128 content coordinates "
+                        "(3-bit IsoQuant-Full) + 64 fp16 RoPE coordinates, values of 128; fused decode call",
+            "ms": round(ms, 5), "value": round(gbs, 2), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_call": int(kv + qo)}
 
 
 def run_c3_latency(torch, dev, reps=20):

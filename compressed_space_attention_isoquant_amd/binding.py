@@ -61,6 +61,13 @@ def lib() -> ctypes.CDLL:
         L.iq_quantize_append.argtypes = [ctypes.POINTER(IQConfigC), P, i32, i32, i32, P,
                                          ctypes.POINTER(IQCacheC), P]
         L.iq_quantize_append.restype = ctypes.c_int
+        L.iq_quantize_append_rope.argtypes = [ctypes.POINTER(IQConfigC), P, i32, i32, i32, i32, P,
+                                              ctypes.POINTER(IQCacheC), P, P]
+        L.iq_quantize_append_rope.restype = ctypes.c_int
+        L.iq_decode_attention_rope.argtypes = [ctypes.POINTER(IQConfigC), P, i32, i32, i32,
+                                               ctypes.POINTER(IQCacheC), P, i32, ctypes.POINTER(IQCacheC), P,
+                                               i64, ctypes.c_float, P, i32, P, P, P, ctypes.c_size_t, P]
+        L.iq_decode_attention_rope.restype = ctypes.c_int
         L.iq_dequantize.argtypes = [ctypes.POINTER(IQConfigC), ctypes.POINTER(IQCacheC), i32, P, i32,
                                     P, i32, P]
         L.iq_dequantize.restype = ctypes.c_int
@@ -179,6 +186,16 @@ def iq_quantize_append(cfg: Config, x, start_pos, out: PackedCache, stream=None)
                                     _ptr(start_pos), ctypes.byref(oc), _stream(stream)))
 
 
+def iq_quantize_append_rope(cfg: Config, x, rope_dim: int, start_pos, out: PackedCache, rope_out,
+                            stream=None) -> None:
+    """x: (B, n_new, H_kv, d + rope_dim) fp32/fp16, RoPE coordinates last;
+    rope_out: int16 (B, H_kv, capacity, rope_dim) device tensor (fp16 bits)."""
+    batch, n_new = int(x.shape[0]), int(x.shape[1])
+    cc, oc = cfg.c(), out.c()
+    _check(lib().iq_quantize_append_rope(ctypes.byref(cc), _ptr(x), _dtype_code(x), batch, n_new, int(rope_dim),
+                                         _ptr(start_pos), ctypes.byref(oc), _ptr(rope_out), _stream(stream)))
+
+
 def iq_dequantize(cfg: Config, cache: PackedCache, start_pos, n: int, out, stream=None) -> None:
     """out: (B, n, H_kv, d) fp32/fp16 device tensor."""
     batch = int(out.shape[0])
@@ -208,6 +225,24 @@ def iq_decode_attention(cfg: Config, q, k: PackedCache, v: PackedCache, kv_len, 
                                      float(softmax_scale), _ptr(out), _dtype_code(out),
                                      _ptr(lse), _ptr(argmax), _ptr(workspace), ws_bytes,
                                      _stream(stream)))
+
+
+def iq_decode_attention_rope(cfg: Config, q, k: PackedCache, k_rope, v: PackedCache, kv_len, max_kv_len: int,
+                             softmax_scale: float, out, lse=None, argmax=None, workspace=None,
+                             stream=None) -> None:
+    """As iq_decode_attention with a RoPE sub-block: q (B, Hq, d + r), k_rope
+    int16 (B, H_kv, capacity, r) fp16 bits; out (B, Hq, d)."""
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    rope_dim = int(k_rope.shape[-1])
+    cc, kc, vc = cfg.c(), k.c(), v.c()
+    if workspace is None:
+        raise ValueError("workspace tensor required (size from iq_decode_workspace_bytes)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().iq_decode_attention_rope(ctypes.byref(cc), _ptr(q), _dtype_code(q), batch, hq,
+                                          ctypes.byref(kc), _ptr(k_rope), rope_dim, ctypes.byref(vc),
+                                          _ptr(kv_len), int(max_kv_len), float(softmax_scale), _ptr(out),
+                                          _dtype_code(out), _ptr(lse), _ptr(argmax), _ptr(workspace), ws_bytes,
+                                          _stream(stream)))
 
 
 def iq_decode_attention_partial(cfg: Config, q, k: PackedCache, v: PackedCache, kv_len, max_kv_len: int,

@@ -15,6 +15,11 @@ namespace {
 
 using iq::Tables;
 
+// RoPE coordinates per key: a multiple of 8 (16-byte fp16 rows) up to this;
+// decode attention takes kDecodeRopeDim of them.
+constexpr int32_t kMaxRopeDim = 512;
+constexpr int32_t kDecodeRopeDim = 64;
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_config(const iq_config *cfg) {
@@ -211,9 +216,11 @@ int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out) {
   return IQ_OK;
 }
 
-int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch,
-                       int32_t n_new, const int32_t *start_pos, const iq_cache *out,
-                       hipStream_t stream) {
+namespace {
+
+int quantize_append_impl(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch, int32_t n_new,
+                         int32_t rope_dim, const int32_t *start_pos, const iq_cache *out, uint16_t *rope_out,
+                         hipStream_t stream) {
   int st = check_config(cfg);
   if (st != IQ_OK) return st;
   if (!x || !start_pos) return IQ_ERR_INVALID_ARG;
@@ -223,8 +230,14 @@ int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype, int
   if (st != IQ_OK) return st;
   if (n_new > out->capacity) return IQ_ERR_INVALID_ARG;
   if (!aligned16(x)) return IQ_ERR_MISALIGNED;
+  if (rope_dim > 0) {
+    if (!rope_out) return IQ_ERR_INVALID_ARG;
+    if (rope_dim % 8 != 0 || rope_dim > kMaxRopeDim) return IQ_ERR_UNSUPPORTED;
+    if (!aligned16(rope_out)) return IQ_ERR_MISALIGNED;
+  }
   iq::QuantArgs a;
   a.x = x;
+  a.x_stride = cfg->head_dim + rope_dim;
   a.quats = cfg->quats;
   a.start_pos = start_pos;
   a.codes = out->codes;
@@ -235,7 +248,34 @@ int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype, int
   a.hkv = cfg->num_kv_heads;
   a.tab = make_tables(cfg);
   a.cells = make_cells(a.tab, cfg->bits);
-  return hip_status(iq::launch_quantize(cfg->head_dim, cfg->bits, cfg->variant, x_dtype == IQ_F16, a, stream));
+  st = hip_status(iq::launch_quantize(cfg->head_dim, cfg->bits, cfg->variant, x_dtype == IQ_F16, a, stream));
+  if (st != IQ_OK || rope_dim == 0) return st;
+  iq::RopeArgs r;
+  r.x = x;
+  r.start_pos = start_pos;
+  r.out = rope_out;
+  r.capacity = out->capacity;
+  r.batch = batch;
+  r.n = n_new;
+  r.hkv = cfg->num_kv_heads;
+  r.d = cfg->head_dim;
+  r.r = rope_dim;
+  return hip_status(iq::launch_rope_copy(x_dtype == IQ_F16, r, stream));
+}
+
+}  // namespace
+
+int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch,
+                       int32_t n_new, const int32_t *start_pos, const iq_cache *out,
+                       hipStream_t stream) {
+  return quantize_append_impl(cfg, x, x_dtype, batch, n_new, 0, start_pos, out, nullptr, stream);
+}
+
+int iq_quantize_append_rope(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch,
+                            int32_t n_new, int32_t rope_dim, const int32_t *start_pos,
+                            const iq_cache *out, uint16_t *rope_out, hipStream_t stream) {
+  if (rope_dim < 1) return IQ_ERR_INVALID_ARG;
+  return quantize_append_impl(cfg, x, x_dtype, batch, n_new, rope_dim, start_pos, out, rope_out, stream);
 }
 
 int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch, const int32_t *start_pos,
@@ -290,11 +330,14 @@ static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_
   return IQ_OK;
 }
 
-int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
-                                int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
-                                const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
-                                int32_t track_argmax, void *workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+namespace {
+
+// The split phase; with rope_dim > 0 the keys carry rope_dim fp16 RoPE
+// coordinates in k_rope and the query d + rope_dim coordinates.
+int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
+                        int32_t num_q_heads, const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim,
+                        const iq_cache *v, const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
+                        int32_t track_argmax, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   int group = 0;
   int st = check_decode_common(cfg, batch, num_q_heads, max_kv_len, workspace, workspace_bytes, &group);
   if (st != IQ_OK) return st;
@@ -314,12 +357,21 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
   // the region, so a region holds an even number of rows
   if ((k->capacity & 1) || (v->capacity & 1)) return IQ_ERR_UNSUPPORTED;
   if (!aligned16(q)) return IQ_ERR_MISALIGNED;
+  if (rope_dim > 0) {
+    if (!k_rope) return IQ_ERR_INVALID_ARG;
+    if (rope_dim != kDecodeRopeDim || cfg->head_dim != 128) return IQ_ERR_UNSUPPORTED;
+    if (!aligned16(k_rope)) return IQ_ERR_MISALIGNED;
+    if (k->capacity * rope_dim * 2 >= (int64_t(1) << 30)) return IQ_ERR_UNSUPPORTED;
+  }
 
   const iq::Geometry geo = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
   const int e = centroid_exponent(cfg);
   iq::DecodeArgs a;
   a.q = q;
   a.q_f16 = q_dtype == IQ_F16;
+  a.krope = k_rope;
+  a.rope = rope_dim;
+  a.rmul = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
   a.kc = k->codes;
   a.kn = k->norms;
   a.vc = v->codes;
@@ -349,6 +401,17 @@ int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_d
   return hip_status(iq::launch_decode(cfg->head_dim, cfg->bits, a, stream));
 }
 
+}  // namespace
+
+int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
+                                int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
+                                const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
+                                int32_t track_argmax, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return decode_partial_impl(cfg, q, q_dtype, batch, num_q_heads, k, nullptr, 0, v, kv_len, max_kv_len,
+                             softmax_scale, track_argmax, workspace, workspace_bytes, stream);
+}
+
 int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
                               int64_t max_kv_len, void *out, int32_t out_dtype, float *lse_out,
                               int32_t *argmax_out, const void *workspace, size_t workspace_bytes,
@@ -376,11 +439,13 @@ int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q
   return hip_status(iq::launch_merge(cfg->head_dim, cfg->variant, m, stream));
 }
 
-int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
-                        int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
-                        const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out,
-                        int32_t out_dtype, float *lse_out, int32_t *argmax_out, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+int decode_fused(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                 const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim, const iq_cache *v,
+                 const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out, int32_t out_dtype,
+                 float *lse_out, int32_t *argmax_out, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
   // validate both phases before enqueueing either
   int group = 0;
   int st = check_decode_common(cfg, batch, num_q_heads, max_kv_len, workspace, workspace_bytes, &group);
@@ -389,11 +454,32 @@ int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, in
   if (!valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
   if (!aligned16(out)) return IQ_ERR_MISALIGNED;
   if ((lse_out && !aligned16(lse_out)) || (argmax_out && !aligned16(argmax_out))) return IQ_ERR_MISALIGNED;
-  st = iq_decode_attention_partial(cfg, q, q_dtype, batch, num_q_heads, k, v, kv_len, max_kv_len,
-                                   softmax_scale, argmax_out != nullptr, workspace, workspace_bytes, stream);
+  st = decode_partial_impl(cfg, q, q_dtype, batch, num_q_heads, k, k_rope, rope_dim, v, kv_len, max_kv_len,
+                           softmax_scale, argmax_out != nullptr, workspace, workspace_bytes, stream);
   if (st != IQ_OK) return st;
   return iq_decode_attention_merge(cfg, batch, num_q_heads, max_kv_len, out, out_dtype, lse_out,
                                    argmax_out, workspace, workspace_bytes, stream);
+}
+
+}  // namespace
+
+int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
+                        int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
+                        const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out,
+                        int32_t out_dtype, float *lse_out, int32_t *argmax_out, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return decode_fused(cfg, q, q_dtype, batch, num_q_heads, k, nullptr, 0, v, kv_len, max_kv_len, softmax_scale,
+                      out, out_dtype, lse_out, argmax_out, workspace, workspace_bytes, stream);
+}
+
+int iq_decode_attention_rope(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
+                             int32_t num_q_heads, const iq_cache *k, const uint16_t *k_rope,
+                             int32_t rope_dim, const iq_cache *v, const int32_t *kv_len, int64_t max_kv_len,
+                             float softmax_scale, void *out, int32_t out_dtype, float *lse_out,
+                             int32_t *argmax_out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (rope_dim < 1) return IQ_ERR_INVALID_ARG;
+  return decode_fused(cfg, q, q_dtype, batch, num_q_heads, k, k_rope, rope_dim, v, kv_len, max_kv_len,
+                      softmax_scale, out, out_dtype, lse_out, argmax_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -5,6 +5,7 @@
 namespace iq {
 
 hipError_t launch_decode_128(int bits, const DecodeArgs &a, hipStream_t s) {
+  if (a.rope == kDecodeRope) return partial_dispatch_bits<128, kDecodeRope>(bits, a, s);
   return partial_dispatch_bits<128>(bits, a, s);
 }
 

@@ -20,10 +20,14 @@ constexpr int kDecodeStep = 32;            // tokens per wave iteration
 constexpr int kRecHeader = 4;              // M, L, best score, best position
 constexpr float kLazyTau = 4.0f;           // rescale only when the max grows by more than this
 constexpr float kWeightBias = 25.0f;       // weights 2^(s - M + bias) * ||v|| stay below 2^15
+constexpr int kDecodeRope = 64;            // RoPE coordinates per key the decode kernels take (head_dim 128)
 
 struct DecodeArgs {
-  const void *q;           // [batch][Hq][d]
+  const void *q;           // [batch][Hq][d + rope]
   int q_f16;
+  const uint16_t *krope;   // [batch][H_kv][kcap][rope] fp16 RoPE coordinates of the keys (rope > 0)
+  int rope;                // RoPE coordinates per key and query (0: none)
+  float rmul;              // softmax_scale * log2(e), applied to the query's RoPE part
   const uint8_t *kc;
   const uint16_t *kn;
   const uint8_t *vc;

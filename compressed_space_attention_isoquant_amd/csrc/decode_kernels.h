@@ -115,10 +115,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 
 // Layout of one wave's LDS stage: 32 packed K rows, 32 packed V rows, 32 K
-// norms, 32 V norms.  Rows sit RS = ROWB + PAD bytes apart; PAD (0 or one
-// 16-byte granule) is chosen per shape so that the row reads of a wave
-// spread over the LDS banks.
-template <int D, int BITS>
+// norms, 32 V norms, and with ROPE > 0 the keys' 32 fp16 RoPE rows.  Rows sit
+// RS = ROWB + PAD bytes apart; PAD (0 or one 16-byte granule) is chosen per
+// shape so that the row reads of a wave spread over the LDS banks; RoPE rows
+// are padded by one granule.
+template <int D, int BITS, int ROPE = 0>
 struct Stage {
   static constexpr int ROWB = D * BITS / 8;
   static constexpr int PAD = (D == 128 && BITS == 3) ? 0 : 16;
@@ -128,9 +129,14 @@ struct Stage {
   static constexpr int V_OFF = ROWS_B;
   static constexpr int KN_OFF = 2 * ROWS_B;
   static constexpr int VN_OFF = 2 * ROWS_B + 2 * kDecodeStep;
-  static constexpr int BYTES = 2 * ROWS_B + 4 * kDecodeStep;   // multiple of 16
   static constexpr int ROW_LOADS = (ROWS_B + 1023) / 1024;    // 16-byte-per-lane loads per row block
-  static constexpr int LOADS = 2 * ROW_LOADS + 2;             // buffer->LDS loads per stage
+  static constexpr int RROWB = ROPE * 2;                      // bytes of one RoPE row
+  static constexpr int RRS = ROPE ? RROWB + 16 : 0;
+  static constexpr int R_OFF = 2 * ROWS_B + 4 * kDecodeStep;
+  static constexpr int R_B = kDecodeStep * RRS;
+  static constexpr int R_LOADS = (R_B + 1023) / 1024;
+  static constexpr int BYTES = R_OFF + R_B;                   // multiple of 16
+  static constexpr int LOADS = 2 * ROW_LOADS + 2 + R_LOADS;   // buffer->LDS loads per stage
 };
 
 // Byte offset past every cache buffer (the host keeps each (sequence, head)
@@ -149,17 +155,28 @@ __device__ __forceinline__ uint32_t granule_offset(int c, int lane) {
   return o < S::ROWB / 16 ? (uint32_t)(r * S::ROWB + 16 * o) : kOutOfRange;
 }
 
+// The same for RoPE row load c (rows of RROWB bytes padded to RRS in LDS).
+template <int D, int BITS, int ROPE>
+__device__ __forceinline__ uint32_t rope_granule_offset(int c, int lane) {
+  using S = Stage<D, BITS, ROPE>;
+  const int g = 64 * c + lane;
+  const int r = g / (S::RRS / 16), o = g % (S::RRS / 16);
+  return o < S::RROWB / 16 ? (uint32_t)(r * S::RROWB + 16 * o) : kOutOfRange;
+}
+
 // Issue the asynchronous buffer->LDS loads of one 32-token stage starting at
 // token t0 (wave-uniform); stage_lds is the stage's LDS byte address and
 // goff[c] the lane's granule offsets.  The token offset rides in the per-lane
 // offset, which the buffer range check always covers.  A stage that is not
 // needed (valid false) is still issued, pointing out of range, so that every
 // stage counts the same number of loads.
-template <int D, int BITS>
+template <int D, int BITS, int ROPE>
 __device__ __forceinline__ void load_stage(uint32_t stage_lds, int32x4_t kr, int32x4_t vr, int32x4_t knr,
-                                           int32x4_t vnr, int t0, bool valid, int lane,
-                                           const uint32_t (&goff)[Stage<D, BITS>::ROW_LOADS]) {
-  using S = Stage<D, BITS>;
+                                           int32x4_t vnr, int32x4_t rr, int t0, bool valid, int lane,
+                                           const uint32_t (&goff)[Stage<D, BITS, ROPE>::ROW_LOADS],
+                                           const uint32_t (&groff)[Stage<D, BITS, ROPE>::R_LOADS > 0
+                                                                      ? Stage<D, BITS, ROPE>::R_LOADS : 1]) {
+  using S = Stage<D, BITS, ROPE>;
   const uint32_t row_off = valid ? (uint32_t)(t0 * S::ROWB) : kOutOfRange;
   const uint32_t norm_off = valid ? (uint32_t)(t0 * 2) : kOutOfRange;
 #pragma unroll
@@ -172,6 +189,12 @@ __device__ __forceinline__ void load_stage(uint32_t stage_lds, int32x4_t kr, int
   if (lane < kDecodeStep / 2) {
     dma_to_lds<4>(knr, stage_lds + S::KN_OFF, norm_off + lane * 4, 0);
     dma_to_lds<4>(vnr, stage_lds + S::VN_OFF, norm_off + lane * 4, 0);
+  }
+  if constexpr (ROPE > 0) {
+    const uint32_t rope_off = valid ? (uint32_t)(t0 * S::RROWB) : kOutOfRange;
+#pragma unroll
+    for (int c = 0; c < S::R_LOADS; ++c)
+      if (c * 1024 + lane * 16 < S::R_B) dma_to_lds<16>(rr, stage_lds + S::R_OFF + c * 1024, groff[c] + rope_off, 0);
   }
 }
 
@@ -200,20 +223,20 @@ constexpr int ilog2() {
 // wave next to its pair table and `extra` bytes (more waves hide latency
 // better than a deeper ring), else two; then as many stages as fit, up to 4,
 // at least 2 (double buffering).
-template <int D, int BITS>
+template <int D, int BITS, int ROPE = 0>
 constexpr int stages_fitting(int budget, int extra) {
   const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
-  return (budget - table - extra) / (kDecodeWaves * Stage<D, BITS>::BYTES);
+  return (budget - table - extra) / (kDecodeWaves * Stage<D, BITS, ROPE>::BYTES);
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int ROPE = 0>
 constexpr int resident_groups(int extra) {
-  return stages_fitting<D, BITS>(160 * 1024 / 3, extra) >= 3 ? 3 : 2;
+  return stages_fitting<D, BITS, ROPE>(160 * 1024 / 3, extra) >= 3 ? 3 : 2;
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int ROPE = 0>
 constexpr int stage_count(int extra) {
-  const int n = stages_fitting<D, BITS>(160 * 1024 / resident_groups<D, BITS>(extra), extra);
+  const int n = stages_fitting<D, BITS, ROPE>(160 * 1024 / resident_groups<D, BITS, ROPE>(extra), extra);
   return n > 4 ? 4 : (n < 2 ? 2 : n);
 }
 
@@ -221,15 +244,15 @@ constexpr int stage_count(int extra) {
 // layout: three where three workgroups share a CU (at most 168 registers per
 // lane), two where the LDS of two fits (head_dim <= 256; 256 registers),
 // else no constraint.
-template <int D, int BITS>
+template <int D, int BITS, int ROPE = 0>
 constexpr int partial_waves(int extra) {
   const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
-  const int lds = table + extra + kDecodeWaves * stage_count<D, BITS>(extra) * Stage<D, BITS>::BYTES;
-  return resident_groups<D, BITS>(extra) == 3 ? 3 : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
+  const int lds = table + extra + kDecodeWaves * stage_count<D, BITS, ROPE>(extra) * Stage<D, BITS, ROPE>::BYTES;
+  return resident_groups<D, BITS, ROPE>(extra) == 3 ? 3 : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
 }
 
-template <int D, int BITS, int G, bool ARGMAX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(partial_waves<D, BITS>(G * D * 4))))
+template <int D, int BITS, int G, bool ARGMAX, int ROPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(partial_waves<D, BITS, ROPE>(G * (D + ROPE) * 4))))
 void partial_kernel(DecodeArgs a) {
   constexpr int NLEV = 1 << BITS;
   constexpr int KS = D / 32;                 // k-steps of the score product
@@ -247,9 +270,11 @@ void partial_kernel(DecodeArgs a) {
   constexpr int VW = (VCB + 31) / 32 + 1;    // dwords read to cover them at any bit offset
   constexpr int VX = (VCB + 31) / 32;        // dwords after extraction
   constexpr int NROW = 2 * G;                // live rows/columns (hi + lo)
-  using S = Stage<D, BITS>;
-  constexpr int PRO_B = G * D * 4;                                  // prologue q~ staging
-  constexpr int NST = stage_count<D, BITS>(PRO_B);
+  using S = Stage<D, BITS, ROPE>;
+  constexpr int RK = ROPE / 32;                                     // k-steps of the RoPE score product
+  constexpr int DQ = D + ROPE;                                      // query coordinates
+  constexpr int PRO_B = G * DQ * 4;                                 // prologue q~ staging
+  constexpr int NST = stage_count<D, BITS, ROPE>(PRO_B);
   static_assert((NST - 1) * S::LOADS < 64, "in-flight loads exceed the vmcnt range");
   constexpr int STG_B = kDecodeWaves * NST * S::BYTES;              // ring of stages per wave
   constexpr int RED_B = kDecodeWaves * G * (D + 4) * 4;             // wave states at the end
@@ -285,8 +310,8 @@ void partial_kernel(DecodeArgs a) {
   // q~ staging in LDS of its own where it fits (then the first stages load
   // during the prologue), else in the stage memory (loads after it)
   constexpr bool EARLY = MAIN_B + NLEV * NLEV * REPL * 4 + PRO_B <= 160 * 1024;
-  __shared__ float qs_own[EARLY ? G : 1][EARLY ? D : 1];
-  float (*qs)[D] = EARLY ? reinterpret_cast<float (*)[D]>(&qs_own[0][0]) : reinterpret_cast<float (*)[D]>(smem);
+  __shared__ float qs_own[EARLY ? G : 1][EARLY ? DQ : 1];
+  float (*qs)[DQ] = EARLY ? reinterpret_cast<float (*)[DQ]>(&qs_own[0][0]) : reinterpret_cast<float (*)[DQ]>(smem);
 
   // The workgroup's tokens [base, end) are dealt to the waves tile by tile
   // (tile i to wave i mod 4), so that its waves finish together whatever the
@@ -300,11 +325,15 @@ void partial_kernel(DecodeArgs a) {
   const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
   const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
   const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
+  const int32x4_t rr = ROPE ? make_rsrc(a.krope + hrow * a.kcap * ROPE, (uint32_t)(a.kcap * ROPE * 2)) : kr;
   char *stages = smem + wave * NST * S::BYTES;
   const uint32_t stages_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(stages));
   uint32_t goff[S::ROW_LOADS];
 #pragma unroll
   for (int c = 0; c < S::ROW_LOADS; ++c) goff[c] = granule_offset<D, BITS>(c, lane);
+  uint32_t groff[S::R_LOADS > 0 ? S::R_LOADS : 1];
+#pragma unroll
+  for (int c = 0; c < S::R_LOADS; ++c) groff[c] = rope_granule_offset<D, BITS, ROPE>(c, lane);
   // this wave's tiles k = 0, 1, ...: workgroup tiles wave + 4k
   auto count = [&](int tiles) { return tiles > wave ? (tiles - wave + kDecodeWaves - 1) / kDecodeWaves : 0; };
   const int n_tiles = count((len + kDecodeStep - 1) / kDecodeStep);
@@ -315,16 +344,17 @@ void partial_kernel(DecodeArgs a) {
     if (n_tiles > 0) {
 #pragma unroll
       for (int i = 0; i < NST - 1; ++i)
-        load_stage<D, BITS>(stages_lds + i * S::BYTES, kr, vr, knr, vnr, tile_t0(i), i < n_tiles, lane, goff);
+        load_stage<D, BITS, ROPE>(stages_lds + i * S::BYTES, kr, vr, knr, vnr, rr, tile_t0(i), i < n_tiles, lane,
+                                  goff, groff);
     }
   };
   if constexpr (EARLY) first_stages();
 
   // ---- prologue: q~ = R q for this KV head's query heads --------------------
   for (int i = threadIdx.x; i < NLEV * NLEV * REPL; i += kThreads) lut[i] = a.lut[i / REPL];
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int hh = idx / D, i = idx % D;
-    const size_t off = ((size_t)b * a.hq + kvh * G + hh) * D + i;
+  for (int idx = threadIdx.x; idx < G * DQ; idx += kThreads) {
+    const int hh = idx / DQ, i = idx % DQ;
+    const size_t off = ((size_t)b * a.hq + kvh * G + hh) * DQ + i;
     qs[hh][i] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[off])
                         : static_cast<const float *>(a.q)[off];
   }
@@ -374,6 +404,19 @@ void partial_kernel(DecodeArgs a) {
       const float v = live ? qs[head][dim] : 0.f;
       const _Float16 hi = static_cast<_Float16>(v);
       qB[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
+    }
+  }
+  // B operand of the RoPE score product: k-step s of lane group g4 holds RoPE
+  // coordinates 32 s + 8 g4 .. +7 (the natural order of the RoPE rows), times
+  // softmax_scale * log2(e), hi and lo fp16 parts as for qB.
+  half8 qR[RK > 0 ? RK : 1];
+#pragma unroll
+  for (int s = 0; s < RK; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = live ? qs[head][D + 32 * s + 8 * g4 + e] * a.rmul : 0.f;
+      const _Float16 hi = static_cast<_Float16>(v);
+      qR[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
     }
   }
   if constexpr (!EARLY) {
@@ -502,6 +545,21 @@ void partial_kernel(DecodeArgs a) {
         S2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             as_half8(ka[tile][s][0], ka[tile][s][1], ka[tile][s][2], ka[tile][s][3]), qB[s], S2[tile], 0, 0, 0);
     }
+    // RoPE part of the scores (not scaled by the key norm): the keys' fp16
+    // RoPE rows straight from the stage, lane (token j, group g4)
+    floatx4 SR[2];
+    if constexpr (ROPE > 0) {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        SR[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < RK; ++s) {
+          const half8 kr8 = *reinterpret_cast<const half8 *>(cur + S::R_OFF + (16 * tile + j) * S::RRS +
+                                                             (32 * s + 8 * g4) * 2);
+          SR[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr8, qR[s], SR[tile], 0, 0, 0);
+        }
+      }
+    }
 
     // softmax on this lane's tile (hi lanes: tile 0, lo lanes: tile 1).
     // u = score + an upper bound of the value-norm exponent (byte 1 of its
@@ -512,6 +570,11 @@ void partial_kernel(DecodeArgs a) {
       const float own = my_tile ? S2[1][r] : S2[0][r];
       const float give = my_tile ? S2[0][r] : S2[1][r];      // what the partner lane needs
       float c = (own + xor_g<G>(give)) * half_bits_to_float(kb[r]);
+      if constexpr (ROPE > 0) {
+        const float rown = my_tile ? SR[1][r] : SR[0][r];
+        const float rgive = my_tile ? SR[0][r] : SR[1][r];
+        c += rown + xor_g<G>(rgive);
+      }
       if constexpr (!FULL) {
         const int tok = t0 + 16 * my_tile + 4 * g4 + r;
         c = (live && tok < end) ? c : -INFINITY;
@@ -596,8 +659,8 @@ void partial_kernel(DecodeArgs a) {
     for (int it = 0; it < n_full; ++it) {
       const int ahead = it + NST - 1;
       const int aslot = slot == 0 ? NST - 1 : slot - 1;     // (it + NST - 1) mod NST, processed last iteration
-      load_stage<D, BITS>(stages_lds + aslot * S::BYTES, kr, vr, knr, vnr, tile_t0(ahead), ahead < n_tiles, lane,
-                          goff);
+      load_stage<D, BITS, ROPE>(stages_lds + aslot * S::BYTES, kr, vr, knr, vnr, rr, tile_t0(ahead), ahead < n_tiles,
+                                lane, goff, groff);
       wait_vmem<(NST - 1) * S::LOADS>();
       process(stages + slot * S::BYTES, tile_t0(it), std::true_type{});
       slot = slot == NST - 1 ? 0 : slot + 1;
@@ -753,25 +816,33 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
   }
 }
 
-template <int D, int BITS, bool ARGMAX>
+template <int D, int BITS, bool ARGMAX, int ROPE>
 hipError_t partial_dispatch_group(const DecodeArgs &a, hipStream_t s) {
   dim3 grid((unsigned)a.hkv, (unsigned)a.batch, (unsigned)a.n_split);
   switch (a.group) {
-    case 1: hipLaunchKernelGGL((partial_kernel<D, BITS, 1, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((partial_kernel<D, BITS, 2, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((partial_kernel<D, BITS, 4, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((partial_kernel<D, BITS, 8, ARGMAX>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((partial_kernel<D, BITS, 1, ARGMAX, ROPE>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((partial_kernel<D, BITS, 2, ARGMAX, ROPE>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((partial_kernel<D, BITS, 4, ARGMAX, ROPE>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((partial_kernel<D, BITS, 8, ARGMAX, ROPE>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int BITS, int ROPE>
+hipError_t partial_dispatch_argmax(const DecodeArgs &a, hipStream_t s) {
+  return a.argmax ? partial_dispatch_group<D, BITS, true, ROPE>(a, s)
+                  : partial_dispatch_group<D, BITS, false, ROPE>(a, s);
+}
+
+// ROPE: the RoPE coordinates per key these instantiations take (0: none).
+template <int D, int ROPE = 0>
 hipError_t partial_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
+  if (a.rope != ROPE) return hipErrorInvalidValue;
   switch (bits) {
-    case 2: return a.argmax ? partial_dispatch_group<D, 2, true>(a, s) : partial_dispatch_group<D, 2, false>(a, s);
-    case 3: return a.argmax ? partial_dispatch_group<D, 3, true>(a, s) : partial_dispatch_group<D, 3, false>(a, s);
-    case 4: return a.argmax ? partial_dispatch_group<D, 4, true>(a, s) : partial_dispatch_group<D, 4, false>(a, s);
+    case 2: return partial_dispatch_argmax<D, 2, ROPE>(a, s);
+    case 3: return partial_dispatch_argmax<D, 3, ROPE>(a, s);
+    case 4: return partial_dispatch_argmax<D, 4, ROPE>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -33,15 +33,25 @@ struct CellTable {
 };
 
 struct QuantArgs {
-  const void *x;           // [batch][n][H_kv][d]
+  const void *x;           // [batch][n][H_kv][x_stride], the first d of each vector quantised
   const float *quats;      // [H_kv][d/4][2][4] (Full, Fast) or [H_kv][d/2][2] (Planar)
   const int32_t *start_pos;
   uint8_t *codes;          // [batch][H_kv][cap][row]
   uint16_t *norms;         // [batch][H_kv][cap]
   long long capacity;
   int batch, n, hkv;
+  int x_stride;            // elements from one input vector to the next (d, or d + RoPE coordinates)
   Tables tab;
   CellTable cells;
+};
+
+// The RoPE coordinates of the keys, copied unrotated and unquantised (fp16).
+struct RopeArgs {
+  const void *x;           // [batch][n][H_kv][d + r]
+  const int32_t *start_pos;
+  uint16_t *out;           // [batch][H_kv][cap][r] fp16 bits
+  long long capacity;
+  int batch, n, hkv, d, r;
 };
 
 struct DequantArgs {
@@ -60,6 +70,7 @@ hipError_t launch_quantize(int d, int bits, int variant, int in_f16, const Quant
                            hipStream_t s);
 hipError_t launch_dequantize(int d, int bits, int variant, int out_f16, const DequantArgs &a,
                              hipStream_t s);
+hipError_t launch_rope_copy(int in_f16, const RopeArgs &a, hipStream_t s);
 hipError_t launch_decode(int d, int bits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge(int d, int variant, const MergeArgs &a, hipStream_t s);
 

@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   auto fetch = [&](const VecPos &p, TIn (&x)[32], int &sp) {
     int b, t;
     clamp(p, b, t);
-    IO<TIn>::load32(static_cast<const TIn *>(a.x) + ((size_t)(b * n + t) * a.hkv + h) * D + 32 * j, x);
+    IO<TIn>::load32(static_cast<const TIn *>(a.x) + ((size_t)(b * n + t) * a.hkv + h) * a.x_stride + 32 * j, x);
     sp = a.start_pos[b];
   };
   // Workgroups stride over the vectors of one head, so the tables above are
@@ -471,6 +471,29 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   }
 }
 
+// RoPE coordinates (the last r of each input vector) to the fp16 side cache,
+// 8 coordinates (16 output bytes) per thread, grid-stride.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void rope_copy_kernel(RopeArgs a) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const int cpv = a.r / 8;                                   // chunks per vector
+  const long long total = (long long)a.batch * a.n * a.hkv * cpv;
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < total;
+       i += (long long)gridDim.x * kThreads) {
+    const int c = (int)(i % cpv);
+    const long long v = i / cpv;                             // (b * n + t) * hkv + h
+    const int h = (int)(v % a.hkv);
+    const long long bt = v / a.hkv;
+    const int t = (int)(bt % a.n), b = (int)(bt / a.n);
+    const TIn *src = static_cast<const TIn *>(a.x) + v * (a.d + a.r) + a.d + 8 * c;
+    h8 o;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = static_cast<_Float16>(src[k]);
+    const long long row = ((long long)b * a.hkv + h) * a.capacity + a.start_pos[b] + t;
+    *reinterpret_cast<h8 *>(a.out + row * a.r + 8 * c) = o;
+  }
+}
+
 // Workgroups per head: one per VPB vectors, at most about 2048 in all
 // (8 per compute unit), each then looping over its share.
 unsigned stage1_groups(long long nvec, int vpb, int hkv) {
@@ -545,6 +568,17 @@ hipError_t dequantize_dispatch_bits(int bits, int variant, int out_f16, const De
 }
 
 }  // namespace
+
+hipError_t launch_rope_copy(int in_f16, const RopeArgs &a, hipStream_t s) {
+  const long long chunks = (long long)a.batch * a.n * a.hkv * (a.r / 8);
+  long long g = (chunks + kThreads - 1) / kThreads;
+  if (g > 2048) g = 2048;
+  if (in_f16)
+    hipLaunchKernelGGL((rope_copy_kernel<_Float16>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((rope_copy_kernel<float>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(int d, int bits, int variant, int in_f16, const QuantArgs &a, hipStream_t s) {
   switch (d) {

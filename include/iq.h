@@ -123,6 +123,25 @@ int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype,
                        int32_t batch, int32_t n_new, const int32_t *start_pos,
                        const iq_cache *out, hipStream_t stream);
 
+/* Quantize and append keys with a RoPE sub-block (RotaryQuant §5, the
+ * MLA/RoPE limitation: positional coordinates must be neither rotated nor
+ * quantised).  Each key is (content, positional) with the rope_dim RoPE
+ * coordinates last; the content part (d coordinates) is quantised exactly as
+ * by iq_quantize_append (its own norm, rotation and codes), the RoPE part is
+ * stored unrotated and unquantised as fp16 (round to nearest even).
+ *   x:         [batch][n_new][H_kv][d + rope_dim] of x_dtype, 16-B aligned.
+ *   rope_dim:  multiple of 8, 8 .. 512 (IQ_ERR_UNSUPPORTED otherwise; decode
+ *              attention takes 64).
+ *   rope_out:  DEVICE [batch][H_kv][out->capacity][rope_dim] fp16 bits,
+ *              16-B aligned; row start_pos[b] + t receives vector t's RoPE
+ *              coordinates, like `out`.
+ * Other arguments and errors as iq_quantize_append.  Values have no RoPE part
+ * and use iq_quantize_append. */
+int iq_quantize_append_rope(const iq_config *cfg, const void *x, int32_t x_dtype,
+                            int32_t batch, int32_t n_new, int32_t rope_dim,
+                            const int32_t *start_pos, const iq_cache *out,
+                            uint16_t *rope_out, hipStream_t stream);
+
 /* Dequantize n rows per (sequence, KV head) starting at start_pos[b]
  * (the stage-1 return path of the IsoQuant abstract; inverse of RotaryQuant
  * eq. (2) as in §3.4):  out[b][t][h][:] = fp16(s) * R^T c[codes].
@@ -171,6 +190,27 @@ int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype,
                         float *lse_out, int32_t *argmax_out,
                         void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/* iq_decode_attention for keys with a RoPE sub-block (RotaryQuant §5, the
+ * MLA/RoPE limitation), written by iq_quantize_append_rope: the score of
+ * token j is softmax_scale * (q_content . k_j + q_rope . k_rope_j), where k_j
+ * is the content key held packed in k (attended in rotated space as in
+ * iq_decode_attention) and k_rope_j its fp16 RoPE coordinates, neither
+ * rotated nor scaled by the content norm.  Values have no RoPE part.
+ *   q:        [batch][Hq][d + rope_dim] of q_dtype, RoPE coordinates last.
+ *   k_rope:   DEVICE [batch][H_kv][k->capacity][rope_dim] fp16 bits, 16-B
+ *             aligned; k->capacity * rope_dim * 2 below 2^30 bytes.
+ *   rope_dim: 64, with head_dim 128 (IQ_ERR_UNSUPPORTED otherwise).
+ *   out:      [batch][Hq][d] (the content coordinates).
+ * Other arguments, workspace and errors as iq_decode_attention. */
+int iq_decode_attention_rope(const iq_config *cfg, const void *q, int32_t q_dtype,
+                             int32_t batch, int32_t num_q_heads,
+                             const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim,
+                             const iq_cache *v, const int32_t *kv_len, int64_t max_kv_len,
+                             float softmax_scale, void *out, int32_t out_dtype,
+                             float *lse_out, int32_t *argmax_out,
+                             void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Split phase of iq_decode_attention (the context is cut into splits, as in
  * FlashAttention's tiling that RotaryQuant §2 cites): rotates each query once,

@@ -25,7 +25,8 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) >= {"iq_quantize_append", "iq_dequantize", "iq_decode_attention",
                           "iq_decode_workspace_bytes", "iq_status_string", "iq_codebook",
-                          "iq_decode_attention_partial", "iq_decode_attention_merge"}
+                          "iq_decode_attention_partial", "iq_decode_attention_merge",
+                          "iq_quantize_append_rope", "iq_decode_attention_rope"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -237,3 +238,37 @@ def test_decode_workspace_geometry(batch, hq, hkv, d, max_len):
     got = L.iq_decode_workspace_bytes(ctypes.byref(cc), batch, hq, max_len)
     assert got == expected_workspace(batch, hq, hkv, d, max_len)
 
+
+
+def test_rope_validation():
+    """The RoPE entry points check their extra arguments before launching."""
+    L = B.lib()
+    c = cfg()
+    cc = c.c()
+    cache = B.IQCacheC(0x4000, 0x5000, 16)
+
+    def append(rope_dim, rope_out=0x9000, x=0x2000):
+        return L.iq_quantize_append_rope(ctypes.byref(cc), x, 1, 1, 4, rope_dim, 0x3000, ctypes.byref(cache),
+                                         rope_out, None)
+
+    assert append(0) == -1                      # use iq_quantize_append without RoPE coordinates
+    assert append(12) == -2                     # not a multiple of 8
+    assert append(520) == -2                    # above 512
+    assert append(64, rope_out=None) == -1
+    assert append(64, rope_out=0x9008) == -3
+
+    need = L.iq_decode_workspace_bytes(ctypes.byref(cc), 1, 32, 16)
+
+    def decode(rope_dim, k_rope=0x9000, conf=c, ws_bytes=need):
+        ccx = conf.c()
+        return L.iq_decode_attention_rope(ctypes.byref(ccx), 0x2000, 1, 1, 32, ctypes.byref(cache), k_rope,
+                                          rope_dim, ctypes.byref(cache), 0x8000, 16, 0.1, 0x6000, 0, None, None,
+                                          0x7000, ws_bytes, None)
+
+    assert decode(0) == -1
+    assert decode(32) == -2                     # the kernels take 64
+    assert decode(64, k_rope=None) == -1
+    assert decode(64, k_rope=0x9004) == -3
+    big = cfg(d=256)
+    assert decode(64, conf=big, ws_bytes=L.iq_decode_workspace_bytes(ctypes.byref(big.c()), 1, 32, 16)) == -2
+    assert decode(64, ws_bytes=need - 1) == -4
