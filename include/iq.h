@@ -12,12 +12,17 @@
  *     row = BitPack_b(codes), norm = fp16(s).
  *     R_SO(4) acts on contiguous 4-element blocks seen as quaternions:
  *     Full: v -> q_L v conj(q_R); Fast: v -> q_L v (IsoQuant abstract).
+ *     Planar, the framework's 2-D special case: each coordinate pair, seen as
+ *     a complex number, times a unit complex number.
  *   dequantize (RotaryQuant §3.4: R^-1 = R^T via the same butterfly and the
  *     block transpose): x' = fp16(s) * H_d R_SO(4)^T c[codes].
  *   decode attention (RotaryQuant §3.4 Table 2 and Appendix A): q~ = R q once
  *     per query head, scores and an online softmax on the packed K rows in
  *     rotated space, value accumulation on the packed V rows in rotated space,
  *     one R^T on the aggregated output.  No fp16/fp32 K or V is written.
+ *   RoPE sub-block (RotaryQuant §5, the MLA/RoPE limitation): keys whose last
+ *     coordinates are RoPE coordinates keep those unrotated and unquantised
+ *     in fp16; their dot product with the query's RoPE part joins the score.
  *
  * Conventions shared by every entry point
  *   - Every pointer is DEVICE memory owned by the caller unless marked HOST.
@@ -38,11 +43,13 @@
  *   quaternions         [H_kv][d/4][2][4] fp32, (w,x,y,z), q_L then q_R, unit
  *                       length; one rotation per KV head shared by K, V and the
  *                       query heads of that group (RotaryQuant Appendix A).
+ *                       Planar: [H_kv][d/2][2] fp32 (cos, sin).
  *   packed codes        [batch][H_kv][capacity][d*b/8]   uint8
  *                       LSB-first bitstream: bit r of code i is bit (b*i + r)
  *                       of the row, bytes little-endian (d*b/8 = 48 bytes at
  *                       d = 128, b = 3, RotaryQuant §3.2 Step 4).
  *   norms               [batch][H_kv][capacity]          IEEE fp16 bits
+ *   RoPE side cache     [batch][H_kv][capacity][r]       IEEE fp16 bits
  *   queries / outputs   [batch][Hq][d]                   fp32 or fp16
  *   code of a value v:  number of thresholds t_k = (c_k + c_{k+1})/2 with
  *                       v > t_k (ascending centroids c).
