@@ -216,9 +216,7 @@ int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out) {
   return IQ_OK;
 }
 
-namespace {
-
-int quantize_append_impl(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch, int32_t n_new,
+static int quantize_append_impl(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch, int32_t n_new,
                          int32_t rope_dim, const int32_t *start_pos, const iq_cache *out, uint16_t *rope_out,
                          hipStream_t stream) {
   int st = check_config(cfg);
@@ -262,8 +260,6 @@ int quantize_append_impl(const iq_config *cfg, const void *x, int32_t x_dtype, i
   r.r = rope_dim;
   return hip_status(iq::launch_rope_copy(x_dtype == IQ_F16, r, stream));
 }
-
-}  // namespace
 
 int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch,
                        int32_t n_new, const int32_t *start_pos, const iq_cache *out,
@@ -330,11 +326,9 @@ static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_
   return IQ_OK;
 }
 
-namespace {
-
 // The split phase; with rope_dim > 0 the keys carry rope_dim fp16 RoPE
 // coordinates in k_rope and the query d + rope_dim coordinates.
-int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
+static int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
                         int32_t num_q_heads, const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim,
                         const iq_cache *v, const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
                         int32_t track_argmax, void *workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -401,8 +395,6 @@ int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dtype, in
   return hip_status(iq::launch_decode(cfg->head_dim, cfg->bits, a, stream));
 }
 
-}  // namespace
-
 int iq_decode_attention_partial(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
                                 int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
                                 const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
@@ -439,9 +431,7 @@ int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q
   return hip_status(iq::launch_merge(cfg->head_dim, cfg->variant, m, stream));
 }
 
-namespace {
-
-int decode_fused(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+static int decode_fused(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                  const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim, const iq_cache *v,
                  const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out, int32_t out_dtype,
                  float *lse_out, int32_t *argmax_out, void *workspace, size_t workspace_bytes,
@@ -460,8 +450,6 @@ int decode_fused(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t b
   return iq_decode_attention_merge(cfg, batch, num_q_heads, max_kv_len, out, out_dtype, lse_out,
                                    argmax_out, workspace, workspace_bytes, stream);
 }
-
-}  // namespace
 
 int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
                         int32_t num_q_heads, const iq_cache *k, const iq_cache *v,
