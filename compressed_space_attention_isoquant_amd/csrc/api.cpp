@@ -217,8 +217,8 @@ int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out) {
 }
 
 static int quantize_append_impl(const iq_config *cfg, const void *x, int32_t x_dtype, int32_t batch, int32_t n_new,
-                         int32_t rope_dim, const int32_t *start_pos, const iq_cache *out, uint16_t *rope_out,
-                         hipStream_t stream) {
+                                int32_t rope_dim, const int32_t *start_pos, const iq_cache *out, uint16_t *rope_out,
+                                hipStream_t stream) {
   int st = check_config(cfg);
   if (st != IQ_OK) return st;
   if (!x || !start_pos) return IQ_ERR_INVALID_ARG;
@@ -329,9 +329,9 @@ static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_
 // The split phase; with rope_dim > 0 the keys carry rope_dim fp16 RoPE
 // coordinates in k_rope and the query d + rope_dim coordinates.
 static int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch,
-                        int32_t num_q_heads, const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim,
-                        const iq_cache *v, const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
-                        int32_t track_argmax, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                               int32_t num_q_heads, const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim,
+                               const iq_cache *v, const int32_t *kv_len, int64_t max_kv_len, float softmax_scale,
+                               int32_t track_argmax, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   int group = 0;
   int st = check_decode_common(cfg, batch, num_q_heads, max_kv_len, workspace, workspace_bytes, &group);
   if (st != IQ_OK) return st;
@@ -432,10 +432,10 @@ int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q
 }
 
 static int decode_fused(const iq_config *cfg, const void *q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
-                 const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim, const iq_cache *v,
-                 const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out, int32_t out_dtype,
-                 float *lse_out, int32_t *argmax_out, void *workspace, size_t workspace_bytes,
-                 hipStream_t stream) {
+                        const iq_cache *k, const uint16_t *k_rope, int32_t rope_dim, const iq_cache *v,
+                        const int32_t *kv_len, int64_t max_kv_len, float softmax_scale, void *out, int32_t out_dtype,
+                        float *lse_out, int32_t *argmax_out, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   // validate both phases before enqueueing either
   int group = 0;
   int st = check_decode_common(cfg, batch, num_q_heads, max_kv_len, workspace, workspace_bytes, &group);
