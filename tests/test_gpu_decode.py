@@ -346,6 +346,53 @@ def test_sorted_work_order_batch():
                       check_arg=True)
 
 
+def test_uniform_32k_batched_sampled():
+    """The long-context head layout batched to fill the GPU (64 sequences of
+    32,768 tokens, 32 query / 4 KV heads, d=128, 3-bit Full), in the split +
+    merge launch configuration the benchmark times (no argmax, fp16 output);
+    two sampled sequences against the oracle, the fp16 output within one fp16
+    step of the fused call's fp32 output."""
+    t = torch()
+    d, bits, hq, hkv, batch, T = 128, 3, 32, 4, 64, 32768
+    rng = np.random.default_rng(27)
+    ch_k = inputs.outlier_channels(rng, hkv, d)
+    ch_v = inputs.outlier_channels(rng, hkv, d)
+    cfg, quats = make_config(d, bits, O.FULL, hkv)
+    kc = B.new_cache(batch, hkv, T, d, bits, DEV)
+    vc = B.new_cache(batch, hkv, T, d, bits, DEV)
+    zero = t.zeros((1,), dtype=t.int32, device=DEV)
+    for b in range(batch):
+        for cache, idx, ch in ((kc, 2 * b, ch_k), (vc, 2 * b + 1, ch_v)):
+            x = inputs.device_kv(27, idx, T, ch, d, DEV)
+            B.iq_quantize_append(cfg, x[None], zero, B.PackedCache(cache.codes[b:b + 1], cache.norms[b:b + 1]))
+    q = inputs.device_normal(27, 99_999, (batch, hq, d), DEV, t.float16)
+    kv_len = t.full((batch,), T, dtype=t.int32, device=DEV)
+    ws = t.empty((B.iq_decode_workspace_bytes(cfg, batch, hq, T),), dtype=t.uint8, device=DEV)
+    out16 = t.empty((batch, hq, d), dtype=t.float16, device=DEV)
+    B.iq_decode_attention_partial(cfg, q, kc, vc, kv_len, T, scale_for(d), ws, track_argmax=False)
+    B.iq_decode_attention_merge(cfg, batch, hq, T, out16, None, None, ws)
+    out = t.empty((batch, hq, d), dtype=t.float32, device=DEV)
+    lse = t.empty((batch, hq), dtype=t.float32, device=DEV)
+    arg = t.empty((batch, hq), dtype=t.int32, device=DEV)
+    B.iq_decode_attention(cfg, q, kc, vc, kv_len, T, scale_for(d), out, lse, arg, ws)
+    t.cuda.synchronize()
+    got, glse, garg = out.cpu().numpy().astype(np.float64), lse.cpu().numpy(), arg.cpu().numpy()
+    g16 = out16.cpu().numpy().astype(np.float64)
+    step = np.abs(np.spacing(got.astype(np.float16)).astype(np.float64))
+    assert np.all(np.abs(g16 - got) <= step + 1e-6 * np.abs(got))
+    qh = q.cpu().numpy()
+    cb = O.codebook(bits, d)
+    for b in (0, int(rng.integers(1, batch))):
+        kx = inputs.device_kv(27, 2 * b, T, ch_k, d, DEV).cpu().numpy()
+        vx = inputs.device_kv(27, 2 * b + 1, T, ch_v, d, DEV).cpu().numpy()
+        gk = (kc.codes[b].cpu().numpy(), kc.norms[b].cpu().numpy().view(np.uint16))
+        gv = (vc.codes[b].cpu().numpy(), vc.norms[b].cpu().numpy().view(np.uint16))
+        kr, kn, _ = oracle_cache(kx, quats, cb, O.FULL, bits, gk[0], gk[1])
+        vr, vn, _ = oracle_cache(vx, quats, cb, O.FULL, bits, gv[0], gv[1])
+        ro, rl, ra = O.attend(qh[b], kr, kn, vr, vn, quats, cb, bits, O.FULL, scale_for(d))
+        check_outputs(f"uniform 32K: sequence {b}", got[b], glse[b], garg[b], ro, rl, ra, 2e-3, check_arg=True)
+
+
 def test_c5_batched_append_decode():
     """64 sequences, lengths U[1024, 32768], Hq=16, H_kv=8, d=256, 3-bit, Fast:
     each step appends one K and one V token per sequence then attends over
