@@ -589,7 +589,7 @@ def run_stage1(torch, dev):
 
 
 # Kernels whose HBM traffic is recorded, by the workload they run in.
-TRAFFIC_KERNELS = {"headline": "partial_kernel<256, 3, 2, false>", "uniform_32k": "partial_kernel<128, 3, 8, false>"}
+TRAFFIC_KERNELS = {"headline": "partial_kernel<256, 3, 2, false, 0>", "uniform_32k": "partial_kernel<128, 3, 8, false, 0>"}
 
 
 def summarize_counters(fetch_csv, write_csv):
