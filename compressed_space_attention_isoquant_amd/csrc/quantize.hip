@@ -128,6 +128,38 @@ __device__ __forceinline__ float lane_sign(int j) {
   return (__builtin_popcount(j & (LPV - 1)) & 1) ? -1.f : 1.f;
 }
 
+// r[k] += sign * r[k] of lane (lane ^ M), k = K0 .. K0+7, for M = 1, 2, 8:
+// one v_fmac_f32 per value whose first operand is read through DPP, so the
+// exchange costs no instruction of its own (the compiler keeps a separate
+// DPP move here).  The leading s_nop gives the two wait states a DPP read
+// needs after a VALU write of the same register; the same fused multiply-add
+// as fmaf, so results are unchanged.
+#define IQ_DPP_FMAC8(CTRL)                                                                        \
+  asm volatile("s_nop 1\n"                                                                       \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                   \
+               : "+v"(r[K0]), "+v"(r[K0 + 1]), "+v"(r[K0 + 2]), "+v"(r[K0 + 3]), "+v"(r[K0 + 4]), \
+                 "+v"(r[K0 + 5]), "+v"(r[K0 + 6]), "+v"(r[K0 + 7])                               \
+               : "v"(sign))
+
+template <int M, int K0>
+__device__ __forceinline__ void dpp_fmac8(float (&r)[32], float sign) {
+  static_assert(M == 1 || M == 2 || M == 8, "DPP exchange");
+  if constexpr (M == 1)
+    IQ_DPP_FMAC8("quad_perm:[1,0,3,2]");
+  else if constexpr (M == 2)
+    IQ_DPP_FMAC8("quad_perm:[2,3,0,1]");
+  else
+    IQ_DPP_FMAC8("row_ror:8");
+}
+#undef IQ_DPP_FMAC8
+
 template <int LPV, bool DPP>
 __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
 #pragma unroll
@@ -144,8 +176,15 @@ __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
   static_for_pow2<LPV>([&](auto hl_c) {
     constexpr int hl = decltype(hl_c)::value;
     const float sign = (j & hl) ? -1.f : 1.f;
+    if constexpr (hl == 1 || hl == 2 || hl == 8) {
+      dpp_fmac8<hl, 0>(r, sign);
+      dpp_fmac8<hl, 8>(r, sign);
+      dpp_fmac8<hl, 16>(r, sign);
+      dpp_fmac8<hl, 24>(r, sign);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) r[k] = fmaf(lane_xor<hl, DPP>(r[k]), sign, r[k]);
+      for (int k = 0; k < 32; ++k) r[k] = fmaf(lane_xor<hl, DPP>(r[k]), sign, r[k]);
+    }
     // Finish the stage before the next: left to itself the scheduler runs
     // each value through all stages in turn, one exchange latency at a time.
     __builtin_amdgcn_sched_barrier(0);
@@ -257,10 +296,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     const int sp = spn;
     fetch(nxt, xn, spn);
 
-    // s = ||x||_2 (fp32 sum of squares, tree over the vector's lanes)
-    float ss = 0.f;
+    // s = ||x||_2 (fp32 sum of squares: four interleaved partial sums per
+    // lane, then a tree over the vector's lanes)
+    float sp4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 32; ++k) ss = fmaf((float)xin[k], (float)xin[k], ss);
+    for (int k = 0; k < 32; ++k) sp4[k & 3] = fmaf((float)xin[k], (float)xin[k], sp4[k & 3]);
+    float ss = (sp4[0] + sp4[1]) + (sp4[2] + sp4[3]);
 #pragma unroll
     for (int m = 1; m < LPV; m <<= 1) ss += shfl_xor(ss, m);
     const float s = sqrtf(ss);
