@@ -747,34 +747,94 @@ void partial_kernel(DecodeArgs a) {
   }
 }
 
+constexpr int kMergeChunk = 1024;          // split records whose weights are staged in LDS at a time
+
 template <int D, int VARIANT>
 __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
+  constexpr int RS = D + kRecHeader;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int g = h / a.group;
   const int i = threadIdx.x;
-  const float *recs = a.ws + ((size_t)b * a.hq + h) * a.n_part * (D + kRecHeader);
+  const int n = a.n_part;
+  const float *recs = a.ws + ((size_t)b * a.hq + h) * n * RS;
+  __shared__ float red[D];
+  __shared__ int redi[D];
+  __shared__ float wbuf[kMergeChunk];
 
-  float M = -INFINITY;
-  for (int p = 0; p < a.n_part; ++p) {
-    const float *rec = recs + (size_t)p * (D + kRecHeader);
-    if (rec[1] > 0.f) M = fmaxf(M, rec[0]);
-  }
-  float L = 0.f, o = 0.f, bsc = -INFINITY;
-  int arg = -1;
-  for (int p = 0; p < a.n_part; ++p) {
-    const float *rec = recs + (size_t)p * (D + kRecHeader);
-    const float lp = rec[1];
-    if (lp > 0.f) {
-      const float w = exp2f(rec[0] - M);
-      L += lp * w;
-      o += rec[kRecHeader + i] * w;
-      if (rec[2] > bsc) {          // strict: ties keep the earlier (lower) positions
-        bsc = rec[2];
-        arg = __builtin_bit_cast(int, rec[3]);
+  // Headers are read in parallel (thread t: records t, t + D, ...): the
+  // running maximum and the best score with its position (ties: the lower
+  // position; splits cover increasing positions).
+  float Mt = -INFINITY, bt = -INFINITY;
+  int at = -1;
+  for (int p = i; p < n; p += D) {
+    const float *rec = recs + (size_t)p * RS;
+    if (rec[1] > 0.f) {
+      Mt = fmaxf(Mt, rec[0]);
+      const float sc = rec[2];
+      const int pos = __builtin_bit_cast(int, rec[3]);
+      if (sc > bt || (sc == bt && pos < at)) {
+        bt = sc;
+        at = pos;
       }
     }
   }
+  red[i] = Mt;
+  __syncthreads();
+  for (int st = D / 2; st > 0; st >>= 1) {
+    if (i < st) red[i] = fmaxf(red[i], red[i + st]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  red[i] = bt;
+  redi[i] = at;
+  __syncthreads();
+  for (int st = D / 2; st > 0; st >>= 1) {
+    if (i < st) {
+      const float os = red[i + st];
+      const int oj = redi[i + st];
+      if (os > red[i] || (os == red[i] && oj >= 0 && (redi[i] < 0 || oj < redi[i]))) {
+        red[i] = os;
+        redi[i] = oj;
+      }
+    }
+    __syncthreads();
+  }
+  const float bsc = red[0];
+  const int arg = redi[0];
+  __syncthreads();
+
+  // Weights 2^(M_p - M) (0 for empty splits) staged in LDS chunk by chunk;
+  // each thread then sums its coordinate over the records in split order,
+  // with independent loads.
+  float Lt = 0.f, o = 0.f;
+  for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
+    const int cn = min(kMergeChunk, n - c0);
+    for (int p = i; p < cn; p += D) {
+      const float *rec = recs + (size_t)(c0 + p) * RS;
+      const float lp = rec[1];
+      const float w = lp > 0.f ? exp2f(rec[0] - M) : 0.f;
+      wbuf[p] = w;
+      Lt += lp > 0.f ? lp * w : 0.f;
+    }
+    __syncthreads();
+    const float *col = recs + (size_t)c0 * RS + kRecHeader + i;
+#pragma unroll 8
+    for (int p = 0; p < cn; ++p) {
+      const float w = wbuf[p];
+      const float v = col[(size_t)p * RS];
+      o += w > 0.f ? v * w : 0.f;
+    }
+    __syncthreads();
+  }
+  red[i] = Lt;
+  __syncthreads();
+  for (int st = D / 2; st > 0; st >>= 1) {
+    if (i < st) red[i] += red[i + st];
+    __syncthreads();
+  }
+  const float L = red[0];
 
   __shared__ float y[D];
   y[i] = L > 0.f ? o * a.oscale / L : 0.f;
