@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.iq_quantize_append.argtypes = [ctypes.POINTER(IQConfigC), P, i32, i32, i32, P,
                                          ctypes.POINTER(IQCacheC), P]
         L.iq_quantize_append.restype = ctypes.c_int
+        L.iq_quantize_append_many.argtypes = [ctypes.POINTER(IQConfigC), i32, ctypes.POINTER(ctypes.c_void_p), i32,
+                                              i32, i32, P, ctypes.POINTER(IQCacheC), P]
+        L.iq_quantize_append_many.restype = ctypes.c_int
         L.iq_quantize_append_rope.argtypes = [ctypes.POINTER(IQConfigC), P, i32, i32, i32, i32, P,
                                               ctypes.POINTER(IQCacheC), P, P]
         L.iq_quantize_append_rope.restype = ctypes.c_int
@@ -184,6 +187,38 @@ def iq_quantize_append(cfg: Config, x, start_pos, out: PackedCache, stream=None)
     cc, oc = cfg.c(), out.c()
     _check(lib().iq_quantize_append(ctypes.byref(cc), _ptr(x), _dtype_code(x), batch, n_new,
                                     _ptr(start_pos), ctypes.byref(oc), _stream(stream)))
+
+
+def prepare_append_many(cfgs, xs, outs):
+    """Marshal the arguments of iq_quantize_append_many once: returns
+    f(start_pos, stream=None) that enqueues the call (the tensors must stay
+    alive and in place).  Tensor i: xs[i] (B, n_new, H_kv, d), quantised with
+    cfgs[i] into outs[i]; all of one shape, dtype and codebook."""
+    n = len(xs)
+    if not (len(cfgs) == n == len(outs)) or n == 0:
+        raise ValueError("cfgs, xs and outs must be non-empty lists of one length")
+    batch, n_new = int(xs[0].shape[0]), int(xs[0].shape[1])
+    for x in xs:
+        if tuple(x.shape) != tuple(xs[0].shape) or x.dtype != xs[0].dtype:
+            raise ValueError("every input must have the first one's shape and dtype")
+    keep = [c.c() for c in cfgs]
+    cc = (IQConfigC * n)(*keep)
+    xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    oc = (IQCacheC * n)(*[o.c() for o in outs])
+    dt = _dtype_code(xs[0])
+    L = lib()
+
+    def call(start_pos, stream=None):
+        _check(L.iq_quantize_append_many(cc, n, xp, dt, batch, n_new, _ptr(start_pos), oc, _stream(stream)))
+
+    call.keep = (keep, cfgs, xs, outs)
+    return call
+
+
+def iq_quantize_append_many(cfgs, xs, start_pos, outs, stream=None) -> None:
+    """Tensor i: xs[i] (B, n_new, H_kv, d), quantised with cfgs[i] into outs[i];
+    all of one shape, dtype and codebook; start_pos int32 (B,) device tensor."""
+    prepare_append_many(cfgs, xs, outs)(start_pos, stream)
 
 
 def iq_quantize_append_rope(cfg: Config, x, rope_dim: int, start_pos, out: PackedCache, rope_out,

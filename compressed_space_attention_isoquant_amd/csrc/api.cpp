@@ -234,13 +234,10 @@ static int quantize_append_impl(const iq_config *cfg, const void *x, int32_t x_d
     if (!aligned16(rope_out)) return IQ_ERR_MISALIGNED;
   }
   iq::QuantArgs a;
-  a.x = x;
+  a.ntens = 1;
+  a.t[0] = iq::AppendTensor{x, cfg->quats, out->codes, out->norms, out->capacity};
   a.x_stride = cfg->head_dim + rope_dim;
-  a.quats = cfg->quats;
   a.start_pos = start_pos;
-  a.codes = out->codes;
-  a.norms = out->norms;
-  a.capacity = out->capacity;
   a.batch = batch;
   a.n = n_new;
   a.hkv = cfg->num_kv_heads;
@@ -272,6 +269,51 @@ int iq_quantize_append_rope(const iq_config *cfg, const void *x, int32_t x_dtype
                             const iq_cache *out, uint16_t *rope_out, hipStream_t stream) {
   if (rope_dim < 1) return IQ_ERR_INVALID_ARG;
   return quantize_append_impl(cfg, x, x_dtype, batch, n_new, rope_dim, start_pos, out, rope_out, stream);
+}
+
+int iq_quantize_append_many(const iq_config *cfgs, int32_t count, const void *const *xs, int32_t x_dtype,
+                            int32_t batch, int32_t n_new, const int32_t *start_pos, const iq_cache *outs,
+                            hipStream_t stream) {
+  if (!cfgs || !xs || !outs || count < 1) return IQ_ERR_INVALID_ARG;
+  // every tensor: valid on its own, the same shape and codebook as the first
+  for (int32_t i = 0; i < count; ++i) {
+    const iq_config *c = &cfgs[i];
+    int st = check_config(c);
+    if (st != IQ_OK) return st;
+    if (c->head_dim != cfgs[0].head_dim || c->bits != cfgs[0].bits || c->variant != cfgs[0].variant ||
+        c->num_kv_heads != cfgs[0].num_kv_heads)
+      return IQ_ERR_INVALID_ARG;
+    for (int k = 0; k < (1 << c->bits); ++k)
+      if (c->centroids[k] != cfgs[0].centroids[k]) return IQ_ERR_INVALID_ARG;
+    if (!xs[i]) return IQ_ERR_INVALID_ARG;
+    if (!aligned16(xs[i])) return IQ_ERR_MISALIGNED;
+    st = check_cache(&outs[i]);
+    if (st != IQ_OK) return st;
+    if (n_new > outs[i].capacity) return IQ_ERR_INVALID_ARG;
+  }
+  if (!start_pos) return IQ_ERR_INVALID_ARG;
+  if (!valid_dtype(x_dtype)) return IQ_ERR_UNSUPPORTED;
+  if (batch < 1 || n_new < 1 || !vector_count_ok(batch, n_new)) return IQ_ERR_INVALID_ARG;
+  const iq_config *cfg = &cfgs[0];
+  iq::QuantArgs a;
+  a.x_stride = cfg->head_dim;
+  a.start_pos = start_pos;
+  a.batch = batch;
+  a.n = n_new;
+  a.hkv = cfg->num_kv_heads;
+  a.tab = make_tables(cfg);
+  a.cells = make_cells(a.tab, cfg->bits);
+  for (int32_t i0 = 0; i0 < count; i0 += iq::kMaxAppendTensors) {
+    a.ntens = std::min<int32_t>(iq::kMaxAppendTensors, count - i0);
+    for (int k = 0; k < a.ntens; ++k) {
+      const int32_t i = i0 + k;
+      a.t[k] = iq::AppendTensor{xs[i], cfgs[i].quats, outs[i].codes, outs[i].norms, outs[i].capacity};
+    }
+    const int st = hip_status(iq::launch_quantize(cfg->head_dim, cfg->bits, cfg->variant, x_dtype == IQ_F16, a,
+                                                  stream));
+    if (st != IQ_OK) return st;
+  }
+  return IQ_OK;
 }
 
 int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch, const int32_t *start_pos,

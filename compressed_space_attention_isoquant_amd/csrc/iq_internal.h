@@ -32,13 +32,23 @@ struct CellTable {
   uint2 e[kMaxCells];
 };
 
-struct QuantArgs {
+// One tensor of an append: its input, rotation and cache.
+struct AppendTensor {
   const void *x;           // [batch][n][H_kv][x_stride], the first d of each vector quantised
   const float *quats;      // [H_kv][d/4][2][4] (Full, Fast) or [H_kv][d/2][2] (Planar)
-  const int32_t *start_pos;
   uint8_t *codes;          // [batch][H_kv][cap][row]
   uint16_t *norms;         // [batch][H_kv][cap]
   long long capacity;
+};
+
+// Tensors one quantize launch takes (grid z); each shares the shape, the
+// codebook and the append positions.
+constexpr int kMaxAppendTensors = 16;
+
+struct QuantArgs {
+  AppendTensor t[kMaxAppendTensors];
+  int ntens;
+  const int32_t *start_pos;
   int batch, n, hkv;
   int x_stride;            // elements from one input vector to the next (d, or d + RoPE coordinates)
   Tables tab;

@@ -249,10 +249,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   constexpr int NLEV = 1 << BITS;
   constexpr int ROWB = D * BITS / 8;     // packed row bytes
   const int h = blockIdx.y;
+  const AppendTensor &T = a.t[blockIdx.z];
 
   __shared__ BlockMatrices<LPV> qm;      // block rotation matrices of this head
   __shared__ uint2 cells[kMaxCells];
-  load_block_matrices<D, VARIANT, true>(qm, a.quats + (size_t)h * (D / 4) * block_param_floats(VARIANT));
+  load_block_matrices<D, VARIANT, true>(qm, T.quats + (size_t)h * (D / 4) * block_param_floats(VARIANT));
   static_assert(kMaxCells <= kThreads, "one cell per thread");
   if ((int)threadIdx.x < a.cells.n) cells[threadIdx.x] = a.cells.e[threadIdx.x];
   __syncthreads();
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   auto fetch = [&](const VecPos &p, TIn (&x)[32], int &sp) {
     int b, t;
     clamp(p, b, t);
-    IO<TIn>::load32(static_cast<const TIn *>(a.x) + ((size_t)(b * n + t) * a.hkv + h) * a.x_stride + 32 * j, x);
+    IO<TIn>::load32(static_cast<const TIn *>(T.x) + ((size_t)(b * n + t) * a.hkv + h) * a.x_stride + 32 * j, x);
     sp = a.start_pos[b];
   };
   // Workgroups stride over the vectors of one head, so the tables above are
@@ -369,8 +370,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     // every lane of the vector stores the (same) norm
     int b, t;
     clamp(cur, b, t);
-    const long long row = ((long long)b * a.hkv + h) * a.capacity + sp + t;
-    uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + row * ROWB + 4 * BITS * j);
+    const long long row = ((long long)b * a.hkv + h) * T.capacity + sp + t;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(T.codes + row * ROWB + 4 * BITS * j);
     if constexpr (BITS == 4) {
       *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     } else if constexpr (BITS == 2) {
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 #pragma unroll
       for (int i = 0; i < BITS; ++i) dst[i] = w[i];
     }
-    a.norms[row] = float_to_half_bits(s);
+    T.norms[row] = float_to_half_bits(s);
     cur = nxt;
     nxt.advance(sq, sr, n);
   }
@@ -535,11 +536,11 @@ __global__ __launch_bounds__(kThreads) void rope_copy_kernel(RopeArgs a) {
   }
 }
 
-// Workgroups per head: one per VPB vectors, at most about 2048 in all
-// (8 per compute unit), each then looping over its share.
-unsigned stage1_groups(long long nvec, int vpb, int hkv) {
+// Workgroups per head (and tensor): one per VPB vectors, at most about 2048
+// in all (8 per compute unit), each then looping over its share.
+unsigned stage1_groups(long long nvec, int vpb, int heads) {
   long long g = (nvec + vpb - 1) / vpb;
-  const long long cap = (2048 + hkv - 1) / hkv;
+  const long long cap = (2048 + heads - 1) / heads;
   if (g > cap) g = cap;
   return (unsigned)(g < 1 ? 1 : g);
 }
@@ -548,7 +549,7 @@ template <int D, int BITS, int VARIANT>
 hipError_t quantize_dispatch_io(int in_f16, const QuantArgs &a, hipStream_t s) {
   constexpr int VPB = (64 / (D / 32)) * (kThreads / 64);
   const long long nvec = (long long)a.batch * a.n;
-  dim3 grid(stage1_groups(nvec, VPB, a.hkv), (unsigned)a.hkv);
+  dim3 grid(stage1_groups(nvec, VPB, a.hkv * a.ntens), (unsigned)a.hkv, (unsigned)a.ntens);
   if (in_f16)
     hipLaunchKernelGGL((quantize_kernel<D, BITS, VARIANT, _Float16>), grid, dim3(kThreads), 0, s, a);
   else

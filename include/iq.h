@@ -130,6 +130,24 @@ int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype,
                        int32_t batch, int32_t n_new, const int32_t *start_pos,
                        const iq_cache *out, hipStream_t stream);
 
+/* iq_quantize_append for `count` tensors of the same shape in one go, e.g.
+ * the K and V buffers of every layer at the prefill -> decode boundary
+ * (RotaryQuant §3.4 deferred prefill, Appendix C): tensor i quantises xs[i]
+ * with cfgs[i] into outs[i].  One launch covers up to 16 tensors.
+ *   cfgs:      HOST array of `count` configs with equal head_dim, bits,
+ *              variant, num_kv_heads and centroid values (each its own
+ *              rotation); IQ_ERR_INVALID_ARG otherwise.
+ *   xs:        HOST array of `count` DEVICE pointers, each
+ *              [batch][n_new][H_kv][d] of x_dtype, 16-B aligned.
+ *   outs:      HOST array of `count` caches (capacities may differ).
+ *   start_pos: DEVICE int32 [batch], the rows of every tensor.
+ * Other arguments and errors as iq_quantize_append; the results are those of
+ * `count` iq_quantize_append calls. */
+int iq_quantize_append_many(const iq_config *cfgs, int32_t count, const void *const *xs,
+                            int32_t x_dtype, int32_t batch, int32_t n_new,
+                            const int32_t *start_pos, const iq_cache *outs,
+                            hipStream_t stream);
+
 /* Quantize and append keys with a RoPE sub-block (RotaryQuant §5, the
  * MLA/RoPE limitation: positional coordinates must be neither rotated nor
  * quantised).  Each key is (content, positional) with the rope_dim RoPE

@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) >= {"iq_quantize_append", "iq_dequantize", "iq_decode_attention",
                           "iq_decode_workspace_bytes", "iq_status_string", "iq_codebook",
                           "iq_decode_attention_partial", "iq_decode_attention_merge",
-                          "iq_quantize_append_rope", "iq_decode_attention_rope"}
+                          "iq_quantize_append_rope", "iq_decode_attention_rope", "iq_quantize_append_many"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -272,3 +272,28 @@ def test_rope_validation():
     big = cfg(d=256)
     assert decode(64, conf=big, ws_bytes=L.iq_decode_workspace_bytes(ctypes.byref(big.c()), 1, 32, 16)) == -2
     assert decode(64, ws_bytes=need - 1) == -4
+
+
+def test_append_many_validation():
+    """Several tensors per call: the configs must agree in shape and codebook."""
+    L = B.lib()
+    n = 3
+    base = [cfg() for _ in range(n)]
+
+    def call(cfgs, count=n, xs=(0x2000, 0x2100, 0x2200), cap=8):
+        cc = (B.IQConfigC * len(cfgs))(*[c.c() for c in cfgs])
+        xp = (ctypes.c_void_p * len(xs))(*xs)
+        outs = (B.IQCacheC * len(cfgs))(*[B.IQCacheC(0x4000, 0x5000, cap) for _ in cfgs])
+        return L.iq_quantize_append_many(cc, count, xp, 1, 1, 4, 0x3000, outs, None)
+
+    assert call(base, count=0) == -1
+    assert call(base[:2] + [cfg(bits=2)]) == -1                 # another bit width
+    assert call(base[:2] + [cfg(hkv=2)]) == -1                  # another head count
+    other = cfg()
+    other.centroids = other.centroids.copy()
+    other.centroids[0] *= 2.0                                  # still a valid codebook
+    assert call(base[:2] + [other]) == -1                       # another codebook
+    assert call(base, xs=(0x2000, 0x2108, 0x2200)) == -3        # misaligned input
+    assert call(base, xs=(0x2000, 0, 0x2200)) == -1
+    assert call(base, cap=2) == -1                              # n_new above a capacity
+    assert call(base[:2] + [cfg(d=96)]) == -2

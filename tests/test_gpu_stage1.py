@@ -231,3 +231,35 @@ def test_c2_full_size_sampled(idx, setting):
     assert err <= TOL[dt]
     # fp16 inputs are unit vectors only to fp16 precision: allow 0.5% slack
     assert abs(mse_all - expect) < (0.002 if dt == np.float32 else 0.005) * expect + 2e-5
+
+
+def test_append_many_equals_single_appends():
+    """20 tensors (two launches of up to 16) with their own rotations appended
+    in one call: every cache equals what a separate iq_quantize_append call
+    writes; one tensor is also checked against the oracle."""
+    t = torch()
+    d, bits, hkv, batch, n, cap, count = 128, 3, 4, 2, 300, 320, 20
+    rng = np.random.default_rng(70)
+    cfgs, quats = [], []
+    for i in range(count):
+        q = inputs.quaternions(hkv, d, seed=100 + i)
+        quats.append(q)
+        cfgs.append(B.Config(d, bits, O.FULL, hkv, t.from_numpy(q).to(DEV), B.iq_codebook(bits, d)))
+    xs = [t.from_numpy((rng.standard_normal((batch, n, hkv, d)) * 3).astype(np.float16)).to(DEV)
+          for _ in range(count)]
+    sp = t.from_numpy(np.array([7, 0], np.int32)).to(DEV)
+    many = [B.new_cache(batch, hkv, cap, d, bits, DEV) for _ in range(count)]
+    B.iq_quantize_append_many(cfgs, xs, sp, many)
+    for i in range(count):
+        one = B.new_cache(batch, hkv, cap, d, bits, DEV)
+        B.iq_quantize_append(cfgs[i], xs[i], sp, one)
+        t.cuda.synchronize()
+        assert t.equal(one.codes, many[i].codes) and t.equal(one.norms, many[i].norms), i
+    codes, norms = host_cache(many[13])
+    x = xs[13].cpu().numpy()
+    for b, s0 in ((0, 7), (1, 0)):
+        for h in range(hkv):
+            ref = O.quantize(x[b, :, h], quats[13][h], O.codebook(bits, d), O.FULL)
+            reconcile_codes(codes[b, h, s0:s0 + n], ref["codes"], ref["flags"], bits, d)
+            reconcile_norms(norms[b, h, s0:s0 + n], ref["norm16"], ref["norm_flags"])
+    say(f"append many: {count} tensors equal to single appends; tensor 13 as the oracle's")
