@@ -262,10 +262,12 @@ def run_headline(torch, dev, args):
     rb = row_bytes(d, bits)
     events = []
 
+    # the step's K and V appends in one launch (same rotation, two caches)
+    append_kv = [B.prepare_append_many([cfg, cfg], [knew[s], vnew[s]], [kc, vc]) for s in range(P)]
+
     def step(g, record):
         s = g % P
-        B.iq_quantize_append(cfg, knew[s], pos_dev[g], kc)
-        B.iq_quantize_append(cfg, vnew[s], pos_dev[g], vc)
+        append_kv[s](pos_dev[g])
         if record:
             e0, e1 = _events(torch)
             e0.record(stream)

@@ -758,13 +758,20 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
   const int i = threadIdx.x;
   const int n = a.n_part;
   const float *recs = a.ws + ((size_t)b * a.hq + h) * n * RS;
-  __shared__ float red[D];
-  __shared__ int redi[D];
+  constexpr int NW = D / 64;                 // waves of the workgroup
+  __shared__ float redf[NW];
+  __shared__ int redi[NW];
   __shared__ float wbuf[kMergeChunk];
+  const int lane = i & 63, wave = i >> 6;
+  // (score, position) pairs: the larger score, ties to the lower valid position
+  auto better = [](float s1, int p1, float s0, int p0) {
+    return s1 > s0 || (s1 == s0 && p1 >= 0 && (p0 < 0 || p1 < p0));
+  };
 
   // Headers are read in parallel (thread t: records t, t + D, ...): the
   // running maximum and the best score with its position (ties: the lower
-  // position; splits cover increasing positions).
+  // position; splits cover increasing positions).  Reductions: across the
+  // wave by lane exchanges, then across the waves through LDS.
   float Mt = -INFINITY, bt = -INFINITY;
   int at = -1;
   for (int p = i; p < n; p += D) {
@@ -773,36 +780,37 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
       Mt = fmaxf(Mt, rec[0]);
       const float sc = rec[2];
       const int pos = __builtin_bit_cast(int, rec[3]);
-      if (sc > bt || (sc == bt && pos < at)) {
+      if (better(sc, pos, bt, at)) {
         bt = sc;
         at = pos;
       }
     }
   }
-  red[i] = Mt;
-  __syncthreads();
-  for (int st = D / 2; st > 0; st >>= 1) {
-    if (i < st) red[i] = fmaxf(red[i], red[i + st]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  red[i] = bt;
-  redi[i] = at;
-  __syncthreads();
-  for (int st = D / 2; st > 0; st >>= 1) {
-    if (i < st) {
-      const float os = red[i + st];
-      const int oj = redi[i + st];
-      if (os > red[i] || (os == red[i] && oj >= 0 && (redi[i] < 0 || oj < redi[i]))) {
-        red[i] = os;
-        redi[i] = oj;
-      }
+  for (int m = 32; m > 0; m >>= 1) {
+    Mt = fmaxf(Mt, __shfl_xor(Mt, m, 64));
+    const float os = __shfl_xor(bt, m, 64);
+    const int oj = __shfl_xor(at, m, 64);
+    if (better(os, oj, bt, at)) {
+      bt = os;
+      at = oj;
     }
-    __syncthreads();
   }
-  const float bsc = red[0];
-  const int arg = redi[0];
+  if (lane == 0) {
+    redf[wave] = Mt;
+    redi[wave] = at;
+    wbuf[wave] = bt;                         // wbuf is free until the weights below
+  }
+  __syncthreads();
+  float M = redf[0], bsc = wbuf[0];
+  int arg = redi[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    M = fmaxf(M, redf[w]);
+    if (better(wbuf[w], redi[w], bsc, arg)) {
+      bsc = wbuf[w];
+      arg = redi[w];
+    }
+  }
   __syncthreads();
 
   // Weights 2^(M_p - M) (0 for empty splits) staged in LDS chunk by chunk;
@@ -828,13 +836,12 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
     }
     __syncthreads();
   }
-  red[i] = Lt;
+  for (int m = 32; m > 0; m >>= 1) Lt += __shfl_xor(Lt, m, 64);
+  if (lane == 0) redf[wave] = Lt;
   __syncthreads();
-  for (int st = D / 2; st > 0; st >>= 1) {
-    if (i < st) red[i] += red[i + st];
-    __syncthreads();
-  }
-  const float L = red[0];
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L += redf[w];
 
   __shared__ float y[D];
   y[i] = L > 0.f ? o * a.oscale / L : 0.f;
