@@ -105,9 +105,10 @@ def run_rope_decode(cfg, q, kc, rope, vc, lens, max_len):
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy(), arg.cpu().numpy()
 
 
-@pytest.mark.parametrize("bits,hq,hkv,variant", [(3, 8, 8, O.FULL), (2, 16, 4, O.FAST), (4, 8, 2, O.PLANAR),
-                                                  (3, 32, 4, O.FAST)])
-def test_rope_decode_ragged(bits, hq, hkv, variant):
+@pytest.mark.parametrize("bits,hq,hkv,variant,qdt", [(3, 8, 8, O.FULL, np.float16), (2, 16, 4, O.FAST, np.float16),
+                                                      (4, 8, 2, O.PLANAR, np.float16), (3, 32, 4, O.FAST, np.float16),
+                                                      (3, 16, 8, O.FULL, np.float32)])
+def test_rope_decode_ragged(bits, hq, hkv, variant, qdt):
     """Three sequences (one empty, one a single token, one of 651 tokens)."""
     d, cap, lens = 128, 700, [0, 1, 651]
     batch = len(lens)
@@ -115,7 +116,7 @@ def test_rope_decode_ragged(bits, hq, hkv, variant):
     cfg, quats = make_config(d, bits, variant, hkv)
     k = (rng.standard_normal((batch, cap, hkv, d + R)) * 2).astype(np.float16)
     v = (rng.standard_normal((batch, cap, hkv, d)) * 2).astype(np.float16)
-    q = rng.standard_normal((batch, hq, d + R)).astype(np.float16)
+    q = rng.standard_normal((batch, hq, d + R)).astype(qdt)
     kc, rope = append_keys(cfg, k, cap, [0] * batch)
     vc = B.new_cache(batch, hkv, cap, d, bits, DEV)
     t = torch()
