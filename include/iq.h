@@ -125,7 +125,8 @@ int iq_codebook(int32_t bits, int32_t head_dim, float *centroids_out);
  *   out:       the packed tensor written (codes and norms).
  * batch * n_new must stay below 2^31 - 2^20 (IQ_ERR_INVALID_ARG otherwise;
  * an input that large would not fit in device memory anyway).
- * K and V are two calls on two caches that share one iq_config. */
+ * K and V are two calls on two caches that share one iq_config (or one
+ * iq_quantize_append_many call). */
 int iq_quantize_append(const iq_config *cfg, const void *x, int32_t x_dtype,
                        int32_t batch, int32_t n_new, const int32_t *start_pos,
                        const iq_cache *out, hipStream_t stream);
