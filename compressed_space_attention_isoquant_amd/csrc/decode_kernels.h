@@ -523,8 +523,11 @@ void partial_kernel(DecodeArgs a) {
             ca = __builtin_amdgcn_alignbit(vch[2 * p][wd + 1], vch[2 * p][wd], off);
             cb = __builtin_amdgcn_alignbit(vch[2 * p + 1][wd + 1], vch[2 * p + 1][wd], off);
           }
-          X[gi][p][0] = (ca & ME) | ((cb & ME) << BITS);
-          X[gi][p][1] = ((ca >> BITS) & ME) | (cb & (ME << BITS));
+          // bit-field inserts (one v_bfi_b32 each): the fields of ca under
+          // ME, those of cb shifted into the gaps; only the group's 8 * BITS
+          // low bits are read afterwards
+          X[gi][p][0] = (ca & ME) | ((cb << BITS) & ~ME);
+          X[gi][p][1] = ((ca >> BITS) & ME) | (cb & ~ME);
         }
       });
       static_for<NB>([&](auto nb) {
