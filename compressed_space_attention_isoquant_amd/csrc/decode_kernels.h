@@ -494,9 +494,13 @@ void partial_kernel(DecodeArgs a) {
           constexpr int wd = pos >> 5, off = pos & 31;
           if constexpr (off + W <= 32 || wd + 1 >= CW)
             ka[tile][s][p] = pair(kw[tile][wd], std::integral_constant<int, off>{});
-          else
-            ka[tile][s][p] = pair(__builtin_amdgcn_alignbit(kw[tile][wd + 1], kw[tile][wd], off),
-                                  std::integral_constant<int, 0>{});
+          else {
+            // a pair across two dwords: the funnel shift also moves the field
+            // to bit LSH, where the table offset wants it
+            static_assert(off >= LSH, "straddling field below the table shift");
+            ka[tile][s][p] = pair(__builtin_amdgcn_alignbit(kw[tile][wd + 1], kw[tile][wd], off - LSH),
+                                  std::integral_constant<int, LSH>{});
+          }
         });
       });
     }
