@@ -626,12 +626,12 @@ def summarize_counters(fetch_csv, write_csv):
     f_write = true_kib / max(write[copy_name])
     out = {"commands": [
                "export TMPDIR=/tmp",
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o f -- python3 bench.py "
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof_out/pmc_fetch -o f -- python3 bench.py "
                "--steps 3 --warmup 1 --no-cpu-baseline --decode-only --calibrate-copy",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o w -- python3 bench.py "
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof_out/pmc_write -o w -- python3 bench.py "
                "--steps 3 --warmup 1 --no-cpu-baseline --decode-only --calibrate-copy",
-               "python3 bench.py --summarize-counters gpurun_out/pmc_fetch/f_counter_collection.csv "
-               "gpurun_out/pmc_write/w_counter_collection.csv"],
+               "python3 bench.py --summarize-counters prof_out/pmc_fetch/f_counter_collection.csv "
+               "prof_out/pmc_write/w_counter_collection.csv"],
            "kernel_source_hash": kernel_source_hash(),
            "copy_calibration": {"kernel": copy_name[:120], "bytes": COPY_BYTES,
                                 "fetch_kib": max(fetch[copy_name]), "write_kib": max(write[copy_name]),
@@ -691,9 +691,9 @@ def summarize_stage1(counter_csv):
     vname = {0: "Full", 1: "Fast", 2: "Planar"}
     lines = ["# Stage-1 kernels: VALU and HBM fractions", "",
              "Commands (from the repository root, on one MI355X):", "", "```", "export TMPDIR=/tmp",
-             "rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_s1 "
+             "rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES GRBM_GUI_ACTIVE --output-format csv -d prof_out/pmc_s1 "
              "-o s -- python3 bench.py --stage1-only",
-             "python3 bench.py --summarize-stage1 gpurun_out/pmc_s1/s_counter_collection.csv", "```", "",
+             "python3 bench.py --summarize-stage1 prof_out/pmc_s1/s_counter_collection.csv", "```", "",
              f"2^20 vectors per dispatch; medians over the dispatches of each kernel.  VALU: wave64 VALU "
              f"instructions per vector x 64 lanes (lane-ops per vector), and the issue ratio = "
              f"SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x the dispatch's cycles, GRBM_GUI_ACTIVE / 8 being "
