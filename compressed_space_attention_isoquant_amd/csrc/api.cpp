@@ -395,7 +395,10 @@ static int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dt
   if (!aligned16(q)) return IQ_ERR_MISALIGNED;
   if (rope_dim > 0) {
     if (!k_rope) return IQ_ERR_INVALID_ARG;
-    if (rope_dim != kDecodeRopeDim || cfg->head_dim != 128) return IQ_ERR_UNSUPPORTED;
+    if (rope_dim != kDecodeRopeDim) return IQ_ERR_UNSUPPORTED;
+    // at head_dim 512 and 4 bits two stages of rows, norms and RoPE rows per
+    // wave no longer fit next to the pair table in LDS
+    if (cfg->head_dim == 512 && cfg->bits == 4) return IQ_ERR_UNSUPPORTED;
     if (!aligned16(k_rope)) return IQ_ERR_MISALIGNED;
     if (k->capacity * rope_dim * 2 >= (int64_t(1) << 30)) return IQ_ERR_UNSUPPORTED;
   }

@@ -5,6 +5,7 @@
 namespace iq {
 
 hipError_t launch_decode_256(int bits, const DecodeArgs &a, hipStream_t s) {
+  if (a.rope == kDecodeRope) return partial_dispatch_bits<256, kDecodeRope>(bits, a, s);
   return partial_dispatch_bits<256>(bits, a, s);
 }
 

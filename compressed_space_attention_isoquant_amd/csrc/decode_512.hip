@@ -5,6 +5,7 @@
 namespace iq {
 
 hipError_t launch_decode_512(int bits, const DecodeArgs &a, hipStream_t s) {
+  if (a.rope == kDecodeRope) return partial_dispatch_bits<512, kDecodeRope>(bits, a, s);
   return partial_dispatch_bits<512>(bits, a, s);
 }
 

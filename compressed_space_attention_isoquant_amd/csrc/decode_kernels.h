@@ -221,8 +221,8 @@ constexpr int ilog2() {
 // LDS layout: workgroups per CU (each holds one wave per SIMD) and stages
 // per wave.  Three workgroups per CU where each can still keep 3 stages per
 // wave next to its pair table and `extra` bytes (more waves hide latency
-// better than a deeper ring), else two; then as many stages as fit, up to 4,
-// at least 2 (double buffering).
+// better than a deeper ring), else two where each keeps 2 stages, else one;
+// then as many stages as fit, up to 4, at least 2 (double buffering).
 template <int D, int BITS, int ROPE = 0>
 constexpr int stages_fitting(int budget, int extra) {
   const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
@@ -231,7 +231,9 @@ constexpr int stages_fitting(int budget, int extra) {
 
 template <int D, int BITS, int ROPE = 0>
 constexpr int resident_groups(int extra) {
-  return stages_fitting<D, BITS, ROPE>(160 * 1024 / 3, extra) >= 3 ? 3 : 2;
+  return stages_fitting<D, BITS, ROPE>(160 * 1024 / 3, extra) >= 3   ? 3
+         : stages_fitting<D, BITS, ROPE>(160 * 1024 / 2, extra) >= 2 ? 2
+                                                                     : 1;
 }
 
 template <int D, int BITS, int ROPE = 0>
@@ -909,6 +911,14 @@ hipError_t partial_dispatch_argmax(const DecodeArgs &a, hipStream_t s) {
                   : partial_dispatch_group<D, BITS, false, ROPE>(a, s);
 }
 
+// Whether the pair table and a ring of two stages per wave fit in one
+// compute unit's LDS (every shape without RoPE coordinates does; with them
+// head_dim 512 at 4 bits does not).
+template <int D, int BITS, int ROPE>
+constexpr bool partial_fits() {
+  return (1 << (2 * BITS)) * lut_repl<BITS>() * 4 + kDecodeWaves * 2 * Stage<D, BITS, ROPE>::BYTES <= 160 * 1024;
+}
+
 // ROPE: the RoPE coordinates per key these instantiations take (0: none).
 template <int D, int ROPE = 0>
 hipError_t partial_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
@@ -916,7 +926,9 @@ hipError_t partial_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
   switch (bits) {
     case 2: return partial_dispatch_argmax<D, 2, ROPE>(a, s);
     case 3: return partial_dispatch_argmax<D, 3, ROPE>(a, s);
-    case 4: return partial_dispatch_argmax<D, 4, ROPE>(a, s);
+    case 4:
+      if constexpr (partial_fits<D, 4, ROPE>()) return partial_dispatch_argmax<D, 4, ROPE>(a, s);
+      break;
   }
   return hipErrorInvalidValue;
 }

@@ -226,7 +226,8 @@ int iq_decode_attention(const iq_config *cfg, const void *q, int32_t q_dtype,
  *   q:        [batch][Hq][d + rope_dim] of q_dtype, RoPE coordinates last.
  *   k_rope:   DEVICE [batch][H_kv][k->capacity][rope_dim] fp16 bits, 16-B
  *             aligned; k->capacity * rope_dim * 2 below 2^30 bytes.
- *   rope_dim: 64, with head_dim 128 (IQ_ERR_UNSUPPORTED otherwise).
+ *   rope_dim: 64 (IQ_ERR_UNSUPPORTED otherwise), with any head_dim and bit
+ *             width except head_dim 512 at 4 bits (IQ_ERR_UNSUPPORTED).
  *   out:      [batch][Hq][d] (the content coordinates).
  * Other arguments, workspace and errors as iq_decode_attention. */
 int iq_decode_attention_rope(const iq_config *cfg, const void *q, int32_t q_dtype,

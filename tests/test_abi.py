@@ -269,7 +269,8 @@ def test_rope_validation():
     assert decode(32) == -2                     # the kernels take 64
     assert decode(64, k_rope=None) == -1
     assert decode(64, k_rope=0x9004) == -3
-    big = cfg(d=256)
+    # head_dim 512 at 4 bits: two stages with RoPE rows do not fit in LDS
+    big = cfg(d=512, bits=4)
     assert decode(64, conf=big, ws_bytes=L.iq_decode_workspace_bytes(ctypes.byref(big.c()), 1, 32, 16)) == -2
     assert decode(64, ws_bytes=need - 1) == -4
 

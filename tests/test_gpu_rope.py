@@ -105,14 +105,16 @@ def run_rope_decode(cfg, q, kc, rope, vc, lens, max_len):
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy(), arg.cpu().numpy()
 
 
-@pytest.mark.parametrize("bits,hq,hkv,variant,qdt", [(3, 8, 8, O.FULL, np.float16), (2, 16, 4, O.FAST, np.float16),
-                                                      (4, 8, 2, O.PLANAR, np.float16), (3, 32, 4, O.FAST, np.float16),
-                                                      (3, 16, 8, O.FULL, np.float32)])
-def test_rope_decode_ragged(bits, hq, hkv, variant, qdt):
+@pytest.mark.parametrize("d,bits,hq,hkv,variant,qdt", [
+    (128, 3, 8, 8, O.FULL, np.float16), (128, 2, 16, 4, O.FAST, np.float16), (128, 4, 8, 2, O.PLANAR, np.float16),
+    (128, 3, 32, 4, O.FAST, np.float16), (128, 3, 16, 8, O.FULL, np.float32),
+    (256, 3, 16, 8, O.FAST, np.float16), (256, 4, 8, 1, O.FULL, np.float32), (256, 2, 4, 4, O.PLANAR, np.float16),
+    (512, 3, 8, 2, O.FULL, np.float16), (512, 2, 16, 2, O.FAST, np.float32)])
+def test_rope_decode_ragged(d, bits, hq, hkv, variant, qdt):
     """Three sequences (one empty, one a single token, one of 651 tokens)."""
-    d, cap, lens = 128, 700, [0, 1, 651]
+    cap, lens = 700, [0, 1, 651]
     batch = len(lens)
-    rng = np.random.default_rng(61 + bits + hq)
+    rng = np.random.default_rng(61 + bits + hq + d - 128)
     cfg, quats = make_config(d, bits, variant, hkv)
     k = (rng.standard_normal((batch, cap, hkv, d + R)) * 2).astype(np.float16)
     v = (rng.standard_normal((batch, cap, hkv, d)) * 2).astype(np.float16)
@@ -123,7 +125,7 @@ def test_rope_decode_ragged(bits, hq, hkv, variant, qdt):
     B.iq_quantize_append(cfg, t.from_numpy(v).to(DEV), t.zeros((batch,), dtype=t.int32, device=DEV), vc)
     got, lse, arg = run_rope_decode(cfg, q, kc, rope, vc, lens, max(lens))
     ref, rlse, rarg = oracle_rope_decode(q, k, v, quats, cfg, lens, kc, rope, vc)
-    check_outputs(f"rope decode b={bits} G={hq // hkv} v={variant}", got, lse, arg, ref, rlse, rarg, 2e-3,
+    check_outputs(f"rope decode d={d} b={bits} G={hq // hkv} v={variant}", got, lse, arg, ref, rlse, rarg, 2e-3,
                   check_arg=True)
     assert np.all(got[0] == 0) and np.all(arg[0] == -1)
 
