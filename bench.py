@@ -150,6 +150,7 @@ def main():
         if not args.decode_only:
             extras["rope_32k"] = run_rope_32k(torch, dev)
             extras["c3_latency"] = run_c3_latency(torch, dev)
+            extras["c4_latency"] = run_c3_latency(torch, dev, T=32768, with_argmax=True)
             extras["prefill_compress"] = run_prefill_compress(torch, dev)
         if not args.no_stage1 and not args.decode_only:
             extras["stage1"] = run_stage1(torch, dev)
@@ -448,16 +449,17 @@ def run_rope_32k(torch, dev, reps=20):
             "bytes_per_call": int(kv + qo)}
 
 
-def run_c3_latency(torch, dev, reps=20):
-    """Supplementary: one sequence of 8,192 tokens, 32 query / 4 KV heads,
-    d=128, 3-bit Full (3.3 MB of packed K/V: it fits the 256 MB last-level
-    cache).  Latency of one decode call (order, partial, merge), warm (back
-    to back) and cold (512 MiB written between calls, events around the
-    call only)."""
+def run_c3_latency(torch, dev, reps=20, T=8192, with_argmax=False):
+    """Supplementary: one sequence of T tokens (8,192; 32,768 for the
+    needle-search shape, which also writes the per-head argmax), 32 query /
+    4 KV heads, d=128, 3-bit Full (3.3 / 13.1 MB of packed K/V: both fit the
+    256 MB last-level cache).  Latency of one decode call (order, partial,
+    merge), warm (back to back) and cold (512 MiB written between calls,
+    events around the call only)."""
     from compressed_space_attention_isoquant_amd import binding as B
     from compressed_space_attention_isoquant_amd import inputs
 
-    T, hq, hkv, d, bits = 8192, 32, 4, 128, 3
+    hq, hkv, d, bits = 32, 4, 128, 3
     quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
     cfg = B.Config(d, bits, B.IQ_FULL, hkv, quats, B.iq_codebook(bits, d))
     rng = np.random.default_rng(3)
@@ -470,6 +472,8 @@ def run_c3_latency(torch, dev, reps=20):
     q = inputs.device_normal(72, 0, (1, hq, d), dev, torch.float16)
     kv_len = torch.full((1,), T, dtype=torch.int32, device=dev)
     out = torch.empty((1, hq, d), dtype=torch.float32, device=dev)
+    arg = torch.empty((1, hq), dtype=torch.int32, device=dev) if with_argmax else None
+    lse = torch.empty((1, hq), dtype=torch.float32, device=dev) if with_argmax else None
     ws = torch.empty((B.iq_decode_workspace_bytes(cfg, 1, hq, T),), dtype=torch.uint8, device=dev)
     flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -481,7 +485,7 @@ def run_c3_latency(torch, dev, reps=20):
                 flush.fill_(1)
             e0, e1 = _events(torch)
             e0.record(stream)
-            B.iq_decode_attention(cfg, q, kc, vc, kv_len, T, 1.0 / math.sqrt(d), out, None, None, ws)
+            B.iq_decode_attention(cfg, q, kc, vc, kv_len, T, 1.0 / math.sqrt(d), out, lse, arg, ws)
             e1.record(stream)
             ts.append((e0, e1))
         torch.cuda.synchronize()
@@ -490,9 +494,10 @@ def run_c3_latency(torch, dev, reps=20):
     timed(False)
     warm, cold = timed(False), timed(True)
     del flush
-    print(f"[bench] C3 decode latency warm {warm:.1f} us, cold {cold:.1f} us", file=sys.stderr, flush=True)
-    return {"workload": "one sequence of 8192 tokens, 32 query / 4 KV heads, d=128, 3-bit Full, fp16 q, "
-                        "fp32 out; median of 20 calls",
+    print(f"[bench] {T // 1024}K single-sequence decode latency warm {warm:.1f} us, cold {cold:.1f} us",
+          file=sys.stderr, flush=True)
+    return {"workload": f"one sequence of {T} tokens, 32 query / 4 KV heads, d=128, 3-bit Full, fp16 q, "
+                        f"fp32 out{', lse and argmax' if with_argmax else ''}; median of {reps} calls",
             "warm_us": round(warm, 1), "cold_us": round(cold, 1),
             "packed_kv_bytes": int(T * hkv * 2 * (row_bytes(d, bits) + 2))}
 

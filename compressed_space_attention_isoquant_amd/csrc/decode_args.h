@@ -83,9 +83,11 @@ inline size_t decode_workspace_total(int32_t batch, int32_t hq, int n_split, int
 // Split-K geometry of the decode kernels.  About 2048 workgroups (8 per
 // compute unit, two resident at a time): with ragged context lengths the
 // extra, shorter workgroups even out the compute units' loads.  Chunks are
-// kept at 8192 tokens or more while that still gives 1024 workgroups, since
-// each workgroup costs a fixed prologue and epilogue.  Chunks are whole
-// numbers of (waves x tile) token blocks.
+// kept at 8192 tokens or more while that still gives 512 workgroups (about
+// one resident round), since each workgroup costs a fixed prologue and
+// epilogue: a few long sequences then run in one round of workgroups instead
+// of several rounds of one-tile ones.  Chunks are whole numbers of
+// (waves x tile) token blocks.
 struct Geometry {
   int chunk;
   int n_split;
@@ -101,7 +103,7 @@ inline Geometry decode_geometry(int32_t batch, int32_t hkv, int64_t max_kv_len) 
     return (T + want - 1) / want;
   };
   int64_t chunk = chunk_for(2048);
-  const int64_t floor_chunk = std::min<int64_t>(8192, chunk_for(1024));
+  const int64_t floor_chunk = std::min<int64_t>(8192, chunk_for(512));
   if (chunk < floor_chunk) chunk = floor_chunk;
   chunk = (chunk + unit - 1) / unit * unit;
   Geometry g;

@@ -207,7 +207,7 @@ def test_partial_and_merge_validation():
 
 def expected_workspace(batch, hq, hkv, d, max_len):
     """Workspace bytes from the documented split rule: about 2048 workgroups,
-    chunks of at least 8192 tokens while that still gives 1024 workgroups,
+    chunks of at least 8192 tokens while that still gives 512 workgroups,
     whole 128-token blocks; records of d + 4 floats per (sequence, query
     head, split), then (256-byte aligned) 8 bytes per (sequence, split) of
     work order when there are at most 4096 such pairs."""
@@ -218,7 +218,7 @@ def expected_workspace(batch, hq, hkv, d, max_len):
         want = max(1, -(-groups // pairs))
         return -(-T // want)
 
-    chunk = max(chunk_for(2048), min(8192, chunk_for(1024)))
+    chunk = max(chunk_for(2048), min(8192, chunk_for(512)))
     chunk = -(-chunk // 128) * 128
     n_split = -(-T // chunk)
     rec = batch * hq * n_split * (d + 4) * 4

@@ -305,8 +305,8 @@ def test_sorted_work_order_batch():
     lens = inputs.batch_lengths(25, batch, 1, cap)
     T = int(lens.max())
     # the split rule (about 2048 workgroups, chunks of at least 8192 tokens
-    # while that still gives 1024, whole 128-token blocks)
-    chunk = max(-(-T // -(-2048 // batch)), min(8192, -(-T // -(-1024 // batch))))
+    # while that still gives 512, whole 128-token blocks)
+    chunk = max(-(-T // -(-2048 // batch)), min(8192, -(-T // -(-512 // batch))))
     n_split = -(-T // (-(-chunk // 128) * 128))
     assert 1024 < batch * n_split <= 4096, batch * n_split
     rng = np.random.default_rng(25)
