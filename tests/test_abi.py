@@ -229,6 +229,7 @@ def expected_workspace(batch, hq, hkv, d, max_len):
 
 @pytest.mark.parametrize("batch,hq,hkv,d,max_len", [
     (64, 16, 8, 256, 32768), (64, 32, 4, 128, 32768), (1, 32, 4, 128, 8192), (1, 8, 8, 128, 131072),
+    (1, 32, 4, 128, 32768), (16, 32, 4, 128, 32768),
     (4200, 2, 1, 128, 40), (3, 8, 2, 512, 1), (256, 8, 8, 256, 32768), (2, 4, 4, 128, 0)])
 def test_decode_workspace_geometry(batch, hq, hkv, d, max_len):
     """The host's split geometry, observed through the workspace size."""
