@@ -1,21 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the IsoQuant packed-KV decode step on one MI355X.
 
-Headline workload (the batched decode-with-append configuration, synthetic):
-64 sequences whose context lengths are drawn uniformly from [1,024, 32,768]
-(seeded), 16 query heads / 8 KV heads (GQA 2:1), head_dim 256, 3-bit
-IsoQuant-Fast codes for K and V, fp16 I/O.  One step = quantize and append one
-new K and one new V vector per sequence and KV head at the end of its context,
-then decode attention for every query head over the packed caches (the
-sequences grow by one token per step).  100 steps are timed by default.
+Headline workload (the metric's configuration, synthetic): decode attention
+over packed 3-bit K/V at 32K context -- 64 sequences of 32,768 tokens, 32
+query heads / 4 KV heads (GQA 8:1), head_dim 128, 3-bit IsoQuant-Full codes,
+fp16 I/O.  One step = quantize and append one new K and one new V vector per
+sequence and KV head (into the last row), then decode attention for every
+query head over the packed caches.  100 steps are timed by default.
 
 Prints one JSON line: value = packed-KV (+ q, o) bytes the steps' attention
 reads and writes per second of step time (GB/s); the dominant kernel's
 roofline (its algorithmic bytes per launch over its average launch time,
-measured with HIP events on its stream); stage-1 quantize / dequantize rates
-over the whole d x bits x variant x dtype sweep on 2^20 unit vectors; a
-supplementary uniform 32K-context run (64 sequences, 32/4 heads, d=128,
-3-bit Full); and the FP64 oracle timed on the host as a baseline.
+measured with HIP events on its stream); the FP64 oracle timed on the host as
+a baseline; and, as labelled extras, the batched decode-with-append workload
+(64 ragged sequences up to 32K, 16/8 heads, d=256, 3-bit Fast) with its own
+roofline and oracle baseline, stage-1 quantize / dequantize rates over the
+whole d x bits x variant x dtype sweep on 2^20 unit vectors (with the
+oracle's stage-1 rate), single-call latencies (4,096-vector stage-1
+round trip, one 8K and one 32K sequence), the RoPE sub-block case and the
+deferred-prefill compression.
 
   --calibrate-copy  also runs one plain device-to-device copy of 256 MiB first
                     (the reference kernel for scaling the HBM byte counters).
@@ -47,10 +50,21 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 256 << 20
 
-HEADLINE = dict(batch=64, len_lo=1024, len_hi=32768, num_q_heads=16, num_kv_heads=8, head_dim=256, bits=3,
-                variant="fast", length_seed=45)
-UNIFORM_32K = dict(batch=64, kv_len=32768, num_q_heads=32, num_kv_heads=4, head_dim=128, bits=3,
-                   variant="full")
+# The metric's configuration: packed 3-bit K/V at 32K context with the
+# long-context head layout (32 query / 4 KV heads, d=128, Full), batched over
+# 64 sequences so that one decode step streams 839 MB of packed K/V.
+HEADLINE = dict(name="headline", batch=64, kv_len=32768, num_q_heads=32, num_kv_heads=4, head_dim=128, bits=3,
+                variant="full", seed=40,
+                label="decode with append at 32K context: 64 sequences x 32,768 tokens, 32 query / 4 KV heads, "
+                      "head_dim 128, 3-bit IsoQuant-Full K and V, fp16 I/O; each step quantizes and appends one "
+                      "K/V token per sequence (into the last row), then attends over all 32,768")
+# The batched decode-with-append configuration: ragged contexts up to 32K.
+BATCHED_APPEND = dict(name="batched_append_c5", batch=64, len_lo=1024, len_hi=32768, num_q_heads=16,
+                      num_kv_heads=8, head_dim=256, bits=3, variant="fast", length_seed=45, seed=46,
+                      label="batched decode with append: 64 sequences, context lengths uniform in [1024, 32768] "
+                            "(+1 per step), 16 query heads / 8 KV heads, head_dim 256, 3-bit IsoQuant-Fast, fp16 "
+                            "I/O; each step quantize+append one K/V token per sequence, then attend")
+PARTIAL_KERNEL = "partial_kernel"
 
 # Sources of the decode kernel; HBM counter readings recorded for it are
 # reported only while these are unchanged.
@@ -99,7 +113,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-stage1", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
-                    help="headline and uniform 32K decode only (the profiled command)")
+                    help="the 32K headline and the batched-append workload only (the profiled command)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--stage1-only", action="store_true", help="the stage-1 sweep only (the profiled command)")
     ap.add_argument("--summarize-stage1", metavar="COUNTER_CSV",
@@ -139,16 +153,18 @@ def main():
     if args.stage1_only:
         print(json.dumps(run_stage1(torch, dev)))
         return 0
-    head = run_headline(torch, dev, args)
+    head = run_decode_workload(torch, dev, HEADLINE, args.steps, args.warmup)
     if args.headline_child:
         print(json.dumps({"value": head["value"], "ms_per_step": head["ms_per_step"],
                           "partial_ms": head["partial_ms"]}))
         return 0
     extras = {}
     if not args.no_extras:
-        extras["uniform_32k"] = run_uniform_32k(torch, dev, max(10, args.steps // 5), args.warmup)
+        c5 = run_decode_workload(torch, dev, BATCHED_APPEND, max(10, args.steps // 2), args.warmup)
+        extras["batched_append_c5"] = workload_record(BATCHED_APPEND, c5, "batched_append_c5")
         if not args.decode_only:
             extras["rope_32k"] = run_rope_32k(torch, dev)
+            extras["c1_latency"] = run_c1_latency(torch, dev)
             extras["c3_latency"] = run_c3_latency(torch, dev)
             extras["c4_latency"] = run_c3_latency(torch, dev, T=32768, with_argmax=True)
             extras["prefill_compress"] = run_prefill_compress(torch, dev)
@@ -156,49 +172,34 @@ def main():
             extras["stage1"] = run_stage1(torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(head["lengths"], args.cpu_seconds)
+        cpu = cpu_baseline(HEADLINE, head["lengths"], args.cpu_seconds)
+        if "batched_append_c5" in extras:
+            extras["batched_append_c5"]["cpu_baseline"] = cpu_baseline(BATCHED_APPEND, c5["lengths"],
+                                                                       args.cpu_seconds / 2)
+        if "stage1" in extras:
+            extras["stage1"]["cpu_baseline"] = cpu_baseline_stage1(args.cpu_seconds / 2)
 
-    w = HEADLINE
-    traffic = recorded_traffic("headline")
+    rec = workload_record(HEADLINE, head, "headline")
     result = {
         "metric": "packed-KV decode-attn GB/s (% HBM peak) at 32K ctx; quantize Mvec/s",
-        "value": round(head["value"], 2),
+        "value": rec["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["ms_per_step"], 5),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16/f32",
-        "data": "synthetic (seeded torch/NumPy draws: N(0,1) K/V with 4 x10 outlier channels per head, "
-                "N(0,1) queries, context lengths uniform in [1024, 32768])",
-        "config": {
-            "workload": "batched decode with append: 64 sequences, context lengths uniform in [1024, 32768] "
-                        "(+1 per step), 16 query heads / 8 KV heads, head_dim 256, 3-bit IsoQuant-Fast, fp16 I/O; "
-                        "each step quantize+append one K/V token per sequence, then attend",
-            "batch": w["batch"], "num_q_heads": w["num_q_heads"], "num_kv_heads": w["num_kv_heads"],
-            "head_dim": w["head_dim"], "bits": w["bits"], "variant": w["variant"],
-            "mean_kv_len": round(float(np.mean(head["lengths"])), 1),
-            "attention_bytes_per_step": int(head["attn_bytes_per_step"]),
-        },
-        "pct_hbm_peak": round(100.0 * head["value"] / HBM_PEAK_GBS, 2),
-        "steps_per_s": round(1e3 / head["ms_per_step"], 1),
-        "partial_kernel_ms": round(head["partial_ms"], 5),
-        "partial_kernel_ms_spread": {"std": round(head["partial_ms_std"], 5), "min": round(head["partial_ms_min"], 5),
-                                     "cv": round(head["partial_ms_std"] / head["partial_ms"], 4)},
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(head["achieved"], 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": f"partial_kernel<{w['head_dim']},{w['bits']},{w['num_q_heads'] // w['num_kv_heads']}> "
-                      "(split-K decode over packed K/V)",
-            "algorithmic_bytes_per_launch": int(head["partial_bytes_per_launch"]),
-        },
+        "dtype": "u3 codes, f16/f32 arithmetic",
+        "data": "synthetic (seeded torch draws on the GPU: N(0,1) K/V with 4 x10 outlier channels per KV head, "
+                "N(0,1) queries)",
+        "config": rec["config"],
+        "pct_hbm_peak": rec["pct_hbm_peak"],
+        "steps_per_s": rec["steps_per_s"],
+        "partial_kernel_ms": rec["partial_kernel_ms"],
+        "partial_kernel_ms_spread": rec["partial_kernel_ms_spread"],
+        "roofline": rec["roofline"],
         "cpu_baseline": cpu,
     }
     if fresh:
@@ -218,43 +219,93 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def run_headline(torch, dev, args):
+def workload_record(w, r, traffic_name):
+    """The JSON fields of one timed decode workload: its step rate, and the
+    roofline of its dominant (split) kernel."""
+    per = r["per_step_ms"]
+    return {
+        "value": round(r["value"], 2), "unit": "GB/s", "ms_per_step": round(r["ms_per_step"], 5),
+        "steps": len(per),
+        "config": {"workload": w["label"], "batch": w["batch"], "num_q_heads": w["num_q_heads"],
+                   "num_kv_heads": w["num_kv_heads"], "head_dim": w["head_dim"], "bits": w["bits"],
+                   "variant": w["variant"], "mean_kv_len": round(float(np.mean(r["lengths"])), 1),
+                   "attention_bytes_per_step": int(r["attn_bytes_per_step"])},
+        "pct_hbm_peak": round(100.0 * r["value"] / HBM_PEAK_GBS, 2),
+        "steps_per_s": round(1e3 / r["ms_per_step"], 1),
+        "partial_kernel_ms": round(r["partial_ms"], 5),
+        # per-step spread of the split kernel; the first steps' times next to
+        # the median show whether the slow steps are the early ones (clock and
+        # cache warm-up) or spread over the run
+        "partial_kernel_ms_spread": {"std": round(float(np.std(per)), 5), "min": round(float(np.min(per)), 5),
+                                     "median": round(float(np.median(per)), 5),
+                                     "max": round(float(np.max(per)), 5),
+                                     "cv": round(float(np.std(per) / np.mean(per)), 4),
+                                     "first_steps": [round(float(x), 5) for x in per[:5]]},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(r["achieved"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(traffic_name),
+            "kernel": f"{PARTIAL_KERNEL}<{w['head_dim']},{w['bits']},{w['num_q_heads'] // w['num_kv_heads']}> "
+                      "(split decode over packed K/V)",
+            "algorithmic_bytes_per_launch": int(r["partial_bytes_per_launch"]),
+        },
+    }
+
+
+def run_decode_workload(torch, dev, w, steps, warmup):
+    """One decode workload, timed.  Set-up (not timed): every cache row of K
+    and V holds a quantized synthetic token.  A step appends one new K and one
+    new V token per sequence and KV head (one batched launch) and runs decode
+    attention for every query head over the packed caches: the ragged
+    workload's sequences grow by one token per step; the uniform workload
+    appends into its last row, so each step attends over exactly kv_len
+    tokens.  HIP events on the stream the split kernel is launched on bracket
+    that (dominant) kernel in every timed step."""
     from compressed_space_attention_isoquant_amd import binding as B
     from compressed_space_attention_isoquant_amd import inputs
 
-    w = HEADLINE
     batch, hq, hkv, d, bits = (w[k] for k in ("batch", "num_q_heads", "num_kv_heads", "head_dim", "bits"))
-    lengths = inputs.batch_lengths(w["length_seed"], batch, w["len_lo"], w["len_hi"])
-    n_total = args.warmup + args.steps
-    cap = (int(lengths.max()) + n_total + 1) // 2 * 2       # decode needs an even capacity
+    variant = {"full": B.IQ_FULL, "fast": B.IQ_FAST}[w["variant"]]
+    n_total = warmup + steps
+    if w.get("kv_len"):
+        lens = np.full(batch, w["kv_len"], np.int64)
+        grow = 0
+        cap = int(w["kv_len"])
+    else:
+        lens = inputs.batch_lengths(w["length_seed"], batch, w["len_lo"], w["len_hi"]).astype(np.int64)
+        grow = 1
+        cap = (int(lens.max()) + n_total + 1) // 2 * 2       # decode needs an even capacity
+    seed = w["seed"]
     quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
-    cfg = B.Config(d, bits, B.IQ_FAST, hkv, quats, B.iq_codebook(bits, d))
-    rng = np.random.default_rng(46)
+    cfg = B.Config(d, bits, variant, hkv, quats, B.iq_codebook(bits, d))
+    rng = np.random.default_rng(seed)
     ch_k = inputs.outlier_channels(rng, hkv, d)
     ch_v = inputs.outlier_channels(rng, hkv, d)
 
-    # ---- set-up (not timed): fill every cache row with quantized tokens ----
     kc = B.new_cache(batch, hkv, cap, d, bits, dev)
     vc = B.new_cache(batch, hkv, cap, d, bits, dev)
     sb, st = 8, 4096
     for cache, idx, ch in ((kc, 0, ch_k), (vc, 1, ch_v)):
         for b0 in range(0, batch, sb):
-            sub = B.PackedCache(cache.codes[b0:b0 + sb], cache.norms[b0:b0 + sb])
+            nb = min(sb, batch - b0)
+            sub = B.PackedCache(cache.codes[b0:b0 + nb], cache.norms[b0:b0 + nb])
             for t0 in range(0, cap, st):
                 nt = min(st, cap - t0)
-                x = inputs.device_kv(47 + idx, (b0 // sb) * 1000 + t0 // st, sb * nt, ch, d, dev)
-                pos = torch.full((sb,), t0, dtype=torch.int32, device=dev)
-                B.iq_quantize_append(cfg, x.view(sb, nt, hkv, d), pos, sub)
+                x = inputs.device_kv(seed + 1 + idx, (b0 // sb) * 1000 + t0 // st, nb * nt, ch, d, dev)
+                pos = torch.full((nb,), t0, dtype=torch.int32, device=dev)
+                B.iq_quantize_append(cfg, x.view(nb, nt, hkv, d), pos, sub)
                 del x
     torch.cuda.synchronize()
     P = 8   # distinct new-token / query draws cycled over the steps
-    knew = [inputs.device_kv(48, s, batch, ch_k, d, dev).view(batch, 1, hkv, d) for s in range(P)]
-    vnew = [inputs.device_kv(49, s, batch, ch_v, d, dev).view(batch, 1, hkv, d) for s in range(P)]
-    qs = [inputs.device_normal(50, s, (batch, hq, d), dev, torch.float16) for s in range(P)]
-    lens = lengths.astype(np.int64)
-    pos_dev = [torch.from_numpy((lens - 1 + g).astype(np.int32)).to(dev) for g in range(n_total)]
-    len_dev = [torch.from_numpy((lens + g).astype(np.int32)).to(dev) for g in range(n_total)]
-    max_len = [int(lens.max()) + g for g in range(n_total)]
+    knew = [inputs.device_kv(seed + 3, s, batch, ch_k, d, dev).view(batch, 1, hkv, d) for s in range(P)]
+    vnew = [inputs.device_kv(seed + 4, s, batch, ch_v, d, dev).view(batch, 1, hkv, d) for s in range(P)]
+    qs = [inputs.device_normal(seed + 5, s, (batch, hq, d), dev, torch.float16) for s in range(P)]
+    pos_dev = [torch.from_numpy((lens - 1 + grow * g).astype(np.int32)).to(dev) for g in range(n_total)]
+    len_dev = [torch.from_numpy((lens + grow * g).astype(np.int32)).to(dev) for g in range(n_total)]
+    max_len = [int(lens.max()) + grow * g for g in range(n_total)]
     out = torch.empty((batch, hq, d), dtype=torch.float16, device=dev)
     lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
     ws = torch.empty((B.iq_decode_workspace_bytes(cfg, batch, hq, max(max_len)),), dtype=torch.uint8, device=dev)
@@ -273,36 +324,36 @@ def run_headline(torch, dev, args):
             e0, e1 = _events(torch)
             e0.record(stream)
         # the two phases of iq_decode_attention, so that the events bracket the
-        # partial (dominant) kernel alone
+        # split (dominant) phase alone
         B.iq_decode_attention_partial(cfg, qs[s], kc, vc, len_dev[g], max_len[g], scale, ws, track_argmax=False)
         if record:
             e1.record(stream)
             events.append((e0, e1))
         B.iq_decode_attention_merge(cfg, batch, hq, max_len[g], out, lse, None, ws)
 
-    for g in range(args.warmup):
+    for g in range(warmup):
         step(g, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for g in range(args.warmup, n_total):
+    for g in range(warmup, n_total):
         step(g, True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / steps
     per_step = np.array([a.elapsed_time(b) for a, b in events])
     partial_ms = float(per_step.mean())
-    kv = np.array([float((lens + g).sum()) * hkv * 2 * (rb + 2) for g in range(args.warmup, n_total)])
+    kv = np.array([float((lens + grow * g).sum()) * hkv * 2 * (rb + 2) for g in range(warmup, n_total)])
     qo = batch * hq * d * 2
     attn_bytes = kv + 2 * qo                 # packed K/V with norms read, q read, o written
-    partial_bytes = kv + qo                  # the split kernel reads K/V and q; its partial states are O(splits*d)
+    partial_bytes = kv + qo                  # the split phase reads K/V and q; its partial states are O(splits*d)
     value = attn_bytes.sum() / (t1 - t0) / 1e9
     achieved = partial_bytes.mean() / (partial_ms * 1e-3) / 1e9
-    print(f"[bench] headline step {ms_per_step:.4f} ms, partial kernel {partial_ms:.4f} ms, "
+    print(f"[bench] {w['name']}: step {ms_per_step:.4f} ms, split phase {partial_ms:.4f} ms, "
           f"{achieved:.1f} GB/s", file=sys.stderr, flush=True)
+    del kc, vc, ws
     return dict(value=value, ms_per_step=ms_per_step, partial_ms=partial_ms, achieved=achieved,
                 attn_bytes_per_step=attn_bytes.mean(), partial_bytes_per_launch=partial_bytes.mean(),
-                lengths=lens, partial_ms_std=float(per_step.std()),
-                partial_ms_min=float(per_step.min()))
+                lengths=lens, per_step_ms=per_step)
 
 
 def run_fresh_headline(steps, warmup):
@@ -318,77 +369,6 @@ def run_fresh_headline(steps, warmup):
     sys.stderr.write(r.stderr)
     sys.stderr.flush()
     return json.loads(r.stdout.strip().splitlines()[-1])
-
-
-def run_uniform_32k(torch, dev, steps, warmup):
-    """Supplementary: 64 sequences at exactly 32,768 tokens, 32 query / 4 KV
-    heads, d=128, 3-bit Full (the long-context head layout, batched to fill
-    the GPU).  Each step appends into the last row, so every step attends over
-    32,768 rows."""
-    from compressed_space_attention_isoquant_amd import binding as B
-    from compressed_space_attention_isoquant_amd import inputs
-
-    w = UNIFORM_32K
-    batch, T, hq, hkv, d, bits = (w[k] for k in ("batch", "kv_len", "num_q_heads", "num_kv_heads",
-                                                 "head_dim", "bits"))
-    quats = torch.from_numpy(inputs.quaternions(hkv, d)).to(dev)
-    cfg = B.Config(d, bits, B.IQ_FULL, hkv, quats, B.iq_codebook(bits, d))
-    rng = np.random.default_rng(4)
-    ch_k = inputs.outlier_channels(rng, hkv, d)
-    ch_v = inputs.outlier_channels(rng, hkv, d)
-    kc = B.new_cache(batch, hkv, T, d, bits, dev)
-    vc = B.new_cache(batch, hkv, T, d, bits, dev)
-    zero = torch.zeros((batch,), dtype=torch.int32, device=dev)
-    for cache, idx, ch in ((kc, 0, ch_k), (vc, 1, ch_v)):
-        x = inputs.device_kv(40, idx, batch * (T - 1), ch, d, dev).view(batch, T - 1, hkv, d)
-        B.iq_quantize_append(cfg, x, zero, cache)
-        del x
-    torch.cuda.synchronize()
-    P = 8
-    knew = [inputs.device_kv(41, s, batch, ch_k, d, dev).view(batch, 1, hkv, d) for s in range(P)]
-    vnew = [inputs.device_kv(42, s, batch, ch_v, d, dev).view(batch, 1, hkv, d) for s in range(P)]
-    qs = [inputs.device_normal(43, s, (batch, hq, d), dev, torch.float16) for s in range(P)]
-    last = torch.full((batch,), T - 1, dtype=torch.int32, device=dev)
-    kv_len = torch.full((batch,), T, dtype=torch.int32, device=dev)
-    out = torch.empty((batch, hq, d), dtype=torch.float16, device=dev)
-    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
-    ws = torch.empty((B.iq_decode_workspace_bytes(cfg, batch, hq, T),), dtype=torch.uint8, device=dev)
-    scale = 1.0 / math.sqrt(d)
-    stream = torch.cuda.current_stream()
-    events = []
-
-    def step(s, record):
-        B.iq_quantize_append(cfg, knew[s % P], last, kc)
-        B.iq_quantize_append(cfg, vnew[s % P], last, vc)
-        if record:
-            e0, e1 = _events(torch)
-            e0.record(stream)
-        B.iq_decode_attention_partial(cfg, qs[s % P], kc, vc, kv_len, T, scale, ws, track_argmax=False)
-        if record:
-            e1.record(stream)
-            events.append((e0, e1))
-        B.iq_decode_attention_merge(cfg, batch, hq, T, out, lse, None, ws)
-
-    for s in range(warmup):
-        step(s, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        step(s, True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
-    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
-    kv = batch * hkv * T * 2 * (row_bytes(d, bits) + 2)
-    qo = batch * hq * d * 2
-    achieved = (kv + qo) / (partial_ms * 1e-3) / 1e9
-    print(f"[bench] uniform 32K step {ms:.4f} ms, partial kernel {partial_ms:.4f} ms, {achieved:.1f} GB/s",
-          file=sys.stderr, flush=True)
-    return {"workload": "64 sequences x 32768 tokens, 32 query / 4 KV heads, d=128, 3-bit IsoQuant-Full, fp16 I/O",
-            "steps": steps, "ms_per_step": round(ms, 5), "value": round((kv + 2 * qo) / (ms * 1e-3) / 1e9, 2),
-            "unit": "GB/s", "partial_kernel_ms": round(partial_ms, 5),
-            "partial_achieved_gbs": round(achieved, 2), "frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("uniform_32k")}
 
 
 def run_rope_32k(torch, dev, reps=20):
@@ -587,23 +567,67 @@ def run_stage1(torch, dev):
                     qms = ev[0].elapsed_time(ev[1]) / reps
                     dms = ev[1].elapsed_time(ev[2]) / reps
                     io = n * (d * x.element_size() + row_bytes(d, bits) + 2)
+                    qg, dg = io / (qms * 1e-3) / 1e9, io / (dms * 1e-3) / 1e9
                     rates[f"d{d}_b{bits}_{vname}_{dname}"] = {
                         "quantize_mvec_s": round(n / (qms * 1e-3) / 1e6, 1),
                         "dequantize_mvec_s": round(n / (dms * 1e-3) / 1e6, 1),
-                        "quantize_gbs": round(io / (qms * 1e-3) / 1e9, 1),
-                        "dequantize_gbs": round(io / (dms * 1e-3) / 1e9, 1)}
+                        "quantize_gbs": round(qg, 1), "dequantize_gbs": round(dg, 1),
+                        "quantize_hbm_frac": round(qg / HBM_PEAK_GBS, 4),
+                        "dequantize_hbm_frac": round(dg / HBM_PEAK_GBS, 4)}
                     del x, o
                 del c1
     for vname in ("full", "fast", "planar"):
         r = rates[f"d128_b3_{vname}_fp16"]
         print(f"[bench] stage-1 d=128 b=3 {vname} fp16: quantize {r['quantize_mvec_s']} Mvec/s, "
               f"dequantize {r['dequantize_mvec_s']} Mvec/s", file=sys.stderr, flush=True)
+    h = rates["d128_b3_full_fp16"]
     return {"workload": "2^20 unit vectors per setting, d in {128,256,512} x bits in {2,3,4} x "
-                        "{Full,Fast,Planar} x {fp16,fp32} I/O", "rates": rates}
+                        "{Full,Fast,Planar} x {fp16,fp32} I/O; HBM fractions are the algorithmic bytes "
+                        "(d x input bytes + d x b / 8 + 2 per vector, the reverse for dequantize) over the "
+                        "kernel time, against 8 TB/s",
+            "quantize_mvec_s_d128_b3_full_fp16": h["quantize_mvec_s"], "rates": rates}
+
+
+def run_c1_latency(torch, dev, reps=20):
+    """The stage-1 parity configuration as a latency: 4,096 unit vectors,
+    d=128, fp32, 3-bit Full; one quantize (append) call and one dequantize
+    call, each timed alone with HIP events (median of reps, warm)."""
+    from compressed_space_attention_isoquant_amd import binding as B
+    from compressed_space_attention_isoquant_amd import inputs
+
+    n, d, bits = 4096, 128, 3
+    cfg = B.Config(d, bits, B.IQ_FULL, 1, torch.from_numpy(inputs.quaternions(1, d)).to(dev),
+                   B.iq_codebook(bits, d))
+    x = torch.from_numpy(inputs.unit_vectors(n, d, np.float32, seed=1)).to(dev).view(1, n, 1, d)
+    o = torch.empty_like(x)
+    cache = B.new_cache(1, 1, n, d, bits, dev)
+    sp = torch.zeros((1,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = _events(torch)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+
+    q_us = timed(lambda: B.iq_quantize_append(cfg, x, sp, cache))
+    d_us = timed(lambda: B.iq_dequantize(cfg, cache, sp, n, o))
+    print(f"[bench] C1 4096 x 128 fp32: quantize {q_us:.1f} us, dequantize {d_us:.1f} us",
+          file=sys.stderr, flush=True)
+    return {"workload": "4,096 unit vectors, d=128, fp32 I/O, 3-bit Full (one head); single calls, median of "
+                        f"{reps}, warm", "quantize_us": round(q_us, 2), "dequantize_us": round(d_us, 2),
+            "quantize_mvec_s": round(n / q_us, 1)}
 
 
 # Kernels whose HBM traffic is recorded, by the workload they run in.
-TRAFFIC_KERNELS = {"headline": "partial_kernel<256, 3, 2, false, 0>", "uniform_32k": "partial_kernel<128, 3, 8, false, 0>"}
+TRAFFIC_KERNELS = {"headline": "partial_kernel<128, 3, 8, false, 0>",
+                   "batched_append_c5": "partial_kernel<256, 3, 2, false, 0>"}
 
 
 def summarize_counters(fetch_csv, write_csv):
@@ -732,15 +756,15 @@ def summarize_stage1(counter_csv):
     return 0
 
 
-def _oracle_worker(T, seconds):
+def _oracle_worker(w, T, seconds):
     """One process: the oracle's dequantize-then-attend on one (sequence,
-    KV head) pair of T rows of the headline shape, repeated for about
-    ``seconds``.  Returns (repetitions, elapsed seconds)."""
+    KV head) pair of T rows of workload w with its G query heads, repeated
+    for about ``seconds``.  Returns (repetitions, elapsed seconds)."""
     import oracle as O
     from compressed_space_attention_isoquant_amd import inputs
 
-    w = HEADLINE
     d, bits = w["head_dim"], w["bits"]
+    variant = {"full": O.FULL, "fast": O.FAST}[w["variant"]]
     group = w["num_q_heads"] // w["num_kv_heads"]
     rng = np.random.default_rng(44)
     ch = inputs.outlier_channels(rng, 1, d)[0]
@@ -752,60 +776,110 @@ def _oracle_worker(T, seconds):
     q = rng.standard_normal((group, d)).astype(np.float16)
     quats = inputs.quaternions(1, d)
     cb = O.codebook(bits, d)
-    rk = O.quantize(k, quats[0], cb, O.FAST)
-    rv = O.quantize(v, quats[0], cb, O.FAST)
+    rk = O.quantize(k, quats[0], cb, variant)
+    rv = O.quantize(v, quats[0], cb, variant)
     kr, kn = O.pack(rk["codes"], bits)[None], rk["norm16"][None]
     vr, vn = O.pack(rv["codes"], bits)[None], rv["norm16"][None]
     reps, t0 = 0, time.perf_counter()
     while True:
-        O.attend(q, kr, kn, vr, vn, quats, cb, bits, O.FAST, 1.0 / math.sqrt(d))
+        O.attend(q, kr, kn, vr, vn, quats, cb, bits, variant, 1.0 / math.sqrt(d))
         reps += 1
         if time.perf_counter() - t0 >= seconds:
             break
     return reps, time.perf_counter() - t0
 
 
-def cpu_baseline(lengths, seconds, max_workers=16):
-    """The FP64 oracle's dequantize-then-attend on a bounded sample of the
-    headline workload: each of W worker processes (one per host core this
-    process may use, at most 16; BLAS held to one thread each) runs one
-    (sequence, KV head) pair at the median context length with its query
-    heads for about ``seconds``.  Aggregate packed-KV GB/s over the workers."""
+# The box grants one GPU 16 host cores, whatever the host has: the baseline's
+# process pool is held to that share.
+CPU_SHARE = 16
+
+
+def _host_workers(max_workers=CPU_SHARE):
+    return max(1, min(max_workers, len(os.sched_getaffinity(0))))
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+def _pool_map(fn, argsets):
+    """Run fn over argsets in one spawned process per entry, BLAS held to one
+    thread per process."""
     import concurrent.futures as cf
     import multiprocessing as mp
 
-    w = HEADLINE
-    d, bits = w["head_dim"], w["bits"]
-    T = int(np.median(lengths))
-    group = w["num_q_heads"] // w["num_kv_heads"]
-    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
     saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in saved:
         os.environ[k] = "1"
     try:
-        with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
-            res = list(ex.map(_oracle_worker, [T] * workers, [seconds] * workers))
+        with cf.ProcessPoolExecutor(max_workers=len(argsets), mp_context=mp.get_context("spawn")) as ex:
+            return list(ex.map(fn, *zip(*argsets)))
     finally:
         for k, val in saved.items():
             if val is None:
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = val
+
+
+def cpu_baseline(w, lengths, seconds):
+    """The FP64 oracle's dequantize-then-attend on a bounded sample of
+    workload w: each of W worker processes (one per host core of the box's
+    share) runs one (sequence, KV head) pair at the median context length
+    with its query heads for about ``seconds``.  Aggregate packed-KV GB/s
+    over the workers."""
+    d, bits = w["head_dim"], w["bits"]
+    T = int(np.median(lengths))
+    group = w["num_q_heads"] // w["num_kv_heads"]
+    workers = _host_workers()
+    res = _pool_map(_oracle_worker, [(w, T, seconds)] * workers)
     nbytes = T * 2 * (row_bytes(d, bits) + 2)
     rate = sum(r * nbytes / dt for r, dt in res)
     per = float(np.mean([dt / r for r, dt in res]))
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
     return {"value": round(rate / 1e9, 5), "unit": "GB/s", "cores": workers, "kind": "oracle",
-            "one_core_value": round(nbytes / per / 1e9, 5), "cpu_model": model,
+            "one_core_value": round(nbytes / per / 1e9, 5), "cpu_model": _cpu_model(),
+            "host_cores_visible": len(os.sched_getaffinity(0)),
             "sample": f"{workers} processes (one BLAS thread each), each repeating one (sequence, KV head) "
-                      f"pair of the headline workload at the median context length {T}: {T} packed K/V rows, "
-                      f"{group} query heads, d={d}; {sum(r for r, _ in res)} repetitions in all, "
-                      f"{per:.3f} s each (NumPy FP64)"}
+                      f"pair of this workload at context length {T}: {T} packed K/V rows, "
+                      f"{group} query heads, d={d}, {bits}-bit {w['variant']}; {sum(r for r, _ in res)} "
+                      f"repetitions in all, {per:.3f} s each (NumPy FP64)"}
+
+
+def _oracle_stage1_worker(d, bits, n, seconds):
+    """One process: the oracle's quantize (normalise, WHT, SO(4), Lloyd-Max,
+    pack) of chunks of n unit vectors, d, bits, Full, fp16 input, repeated
+    for about ``seconds``.  Returns (vectors, elapsed seconds)."""
+    import oracle as O
+    from compressed_space_attention_isoquant_amd import inputs
+
+    x = inputs.unit_vectors(n, d, np.float16, seed=2)
+    quats = inputs.quaternions(1, d)
+    cb = O.codebook(bits, d)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        r = O.quantize(x, quats[0], cb, O.FULL)
+        O.pack(r["codes"], bits)
+        done += n
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline_stage1(seconds, d=128, bits=3, n=8192):
+    """The oracle's stage-1 quantize rate (vectors/s) over the machine's host-core
+    share, each worker quantizing chunks of n vectors of the sweep's d=128,
+    3-bit, Full, fp16 setting for about ``seconds``."""
+    workers = _host_workers()
+    res = _pool_map(_oracle_stage1_worker, [(d, bits, n, seconds)] * workers)
+    rate = sum(v / dt for v, dt in res)
+    return {"value": round(rate / 1e6, 4), "unit": "Mvec/s", "cores": workers, "kind": "oracle",
+            "one_core_value": round(float(np.mean([v / dt for v, dt in res])) / 1e6, 4),
+            "sample": f"{workers} processes, each quantizing chunks of {n} unit vectors (d={d}, {bits}-bit Full, "
+                      f"fp16 in) for about {seconds:.0f} s; {sum(v for v, _ in res)} vectors in all (NumPy FP64)"}
 
 
 if __name__ == "__main__":

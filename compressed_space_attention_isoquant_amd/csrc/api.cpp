@@ -30,28 +30,16 @@ int check_config(const iq_config *cfg) {
   if (cfg->num_kv_heads < 1) return IQ_ERR_INVALID_ARG;
   if (!aligned16(cfg->quats)) return IQ_ERR_MISALIGNED;
   const int n = 1 << cfg->bits;
-  float lo = INFINITY, hi = 0.f;
   for (int k = 0; k < n; ++k) {
     const float c = cfg->centroids[k];
     if (!std::isfinite(c)) return IQ_ERR_INVALID_ARG;
     if (k > 0 && !(c > cfg->centroids[k - 1])) return IQ_ERR_INVALID_ARG;
-    // fp16 precision: at most 11 significant bits (low 13 fp32 mantissa bits clear)
-    uint32_t u;
-    std::memcpy(&u, &c, 4);
-    if (c != 0.f && ((u & 0x1FFFu) != 0 || (u & 0x7F800000u) == 0)) return IQ_ERR_INVALID_ARG;
-    if (c != 0.f) {
-      lo = std::fmin(lo, std::fabs(c));
-      hi = std::fmax(hi, std::fabs(c));
-    }
   }
-  // one power-of-two scale must bring every level into the fp16 normal range
-  if (hi > 0.f && hi / lo >= 0x1p28f) return IQ_ERR_INVALID_ARG;
   return IQ_OK;
 }
 
-// Scale exponent e with max|c| * 2^e in [1, 2), and the table of fp16 pairs
-// (c_i 2^e, c_k 2^e) at index i | k << bits.  Exact: every level has at most
-// 11 significant bits (checked in check_config).
+// Scale exponent e with max|c| * 2^e in [1, 2): the decode kernels feed the
+// levels to fp16 matrix instructions as c * 2^e.
 int centroid_exponent(const iq_config *cfg) {
   float hi = 0.f;
   for (int k = 0; k < (1 << cfg->bits); ++k) hi = std::fmax(hi, std::fabs(cfg->centroids[k]));
@@ -61,19 +49,36 @@ int centroid_exponent(const iq_config *cfg) {
   return 1 - e;
 }
 
-uint16_t fp16_bits_exact(float x) {
+uint16_t fp16_bits(float x) {
   const _Float16 h = static_cast<_Float16>(x);
   uint16_t b;
   std::memcpy(&b, &h, 2);
   return b;
 }
 
+// Whether every level times 2^e (e from centroid_exponent) is an fp16 number
+// exactly, so that the decode kernels attend with the same centroids the
+// quantiser used.  Levels with at most 11 significant bits (what iq_codebook
+// produces) pass whenever max/min nonzero magnitude is below 2^14; past that
+// a level passes only if it is an exact fp16 subnormal once scaled.
+bool decode_codebook_exact(const iq_config *cfg) {
+  const int e = centroid_exponent(cfg);
+  for (int k = 0; k < (1 << cfg->bits); ++k) {
+    const float s = std::ldexp(cfg->centroids[k], e);
+    const _Float16 h = static_cast<_Float16>(s);
+    if (static_cast<float>(h) != s) return false;
+  }
+  return true;
+}
+
+// The table of fp16 pairs (c_i 2^e, c_k 2^e) at index i | k << bits; exact
+// (decode_codebook_exact is checked before any decode launch).
 void fill_pair_table(const iq_config *cfg, int e, uint32_t *lut) {
   const int n = 1 << cfg->bits;
   for (int i = 0; i < n; ++i)
     for (int k = 0; k < n; ++k) {
-      const uint32_t lo = fp16_bits_exact(std::ldexp(cfg->centroids[i], e));
-      const uint32_t hi = fp16_bits_exact(std::ldexp(cfg->centroids[k], e));
+      const uint32_t lo = fp16_bits(std::ldexp(cfg->centroids[i], e));
+      const uint32_t hi = fp16_bits(std::ldexp(cfg->centroids[k], e));
       lut[i | (k << cfg->bits)] = lo | (hi << 16);
     }
 }
@@ -177,7 +182,9 @@ const char *iq_status_string(int status) {
   switch (status) {
     case IQ_OK: return "ok";
     case IQ_ERR_INVALID_ARG: return "invalid argument";
-    case IQ_ERR_UNSUPPORTED: return "unsupported head_dim, bits, group size or dtype";
+    case IQ_ERR_UNSUPPORTED:
+      return "unsupported head_dim, bits, group size, dtype or shape, or (decode) a codebook whose levels "
+             "are not exact fp16 numbers once scaled";
     case IQ_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case IQ_ERR_WORKSPACE: return "workspace too small";
     case IQ_ERR_HIP: return "HIP runtime or launch error";
@@ -345,7 +352,7 @@ constexpr int32_t kMaxDecodeBatch = 65535;
 
 size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
                                  int64_t max_kv_len) {
-  if (check_config(cfg) != IQ_OK) return 0;
+  if (check_config(cfg) != IQ_OK || !decode_codebook_exact(cfg)) return 0;
   if (batch < 1 || batch > kMaxDecodeBatch || num_q_heads < 1 || max_kv_len < 0) return 0;
   if (num_q_heads % cfg->num_kv_heads) return 0;
   const iq::Geometry g = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
@@ -357,6 +364,7 @@ static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_
                                int *group) {
   int st = check_config(cfg);
   if (st != IQ_OK) return st;
+  if (!decode_codebook_exact(cfg)) return IQ_ERR_UNSUPPORTED;
   if (!workspace) return IQ_ERR_INVALID_ARG;
   if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return IQ_ERR_INVALID_ARG;
   if (batch > kMaxDecodeBatch) return IQ_ERR_UNSUPPORTED;

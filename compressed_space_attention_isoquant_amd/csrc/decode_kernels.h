@@ -739,9 +739,13 @@ void partial_kernel(DecodeArgs a) {
         const float sc = exp2f(red_o[w][hh][D] - M);
         o += red_o[w][hh][i] * sc;
         L += red_o[w][hh][D + 1] * sc;
-        if (red_o[w][hh][D + 2] > bsc) {
-          bsc = red_o[w][hh][D + 2];
-          bpos = __builtin_bit_cast(int, red_o[w][hh][D + 3]);
+        // the larger score; on equal scores the lower position (the waves
+        // hold interleaved tiles, so wave order is not position order)
+        const float ws = red_o[w][hh][D + 2];
+        const int wp = __builtin_bit_cast(int, red_o[w][hh][D + 3]);
+        if (ws > bsc || (ws == bsc && wp >= 0 && (bpos < 0 || wp < bpos))) {
+          bsc = ws;
+          bpos = wp;
         }
       }
     }

@@ -92,25 +92,13 @@ struct IO<_Float16> {
   }
 };
 
-// Value of lane (lane ^ M) within groups of 32 lanes, M a power of two < 32.
-// DPP (a vector-ALU move, no latency) serves M = 1, 2 (quad permutes) and
-// M = 8 (row rotate by 8) when DPP is set; otherwise, and for M = 4 and 16,
-// ds_swizzle (bit-mask mode) goes through the LDS crossbar, which costs no
-// vector-ALU slot but has LDS latency.
-template <int M, bool DPP>
+// Value of lane (lane ^ M) within groups of 32 lanes for M = 4 and 16, which
+// no DPP pattern of one row reaches: ds_swizzle (bit-mask mode) goes through
+// the LDS crossbar, which costs no vector-ALU slot but has LDS latency.
+template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
-  static_assert(M > 0 && M < 32 && (M & (M - 1)) == 0, "xor mask");
-  const int x = __builtin_bit_cast(int, v);
-  int r;
-  if constexpr (DPP && M == 1)
-    r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
-  else if constexpr (DPP && M == 2)
-    r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
-  else if constexpr (DPP && M == 8)
-    r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true);  // row_ror:8
-  else
-    r = __builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1F);
-  return __builtin_bit_cast(float, r);
+  static_assert(M == 4 || M == 16, "swizzle exchange");
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), (M << 10) | 0x1F));
 }
 
 // Unnormalised Walsh-Hadamard butterflies over d = 32 * LPV elements held as
@@ -160,7 +148,9 @@ __device__ __forceinline__ void dpp_fmac8(float (&r)[32], float sign) {
 }
 #undef IQ_DPP_FMAC8
 
-template <int LPV, bool DPP>
+// Lane distances 1, 2 and 8 ride on the multiply-add (DPP operand), 4 and 16
+// go through the swizzle.
+template <int LPV>
 __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
@@ -183,7 +173,7 @@ __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
       dpp_fmac8<hl, 24>(r, sign);
     } else {
 #pragma unroll
-      for (int k = 0; k < 32; ++k) r[k] = fmaf(lane_xor<hl, DPP>(r[k]), sign, r[k]);
+      for (int k = 0; k < 32; ++k) r[k] = fmaf(lane_xor<hl>(r[k]), sign, r[k]);
     }
     // Finish the stage before the next: left to itself the scheduler runs
     // each value through all stages in turn, one exchange latency at a time.
@@ -312,9 +302,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 #pragma unroll
     for (int k = 0; k < 32; ++k) r[k] = (float)xin[k] * inv;
 
-    // DPP exchanges measured faster except for d = 128, where the LDS
-    // swizzle relieves the vector ALU
-    wht_butterflies<LPV, (D > 128)>(r, j);
+    wht_butterflies<LPV>(r, j);
 
     // block rotations; the matrices carry the butterflies' lane sign
 #pragma unroll
@@ -481,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
       r[4 * blk + 3] = u.w;
     }
 
-    wht_butterflies<LPV, true>(r, j);
+    wht_butterflies<LPV>(r, j);
 
     const float scale = lane_sign<LPV>(j) * s16 / sqrtf((float)D);
 #pragma unroll

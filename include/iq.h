@@ -69,7 +69,9 @@ extern "C" {
 typedef enum {
   IQ_OK = 0,
   IQ_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum value */
-  IQ_ERR_UNSUPPORTED = -2, /* d, b, group size or dtype outside the built set */
+  IQ_ERR_UNSUPPORTED = -2, /* d, b, group size, dtype or shape outside the built
+                              set, or (decode) a codebook the fp16 matrix cores
+                              cannot hold exactly */
   IQ_ERR_MISALIGNED = -3,  /* a base pointer is not 16-byte aligned */
   IQ_ERR_WORKSPACE = -4,   /* workspace smaller than iq_decode_workspace_bytes */
   IQ_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
@@ -94,10 +96,18 @@ typedef struct {
                               [H_kv][d/4][2][4] unit quaternions (q_L, q_R),
                               each (w, x, y, z); Planar [H_kv][d/2][2] unit
                               complex numbers (cos, sin) */
-  const float *centroids;  /* HOST [2^b] fp32, strictly ascending, finite, each
-                              with at most 11 significant bits (fp16 precision,
-                              as iq_codebook produces) and max/min nonzero
-                              magnitude below 2^28; else IQ_ERR_INVALID_ARG */
+  const float *centroids;  /* HOST [2^b] fp32, strictly ascending and finite
+                              (else IQ_ERR_INVALID_ARG).  The decode entry
+                              points also need every level, times the power
+                              of two 2^e that brings the largest magnitude
+                              into [1, 2), to be an fp16 number exactly: they
+                              multiply the levels on fp16 matrix cores.  Levels
+                              with at most 11 significant bits (iq_codebook's)
+                              meet this whenever max/min nonzero magnitude is
+                              below 2^14; otherwise the decode entry points
+                              return IQ_ERR_UNSUPPORTED (and
+                              iq_decode_workspace_bytes 0), while quantize and
+                              dequantize take any such codebook. */
 } iq_config;
 
 /* One packed tensor (K or V) of a KV cache (a HOST struct). */
@@ -181,7 +191,9 @@ int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch,
 /* Bytes of workspace iq_decode_attention needs for these sizes.  Returns 0 if
  * the arguments are invalid.  O(batch * Hq * splits * d) floats of split
  * records plus 8 bytes per (sequence, split) for the work order: never
- * O(T * d) -- the decode path writes no dequantized K or V. */
+ * O(T * d) -- the decode path writes no dequantized K or V, the
+ * zero-materialization property RotaryQuant Appendix D confirms with its
+ * instrumentation counters (no decompress or key-read calls). */
 size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch,
                                  int32_t num_q_heads, int64_t max_kv_len);
 

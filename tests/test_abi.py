@@ -114,10 +114,12 @@ def test_quantize_validation():
     nan = O.codebook(3, 128).copy()
     nan[0] = np.nan
     assert call_quant(cfg(centroids=nan)) == -1
-    # levels must carry fp16 precision (at most 11 significant bits)
+    # quantize takes any finite, ascending fp32 codebook: a level with more
+    # than 11 significant bits passes the configuration check (the call then
+    # stops at the dtype, the next check)
     fine = O.codebook(3, 128).copy()
     fine[5] = np.nextafter(fine[5], np.float32(1))
-    assert call_quant(cfg(centroids=fine)) == -1
+    assert call_quant(cfg(centroids=fine), xdt=7) == -2
 
 
 def call_decode(c, hq=32, batch=1, max_len=16, cap=16, ws_bytes=None, q=0x2000, out=0x6000,
@@ -155,6 +157,42 @@ def test_decode_validation():
     assert call_decode(c, batch=65536) == -2                # grid limit
     assert L.iq_decode_workspace_bytes(ctypes.byref(cc), 65536, 32, 16) == 0
     assert call_decode(cfg(d=64)) == -2
+
+
+def ratio_codebook(smallest):
+    """Eight ascending levels with largest magnitude 1 and ``smallest`` the
+    smallest positive one."""
+    return np.array([-1.0, -0.5, -0.25, -0.125, smallest, 0.25, 0.5, 1.0], np.float32)
+
+
+def test_decode_codebook_exactness():
+    """Decode multiplies the levels (times the power of two that brings the
+    largest into [1, 2)) on fp16 matrix cores, so it takes a codebook only if
+    every scaled level is an fp16 number exactly: 11 significant bits over a
+    max/min magnitude ratio below 2^14 always; the first 11-bit level past
+    that is rejected (IQ_ERR_UNSUPPORTED, workspace size 0), while quantize
+    still takes it.  Exact fp16 subnormals are accepted."""
+    L = B.lib()
+    ok_edge = 2.0 ** -14 * (1 + 2.0 ** -10)          # ratio just below 2^14: normal fp16
+    first_bad = 2.0 ** -15 * (1 + 2.0 ** -10)        # ratio just below 2^15: not on the subnormal grid
+    for smallest, fits in ((ok_edge, True), (first_bad, False), (2.0 ** -15, True), (3 * 2.0 ** -24, True),
+                           (2.0 ** -25, False)):
+        c = cfg(centroids=ratio_codebook(smallest))
+        cc = c.c()
+        need = L.iq_decode_workspace_bytes(ctypes.byref(cc), 1, 32, 16)
+        assert (need > 0) == fits, smallest
+        # an accepted codebook reaches the workspace check, a rejected one stops before
+        assert call_decode(c, ws_bytes=0) == (-4 if fits else -2), smallest
+        assert call_quant(c, xdt=7) == -2                    # quantize: past the codebook, stops at the dtype
+    # the library's own codebooks always fit
+    for bits in (2, 3, 4):
+        for d in (128, 256, 512):
+            cc = cfg(d=d, bits=bits).c()
+            assert L.iq_decode_workspace_bytes(ctypes.byref(cc), 1, 32, 16) > 0
+    # more than 11 significant bits: quantize yes, decode no
+    fine = O.codebook(3, 128).copy()
+    fine[5] = np.nextafter(fine[5], np.float32(1))
+    assert call_decode(cfg(centroids=fine)) == -2
 
 
 def test_dequantize_validation():

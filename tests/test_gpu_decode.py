@@ -116,19 +116,20 @@ def test_c3_decode_8k(variant):
     say(f"C3 v={variant}: cosine vs unquantized attention min={min(cos):.4f} mean={np.mean(cos):.4f}")
 
 
-def test_c4_needles_32k():
+@pytest.mark.parametrize("variant", [O.FULL, O.FAST])
+def test_c4_needles_32k(variant):
     d, bits, hq, hkv, T = 128, 3, 32, 4, 32768
     case = inputs.decode_case(seed=4, kv_len=T, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, needles=16)
-    cfg, quats, kc, vc = decode_case_gpu(case, d, bits, O.FULL, hkv)
+    cfg, quats, kc, vc = decode_case_gpu(case, d, bits, variant, hkv)
     q = case["q"][None]
     got, lse, arg = run_decode(cfg, q, kc, vc, [T], T)
     ref, rlse, rarg = oracle_decode(q, case["k"][None], case["v"][None], quats, cfg, [T],
                                     host_cache(kc), host_cache(vc))
-    check_outputs("C4", got, lse, arg, ref, rlse, rarg, 2e-3)
+    check_outputs(f"C4 v={variant}", got, lse, arg, ref, rlse, rarg, 2e-3)
     for h, g, p in case["needles"]:
         assert arg[0, h] == p, (h, g, p, arg[0, h])
         assert rarg[0, h] == p
-    say(f"C4: all {len(case['needles'])} needle argmax positions preserved")
+    say(f"C4 v={variant}: all {len(case['needles'])} needle argmax positions preserved")
 
 
 SHAPES = [  # (d, bits, hq, hkv, variant)
@@ -172,6 +173,119 @@ def test_decode_fp32_io():
     got, lse, arg = run_decode(cfg, q, kc, vc, [T], T, q_f16=False)
     ref, rlse, rarg = oracle_decode(q, k, v, quats, cfg, [T], host_cache(kc), host_cache(vc))
     check_outputs("fp32 I/O", got, lse, arg, ref, rlse, rarg, 1e-5)
+
+
+# every (d, b, variant) with fp32 queries and outputs; the group size cycles
+# through 8, 4, 2, 1
+FP32_SWEEP = [(d, bits, variant, (8, 4, 2, 1)[(i + j) % 4])
+              for i, d in enumerate((128, 256, 512)) for j, bits in enumerate((2, 3, 4))
+              for variant in (O.FULL, O.FAST, O.PLANAR)]
+
+
+@pytest.mark.parametrize("d,bits,variant,group", FP32_SWEEP)
+def test_decode_fp32_io_sweep(d, bits, variant, group):
+    """fp32 queries and outputs for every head_dim, bit width and variant, on
+    a ragged batch (an empty sequence, a single token, 651 tokens): max-abs
+    1e-5 and the oracle's argmax."""
+    hkv = 2
+    hq = group * hkv
+    rng = np.random.default_rng(1000 + 10 * d + bits + 100 * variant)
+    cap, lens = 700, [0, 1, 651]
+    batch = len(lens)
+    cfg, quats = make_config(d, bits, variant, hkv)
+    k = (rng.standard_normal((batch, cap, hkv, d)) * 2).astype(np.float16)
+    v = (rng.standard_normal((batch, cap, hkv, d)) * 2).astype(np.float16)
+    q = rng.standard_normal((batch, hq, d)).astype(np.float32)
+    kc = quantize_rows(cfg, k)
+    vc = quantize_rows(cfg, v)
+    got, lse, arg = run_decode(cfg, q, kc, vc, lens, max(lens), q_f16=False)
+    ref, rlse, rarg = oracle_decode(q, k, v, quats, cfg, lens, host_cache(kc), host_cache(vc))
+    check_outputs(f"fp32 I/O d={d} b={bits} G={group} v={variant}", got, lse, arg, ref, rlse, rarg, 1e-5,
+                  check_arg=True)
+    assert np.all(got[0] == 0) and np.all(arg[0] == -1)
+    assert np.all(arg[1] == 0)
+
+
+def test_argmax_ties_lowest_position():
+    """Exact score ties (identical K rows) resolve to the lowest position
+    wherever the tied tokens meet in the kernel: in one tile on the two halves
+    of the score tile (5, 20), in different lane groups (1, 6), in different
+    tiles of one workgroup that different waves take (32, 128), and in
+    different context splits or work ranges (300, 20000, 32767).  One 32K
+    sequence, 32 query / 4 KV heads (the needle-search shape)."""
+    d, bits, hq, hkv, T = 128, 3, 32, 4, 32768
+    case = inputs.decode_case(seed=31, kv_len=T, num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
+    k, q = case["k"], case["q"]
+    med = float(np.median(np.linalg.norm(k[:, 0].astype(np.float64), axis=-1)))
+    ties = {0: (128, 32), 1: (20, 5), 2: (6, 1), 3: (20000, 300), 4: (32767, 300, 20000), 5: (159, 129, 33)}
+    for h, positions in ties.items():
+        qh = q[h].astype(np.float64)
+        key = (1.5 * med * qh / np.linalg.norm(qh)).astype(np.float16)
+        for p in positions:
+            k[p, 0] = key                         # KV head 0 serves query heads 0..7
+    cfg, quats, kc, vc = decode_case_gpu(case, d, bits, O.FULL, hkv)
+    got, lse, arg = run_decode(cfg, q[None], kc, vc, [T], T)
+    ref, rlse, rarg = oracle_decode(q[None], k[None], case["v"][None], quats, cfg, [T], host_cache(kc),
+                                    host_cache(vc))
+    check_outputs("argmax ties", got, lse, arg, ref, rlse, rarg, 2e-3, check_arg=True)
+    for h, positions in ties.items():
+        assert rarg[0, h] == min(positions), (h, rarg[0, h])
+        assert arg[0, h] == min(positions), (h, positions, arg[0, h])
+    say(f"argmax ties: lowest positions {[min(p) for p in ties.values()]} for heads {list(ties)}")
+
+
+def edge_codebook(bits):
+    """An asymmetric codebook whose levels have 11 significant bits and span
+    max/min magnitudes just below 2^14, the widest range the fp16 matrix
+    operands hold exactly (all levels normal fp16 numbers once scaled)."""
+    n = 1 << bits
+    top = 0.25
+    smallest = 2.0 ** -16 * (1 + 2.0 ** -10)      # 0.25 / smallest just below 2^14
+    lv = np.concatenate([-top * np.linspace(0.8, 0.1, n // 2 - 1) ** 1.3, [smallest],
+                         top * np.linspace(0.15, 1.0, n // 2) ** 1.2])
+    m, e = np.frexp(lv)
+    lv = np.ldexp(np.round(np.ldexp(m, 11)), e - 11)      # 11 significant bits
+    lv[n // 2 - 1] = smallest
+    assert np.all(np.diff(lv) > 0) and np.max(np.abs(lv)) / np.min(np.abs(lv)) < 2.0 ** 14
+    return lv.astype(np.float32)
+
+
+@pytest.mark.parametrize("bits,io", [(3, np.float16), (3, np.float32), (2, np.float32), (4, np.float16)])
+def test_decode_custom_codebook_at_range_edge(bits, io):
+    """Decode with a caller's codebook at the edge of what the decode kernels
+    take (levels 2^14 apart in magnitude, asymmetric): the kernels must attend
+    with exactly these centroids, as the oracle does."""
+    t = torch()
+    d, hq, hkv, T = 128, 8, 2, 900
+    rng = np.random.default_rng(40 + bits)
+    cent = edge_codebook(bits)
+    quats = inputs.quaternions(hkv, d)
+    cfg = B.Config(d, bits, O.FULL, hkv, t.from_numpy(quats).to(DEV), cent)
+    k = (rng.standard_normal((1, T, hkv, d)) * 2).astype(np.float16)
+    v = (rng.standard_normal((1, T, hkv, d)) * 2).astype(np.float16)
+    q = rng.standard_normal((1, hq, d)).astype(io)
+    kc = quantize_rows(cfg, k)
+    vc = quantize_rows(cfg, v)
+    got, lse, arg = run_decode(cfg, q, kc, vc, [T], T, q_f16=io == np.float16)
+    hk, hv = host_cache(kc), host_cache(vc)
+    rows, norms = [], []
+    for x, (codes, nrm) in ((k, hk), (v, hv)):
+        r = np.empty((hkv, T, d * bits // 8), np.uint8)
+        n = np.empty((hkv, T), np.uint16)
+        for g in range(hkv):
+            ref = O.quantize(x[0, :, g], quats[g], cent.astype(np.float64), O.FULL)
+            c, _, _ = reconcile_codes(codes[0, g], ref["codes"], ref["flags"], bits, d)
+            n[g], _, _ = reconcile_norms(nrm[0, g], ref["norm16"], ref["norm_flags"])
+            r[g] = O.pack(c, bits)
+        rows.append(r)
+        norms.append(n)
+    used = np.bincount(O.unpack(rows[0], bits, d).ravel(), minlength=1 << bits)
+    ro, rl, ra = O.attend(q[0], rows[0], norms[0], rows[1], norms[1], quats, cent.astype(np.float64), bits,
+                          O.FULL, scale_for(d))
+    tol = 1e-5 if io == np.float32 else 2e-3
+    check_outputs(f"edge codebook b={bits} {np.dtype(io).name}", got, lse, arg, ro[None], rl[None], ra[None], tol,
+                  check_arg=True)
+    assert used[(1 << bits) // 2 - 1] > 0        # the smallest level is in use
 
 
 def test_split_geometry_invariance():

@@ -4,7 +4,8 @@ RoPE coordinates, neither rotated nor quantised) against the oracle.
 Bars as for the plain path: content codes bit-exact outside the 1e-6
 boundary band, norms bit-exact outside the fp16 midpoint band, the fp16 RoPE
 coordinates bit-exact, attention outputs within max-abs 2e-3 on the fp32
-output, lse within 1e-4, argmax equal.
+output for fp16 queries and 1e-5 for fp32 queries, lse within 1e-4, argmax
+equal.
 """
 
 import numpy as np
@@ -125,8 +126,11 @@ def test_rope_decode_ragged(d, bits, hq, hkv, variant, qdt):
     B.iq_quantize_append(cfg, t.from_numpy(v).to(DEV), t.zeros((batch,), dtype=t.int32, device=DEV), vc)
     got, lse, arg = run_rope_decode(cfg, q, kc, rope, vc, lens, max(lens))
     ref, rlse, rarg = oracle_rope_decode(q, k, v, quats, cfg, lens, kc, rope, vc)
-    check_outputs(f"rope decode d={d} b={bits} G={hq // hkv} v={variant}", got, lse, arg, ref, rlse, rarg, 2e-3,
-                  check_arg=True)
+    # fp32 queries and outputs: the fp32 I/O bar (the fp16 RoPE rows are
+    # exact inputs on both sides, so they set no looser bound)
+    tol = 1e-5 if qdt == np.float32 else 2e-3
+    check_outputs(f"rope decode d={d} b={bits} G={hq // hkv} v={variant} q={np.dtype(qdt).name}", got, lse, arg,
+                  ref, rlse, rarg, tol, check_arg=True)
     assert np.all(got[0] == 0) and np.all(arg[0] == -1)
 
 

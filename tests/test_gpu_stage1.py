@@ -96,7 +96,7 @@ def check_custom_codebook(cent, variant, d, dt, label):
     t = torch()
     bits = int(np.log2(len(cent)))
     cent = np.asarray(cent, np.float32)
-    quats = inputs.quaternions(1, d, seed=inputs.QUATERNION_SEED)
+    quats = inputs.rotation_params(1, d, variant, seed=inputs.QUATERNION_SEED)
     cfg = B.Config(d, bits, variant, 1, t.from_numpy(quats).to(DEV), cent)
     x = inputs.unit_vectors(777, d, dt, seed=11 + bits)
     cache = quantize_rows(cfg, x[None, :, None, :])
@@ -128,6 +128,17 @@ def test_custom_codebook_asymmetric():
     cent = np.float16(-0.09 + 0.15 * k ** 1.3).astype(np.float32)
     hist = check_custom_codebook(cent, O.FAST, 256, np.float16, "asymmetric")
     assert hist[0] > 0 and hist[-1] > 0
+
+
+@pytest.mark.parametrize("bits,d,variant,dt", [(3, 128, O.FULL, np.float32), (2, 256, O.FAST, np.float16),
+                                                (4, 512, O.PLANAR, np.float32)])
+def test_full_precision_fp32_codebook(bits, d, variant, dt):
+    """Stage 1 takes a caller's codebook at full fp32 precision (the Lloyd-Max
+    levels for N(0, 1/d) cast to fp32, not held to 11 significant bits): codes
+    and dequantized vectors against the oracle on the same levels."""
+    cent = (O.lloyd_max_gaussian(bits) / np.sqrt(d)).astype(np.float32)
+    assert not np.array_equal(cent, O.codebook(bits, d))          # really beyond fp16 precision
+    check_custom_codebook(cent, variant, d, dt, f"fp32 codebook b={bits} d={d}")
 
 
 def test_append_offsets_batches_and_heads():
