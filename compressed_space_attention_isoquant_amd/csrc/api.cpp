@@ -350,13 +350,18 @@ int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch, const
 // The decode grids carry the sequence index in their second dimension.
 constexpr int32_t kMaxDecodeBatch = 65535;
 
+// Tiles of all (sequence, KV head) segments together stay below this (the
+// kernels index them with 32-bit integers).
+constexpr int64_t kMaxDecodeTiles = int64_t(1) << 30;
+
 size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
                                  int64_t max_kv_len) {
   if (check_config(cfg) != IQ_OK || !decode_codebook_exact(cfg)) return 0;
   if (batch < 1 || batch > kMaxDecodeBatch || num_q_heads < 1 || max_kv_len < 0) return 0;
   if (num_q_heads % cfg->num_kv_heads) return 0;
-  const iq::Geometry g = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
-  return iq::decode_workspace_total(batch, num_q_heads, g.n_split, cfg->head_dim);
+  const int64_t tiles = (max_kv_len + iq::kDecodeStep - 1) / iq::kDecodeStep;
+  if (tiles * batch * cfg->num_kv_heads >= kMaxDecodeTiles) return 0;
+  return iq::decode_workspace_total(batch, cfg->num_kv_heads, num_q_heads, cfg->head_dim);
 }
 
 static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
@@ -369,6 +374,8 @@ static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_
   if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return IQ_ERR_INVALID_ARG;
   if (batch > kMaxDecodeBatch) return IQ_ERR_UNSUPPORTED;
   if (num_q_heads % cfg->num_kv_heads) return IQ_ERR_INVALID_ARG;
+  if ((max_kv_len + iq::kDecodeStep - 1) / iq::kDecodeStep * batch * cfg->num_kv_heads >= kMaxDecodeTiles)
+    return IQ_ERR_UNSUPPORTED;
   *group = num_q_heads / cfg->num_kv_heads;
   if (*group != 1 && *group != 2 && *group != 4 && *group != 8) return IQ_ERR_UNSUPPORTED;
   if (!aligned16(workspace)) return IQ_ERR_MISALIGNED;
@@ -411,7 +418,12 @@ static int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dt
     if (k->capacity * rope_dim * 2 >= (int64_t(1) << 30)) return IQ_ERR_UNSUPPORTED;
   }
 
-  const iq::Geometry geo = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
+  // one resident round of partial workgroups on this device
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return IQ_ERR_HIP;
+  const int groups = iq::decode_groups_per_cu(cfg->head_dim, cfg->bits, rope_dim, track_argmax != 0);
   const int e = centroid_exponent(cfg);
   iq::DecodeArgs a;
   a.q = q;
@@ -432,17 +444,14 @@ static int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dt
   a.hkv = cfg->num_kv_heads;
   a.group = group;
   a.variant = cfg->variant;
-  a.chunk = geo.chunk;
-  a.n_split = geo.n_split;
+  a.n_waves = std::min<int64_t>(iq::kMaxDecodeWaves, int64_t(cus) * groups * iq::kDecodeWaves);
   a.qmul = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634 * std::ldexp(1.0, -e));
   a.argmax = track_argmax != 0;
-  a.ws = static_cast<float *>(workspace);
-  // One sequence: split order is already longest first (only the last split
-  // can be short), so the ranking launch is skipped.
-  a.order = batch > 1 && iq::decode_ordered(batch, geo.n_split)
-                ? reinterpret_cast<int2 *>(static_cast<char *>(workspace) +
-                                           iq::decode_order_offset(batch, num_q_heads, geo.n_split, cfg->head_dim))
-                : nullptr;
+  char *ws = static_cast<char *>(workspace);
+  a.plan = reinterpret_cast<iq::DecodePlan *>(ws);
+  a.qrot = reinterpret_cast<uint16_t *>(ws + iq::decode_qrot_offset(batch));
+  a.qscale = reinterpret_cast<float *>(ws + iq::decode_qscale_offset(batch, num_q_heads, cfg->head_dim));
+  a.ws = reinterpret_cast<float *>(ws + iq::decode_record_offset(batch, num_q_heads, cfg->head_dim));
   std::memset(a.lut, 0, sizeof(a.lut));
   fill_pair_table(cfg, e, a.lut);
   return hip_status(iq::launch_decode(cfg->head_dim, cfg->bits, a, stream));
@@ -468,9 +477,10 @@ int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q
   if (!valid_dtype(out_dtype)) return IQ_ERR_UNSUPPORTED;
   if (!aligned16(out)) return IQ_ERR_MISALIGNED;
   if ((lse_out && !aligned16(lse_out)) || (argmax_out && !aligned16(argmax_out))) return IQ_ERR_MISALIGNED;
-  const iq::Geometry geo = iq::decode_geometry(batch, cfg->num_kv_heads, max_kv_len);
+  const char *ws = static_cast<const char *>(workspace);
   iq::MergeArgs m;
-  m.ws = static_cast<const float *>(workspace);
+  m.plan = reinterpret_cast<const iq::DecodePlan *>(ws);
+  m.ws = reinterpret_cast<const float *>(ws + iq::decode_record_offset(batch, num_q_heads, cfg->head_dim));
   m.quats = cfg->quats;
   m.out = out;
   m.out_f16 = out_dtype == IQ_F16;
@@ -478,8 +488,8 @@ int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q
   m.argmax = argmax_out;
   m.batch = batch;
   m.hq = num_q_heads;
+  m.hkv = cfg->num_kv_heads;
   m.group = group;
-  m.n_part = geo.n_split;
   m.oscale = std::ldexp(1.0f, -centroid_exponent(cfg));
   return hip_status(iq::launch_merge(cfg->head_dim, cfg->variant, m, stream));
 }

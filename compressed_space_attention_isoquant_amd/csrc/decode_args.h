@@ -9,18 +9,47 @@
 
 namespace iq {
 
-// Split-K decode.  Each workgroup (4 waves) of the partial kernel covers
-// `chunk` tokens of one (sequence, KV head) and writes one record per query
-// head: running max M (log2 units, biased by the value-norm exponent), the
-// softmax denominator L, the best score and its position, and the unnormalised
-// rotated-space output o~[d].  The merge kernel combines the records of a
-// (sequence, query head) and applies R^T once.
+// Decode attention runs in three launches:
+//
+// prep    one workgroup plans the work (below); the others rotate the
+//         queries once per (sequence, KV head): q~ = R q, scaled, split into
+//         fp16 hi + lo parts (the score product's operand), in the workspace.
+// partial every wave streams its own equal share of the 32-token tiles of all
+//         (sequence, KV head) segments laid end to end (tiles of sequence b,
+//         KV head 0 first, then KV head 1, ..., then sequence b + 1), so that
+//         ragged lengths cost no imbalance.  Where a wave's share crosses a
+//         segment boundary it writes one record per piece: running max M
+//         (log2 units, biased by the value-norm exponent), softmax denominator
+//         L, best score and its position, and the unnormalised rotated-space
+//         output o~[d], per query head of the group.
+// merge   one workgroup per (sequence, query head) combines the records of
+//         its segment's pieces and applies R^T once.
+//
+// Pieces: tile range [w W, (w + 1) W) of wave w meets segment s in at most one
+// piece, stored as record s + w (distinct for every piece that exists: if wave
+// w met segment s and wave w - 1 met segment s + 1, wave w - 1 would end after
+// wave w begins).  Segment s with tiles [S, S + n) has pieces for the waves
+// S / W .. (S + n - 1) / W: a contiguous run of records.
 constexpr int kDecodeWaves = 4;            // waves per partial workgroup
-constexpr int kDecodeStep = 32;            // tokens per wave iteration
+constexpr int kDecodeStep = 32;            // tokens per tile (one wave iteration)
 constexpr int kRecHeader = 4;              // M, L, best score, best position
 constexpr float kLazyTau = 4.0f;           // rescale only when the max grows by more than this
 constexpr float kWeightBias = 25.0f;       // weights 2^(s - M + bias) * ||v|| stay below 2^15
-constexpr int kDecodeRope = 64;            // RoPE coordinates per key the decode kernels take (head_dim 128)
+constexpr int kDecodeRope = 64;            // RoPE coordinates per key the decode kernels take
+constexpr int kMinTilesPerWave = 4;        // a wave's share is at least this many tiles
+constexpr int kMaxDecodeWaves = 4096;      // waves of the partial launch at most (256 CUs x 16)
+constexpr int kPrepThreads = 256;
+
+// Plan written by the prep kernel at the start of the workspace.
+struct DecodePlan {
+  int total;          // tiles of all segments
+  int per_wave;       // W, tiles per wave (the last busy wave may have fewer)
+  int pad_[2];
+  // then: int seg_base[batch + 1] (tile index of segment (b, 0); the last
+  //       entry is total, so sequence b has (seg_base[b + 1] - seg_base[b]) /
+  //       H_kv tiles per KV head), and
+  //       int start_seg[kMaxDecodeWaves] (the segment holding tile w W)
+};
 
 struct DecodeArgs {
   const void *q;           // [batch][Hq][d + rope]
@@ -37,79 +66,52 @@ struct DecodeArgs {
   const float *quats;
   int batch, hq, hkv, group;
   int variant;
-  int chunk;               // tokens per workgroup (multiple of kDecodeWaves * kDecodeStep)
-  int n_split;             // workgroups per (sequence, KV head)
+  int n_waves;             // waves of the partial launch
   float qmul;              // softmax_scale * log2(e) / 2^cexp, applied to R q
   int argmax;              // track the position of the largest score
-  float *ws;               // records [batch][Hq][n_split][d + kRecHeader]
-  // Nullable.  Entry P (workgroup (kvh, P mod batch, P / batch)) holds the
-  // (sequence, split) it processes, (split << 16 | sequence, kv_len), in
-  // longest-first order of the splits' token counts.
-  int2 *order;
+  DecodePlan *plan;        // workspace: plan, segment bases, start segments
+  uint16_t *qrot;          // workspace: [batch][H_kv][2G][d + rope] fp16, hi rows then lo rows
+  float *qscale;           // workspace: [batch][H_kv] 2^-f, the scale of the rows of q~
+  float *ws;               // workspace: records [(batch H_kv + n_waves) G][d + kRecHeader]
   uint32_t lut[256];       // fp16 pairs (c_i 2^cexp | c_k 2^cexp << 16) at index i | k << bits
 };
 
 struct MergeArgs {
   const float *ws;
+  const DecodePlan *plan;
   const float *quats;
   void *out;               // [batch][Hq][d]
   int out_f16;
   float *lse;              // nullable
   int32_t *argmax;         // nullable
-  int batch, hq, group;
-  int n_part;              // records per (sequence, query head)
+  int batch, hq, hkv, group;
   float oscale;            // 2^-cexp
 };
 
-// Workspace of the decode path: the split records, then (256-byte aligned)
-// the workgroup order when batch * n_split is at most kMaxOrderedPairs.
-constexpr int kMaxOrderedPairs = 4096;
-
-inline size_t decode_record_bytes(int32_t batch, int32_t hq, int n_split, int d) {
-  return (size_t)batch * hq * n_split * (d + kRecHeader) * sizeof(float);
+// Workspace layout: the plan (header, segment bases, start segments), the
+// rotated queries (sized for kDecodeRope RoPE coordinates whether or not a
+// call has them), their scales (batch x Hq floats, at least batch x H_kv),
+// the records; each part 256-byte aligned.
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+inline size_t decode_plan_bytes(int32_t batch) {
+  return align256(sizeof(DecodePlan) + sizeof(int) * ((size_t)batch + 1 + kMaxDecodeWaves));
 }
-inline size_t decode_order_offset(int32_t batch, int32_t hq, int n_split, int d) {
-  return (decode_record_bytes(batch, hq, n_split, d) + 255) / 256 * 256;
+inline size_t decode_qrot_bytes(int32_t batch, int32_t hq, int d, int rope) {
+  return align256((size_t)batch * hq * 2 * (d + rope) * sizeof(uint16_t));
 }
-inline bool decode_ordered(int32_t batch, int n_split) {
-  return (int64_t)batch * n_split <= kMaxOrderedPairs;
+inline size_t decode_record_bytes(int32_t batch, int32_t hkv, int32_t hq, int d) {
+  const int group = hq / hkv;
+  return ((size_t)batch * hkv + kMaxDecodeWaves) * group * (d + kRecHeader) * sizeof(float);
 }
-inline size_t decode_workspace_total(int32_t batch, int32_t hq, int n_split, int d) {
-  return decode_ordered(batch, n_split)
-             ? decode_order_offset(batch, hq, n_split, d) + (size_t)batch * n_split * sizeof(int2)
-             : decode_record_bytes(batch, hq, n_split, d);
+inline size_t decode_qrot_offset(int32_t batch) { return decode_plan_bytes(batch); }
+inline size_t decode_qscale_offset(int32_t batch, int32_t hq, int d) {
+  return decode_qrot_offset(batch) + decode_qrot_bytes(batch, hq, d, kDecodeRope);
 }
-
-// Split-K geometry of the decode kernels.  About 2048 workgroups (8 per
-// compute unit, two resident at a time): with ragged context lengths the
-// extra, shorter workgroups even out the compute units' loads.  Chunks are
-// kept at 8192 tokens or more while that still gives 512 workgroups (about
-// one resident round), since each workgroup costs a fixed prologue and
-// epilogue: a few long sequences then run in one round of workgroups instead
-// of several rounds of one-tile ones.  Chunks are whole numbers of
-// (waves x tile) token blocks.
-struct Geometry {
-  int chunk;
-  int n_split;
-};
-
-inline Geometry decode_geometry(int32_t batch, int32_t hkv, int64_t max_kv_len) {
-  const int64_t unit = (int64_t)kDecodeWaves * kDecodeStep;
-  const int64_t T = max_kv_len > 0 ? max_kv_len : 1;
-  const int64_t pairs = (int64_t)batch * hkv;
-  auto chunk_for = [&](int64_t groups) {
-    int64_t want = (groups + pairs - 1) / pairs;
-    if (want < 1) want = 1;
-    return (T + want - 1) / want;
-  };
-  int64_t chunk = chunk_for(2048);
-  const int64_t floor_chunk = std::min<int64_t>(8192, chunk_for(512));
-  if (chunk < floor_chunk) chunk = floor_chunk;
-  chunk = (chunk + unit - 1) / unit * unit;
-  Geometry g;
-  g.chunk = (int)chunk;
-  g.n_split = (int)((T + chunk - 1) / chunk);
-  return g;
+inline size_t decode_record_offset(int32_t batch, int32_t hq, int d) {
+  return decode_qscale_offset(batch, hq, d) + align256((size_t)batch * hq * sizeof(float));
+}
+inline size_t decode_workspace_total(int32_t batch, int32_t hkv, int32_t hq, int d) {
+  return decode_record_offset(batch, hq, d) + decode_record_bytes(batch, hkv, hq, d);
 }
 
 }  // namespace iq

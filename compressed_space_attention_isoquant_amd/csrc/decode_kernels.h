@@ -1,29 +1,32 @@
-// Compressed-space decode attention (RotaryQuant §3.4 Table 2, Appendix A),
-// split-K over the context, scores and value accumulation on fp16 matrix
-// cores (v_mfma_f32_16x16x32_f16) directly from the packed codes.
+// Compressed-space decode attention (RotaryQuant §3.4 Table 2, Appendix A):
+// scores and value accumulation on fp16 matrix cores
+// (v_mfma_f32_16x16x32_f16) directly from the packed codes, the work of a
+// call spread evenly over the waves of one resident round.
 //
-// partial kernel: one workgroup of 4 waves per (split, KV head, sequence);
-//   the order kernel (decode.hip) may assign the (sequence, split) pairs
-//   longest-first.
-//   Prologue: q~ = R q for the G query heads of the KV head (WHT butterflies
-//   and SO(4) blocks in LDS), scaled, split into fp16 hi + lo parts and held
-//   in registers as the B operand of the score product.
-//   The split's 32-token tiles are dealt to the waves round-robin; per tile:
+// prep kernel: workgroup 0 plans the work (DecodePlan, decode_args.h); each
+//   other workgroup rotates the G query heads of one (sequence, KV head):
+//   q~ = R q (WHT butterflies and SO(4) blocks in LDS), scaled, split into
+//   fp16 hi + lo parts, stored as 2G rows (hi rows, then lo rows).
+// partial kernel: every wave owns W consecutive tiles of 32 tokens of the
+//   (sequence, KV head) segments laid end to end; waves never synchronise.
+//   Per tile:
 //     scores  S^T (16 tokens x 16 columns) = C_K (16 x d) . Q~^T (d x 16) for
 //             two 16-token tiles; column j < G holds q~_hi of head j, column
 //             G + j holds q~_lo of head j, so S_hi + S_lo is the full-precision
 //             score.  C_K comes from the packed K rows through a 2-code table
-//             of exact fp16 centroid pairs (the codebook has 11 significant
-//             bits, scaled by a power of two).
+//             of exact fp16 centroid pairs (each level times 2^e is an fp16
+//             number), read by lane permutation (ds_bpermute) from a register
+//             holding the table at 2 and 3 bits, from LDS at 4 bits.
 //     softmax online, base 2, with a lazily raised running maximum (only
 //             rescaled when a score exceeds it by more than kLazyTau).
 //     values  O~ (16 rows x d) += P (16 x 32 tokens) . C_V (32 x d); row j < G
 //             carries the fp16 hi part of p * ||v|| for head j, row G + j the
 //             lo part, so the fp32 accumulators see the weights to ~2^-22.
-//   The 4 waves merge their states in LDS; the workgroup writes one partial
-//   record (M, L, best score, best position, o~[d]) per query head.
-// merge kernel: one workgroup per (query head, sequence): combines the split
-//   records, divides by the softmax denominator and applies R^T once.
+//   At the end of a segment or of its share the wave writes one record
+//   (M, L, best score, best position, o~[d]) per query head.
+// merge kernel: one workgroup per (query head, sequence): combines the records
+//   of the segment's pieces, divides by the softmax denominator and applies
+//   R^T once.
 #pragma once
 
 #include <type_traits>
@@ -205,56 +208,187 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Replicas of the code-pair table in LDS: lane l reads replica l % REPL
-// (entry e at dword e * REPL + l % REPL), so that a wave's table reads fall
-// in distinct banks whatever the codes are.
-template <int BITS>
-constexpr int lut_repl() {
-  return BITS <= 3 ? 32 : 8;
+// Lane permutation: the value that lane (addr / 4) mod 64 holds in v (the
+// address's bits above 7 and below 2 are ignored).
+__device__ __forceinline__ uint32_t bpermute(uint32_t addr, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)addr, (int)v);
 }
 
-template <int N>
-constexpr int ilog2() {
-  return N <= 1 ? 0 : 1 + ilog2<N / 2>();
+// Where the code-pair table lives: at 2 and 3 bits (16 and 64 pairs) in one
+// register, lane e holding entry e mod 2^(2b), read by lane permutation, so
+// that an entry's address is the pair's bit field anywhere in bits 2..7; at 4
+// bits (256 pairs) in LDS, replicated 8 times so that a wave's reads fall in
+// distinct banks whatever the codes (lane l reads replica l mod 8).
+template <int BITS>
+constexpr bool pair_table_in_register() {
+  return BITS <= 3;
+}
+template <int BITS>
+constexpr int lds_table_bytes() {
+  return pair_table_in_register<BITS>() ? 0 : (1 << (2 * BITS)) * 8 * 4;
 }
 
 // LDS layout: workgroups per CU (each holds one wave per SIMD) and stages
-// per wave.  Three workgroups per CU where each can still keep 3 stages per
-// wave next to its pair table and `extra` bytes (more waves hide latency
-// better than a deeper ring), else two where each keeps 2 stages, else one;
-// then as many stages as fit, up to 4, at least 2 (double buffering).
+// per wave.  Three workgroups per CU where each can keep 3 stages per wave
+// (more waves hide latency better than a deeper ring), else two where each
+// keeps 2 stages, else one; then as many stages as fit, up to 4, at least 2
+// (double buffering).
 template <int D, int BITS, int ROPE = 0>
-constexpr int stages_fitting(int budget, int extra) {
-  const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
-  return (budget - table - extra) / (kDecodeWaves * Stage<D, BITS, ROPE>::BYTES);
+constexpr int stages_fitting(int budget) {
+  return (budget - lds_table_bytes<BITS>()) / (kDecodeWaves * Stage<D, BITS, ROPE>::BYTES);
 }
 
 template <int D, int BITS, int ROPE = 0>
-constexpr int resident_groups(int extra) {
-  return stages_fitting<D, BITS, ROPE>(160 * 1024 / 3, extra) >= 3   ? 3
-         : stages_fitting<D, BITS, ROPE>(160 * 1024 / 2, extra) >= 2 ? 2
-                                                                     : 1;
+constexpr int resident_groups() {
+  return stages_fitting<D, BITS, ROPE>(160 * 1024 / 3) >= 3   ? 3
+         : stages_fitting<D, BITS, ROPE>(160 * 1024 / 2) >= 2 ? 2
+                                                               : 1;
 }
 
 template <int D, int BITS, int ROPE = 0>
-constexpr int stage_count(int extra) {
-  const int n = stages_fitting<D, BITS, ROPE>(160 * 1024 / resident_groups<D, BITS, ROPE>(extra), extra);
+constexpr int stage_count() {
+  const int n = stages_fitting<D, BITS, ROPE>(160 * 1024 / resident_groups<D, BITS, ROPE>());
   return n > 4 ? 4 : (n < 2 ? 2 : n);
 }
 
 // Waves per SIMD the register allocation is held to, matching the LDS
 // layout: three where three workgroups share a CU (at most 168 registers per
 // lane), two where the LDS of two fits (head_dim <= 256; 256 registers),
-// else no constraint.
-template <int D, int BITS, int ROPE = 0>
-constexpr int partial_waves(int extra) {
-  const int table = (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
-  const int lds = table + extra + kDecodeWaves * stage_count<D, BITS, ROPE>(extra) * Stage<D, BITS, ROPE>::BYTES;
-  return resident_groups<D, BITS, ROPE>(extra) == 3 ? 3 : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
+// else no constraint.  Tracking the argmax needs more registers than 168:
+// those instantiations run two waves per SIMD.
+template <int D, int BITS, int ROPE = 0, bool ARGMAX = false>
+constexpr int partial_waves() {
+  const int lds = lds_table_bytes<BITS>() + kDecodeWaves * stage_count<D, BITS, ROPE>() * Stage<D, BITS, ROPE>::BYTES;
+  const int w = resident_groups<D, BITS, ROPE>() == 3 ? 3 : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
+  return ARGMAX && w > 2 ? 2 : w;
 }
 
+// ---------------------------------------------------------------------------
+// prep kernel
+// ---------------------------------------------------------------------------
+
+// Workgroup 0: tiles per segment, their prefix over the sequences (segment
+// (b, h) starts at seg_base[b] + h * tiles(b)), the per-wave share W and, for
+// every busy wave w, the segment holding its first tile w W.
+__device__ void plan_work(const DecodeArgs &a) {
+  __shared__ int part[kPrepThreads];
+  int *seg_base = reinterpret_cast<int *>(a.plan + 1);
+  int *start_seg = seg_base + a.batch + 1;
+  const int t = threadIdx.x;
+  const int per = (a.batch + kPrepThreads - 1) / kPrepThreads;
+  const int b0 = min(a.batch, t * per), b1 = min(a.batch, b0 + per);
+  auto tiles = [&](int b) { return (a.kv_len[b] + kDecodeStep - 1) / kDecodeStep; };
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) mine += a.hkv * tiles(b);
+  part[t] = mine;
+  __syncthreads();
+  // inclusive scan of the per-thread sums (Hillis-Steele)
+  for (int off = 1; off < kPrepThreads; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  const int total = part[kPrepThreads - 1];
+  const int W = max(kMinTilesPerWave, (total + a.n_waves - 1) / a.n_waves);
+  int base = part[t] - mine;
+  for (int b = b0; b < b1; ++b) {
+    const int n = tiles(b);
+    seg_base[b] = base;
+    for (int h = 0; h < a.hkv && n > 0; ++h) {
+      const int s0 = base + h * n;
+      for (int w = (s0 + W - 1) / W; w * W < s0 + n; ++w) start_seg[w] = b * a.hkv + h;
+    }
+    base += a.hkv * n;
+  }
+  if (t == 0) {
+    a.plan->total = total;
+    a.plan->per_wave = W;
+    seg_base[a.batch] = total;
+  }
+}
+
+// Other workgroups: q~ for the G query heads of (sequence, KV head) r.
+template <int D, int ROPE, int G>
+__device__ void rotate_queries(const DecodeArgs &a, int r) {
+  static_assert(kPrepThreads == 256, "four waves");
+  constexpr int DQ = D + ROPE;
+  __shared__ float qs[G][DQ];
+  const int b = r / a.hkv, kvh = r - b * a.hkv;
+  for (int idx = threadIdx.x; idx < G * DQ; idx += kPrepThreads) {
+    const int hh = idx / DQ, i = idx % DQ;
+    const size_t off = ((size_t)b * a.hq + kvh * G + hh) * DQ + i;
+    qs[hh][i] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[off])
+                        : static_cast<const float *>(a.q)[off];
+  }
+  __syncthreads();
+  for (int st = 1; st < D; st <<= 1) {
+    for (int p = threadIdx.x; p < G * D / 2; p += kPrepThreads) {
+      const int hh = p / (D / 2), pp = p % (D / 2);
+      const int i = (pp / st) * 2 * st + (pp % st);
+      const float x0 = qs[hh][i], x1 = qs[hh][i + st];
+      qs[hh][i] = x0 + x1;
+      qs[hh][i + st] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  const float scale = a.qmul / sqrtf((float)D);
+  const float *pg = a.quats + (size_t)kvh * (D / 4) * block_param_floats(a.variant);
+  for (int p = threadIdx.x; p < G * D / 4; p += kPrepThreads) {
+    const int hh = p / (D / 4), blk = p % (D / 4);
+    float4 v = make_float4(qs[hh][4 * blk] * scale, qs[hh][4 * blk + 1] * scale, qs[hh][4 * blk + 2] * scale,
+                           qs[hh][4 * blk + 3] * scale);
+    float4 t = a.variant == 0 ? block_fwd<0>(v, pg, blk)
+               : a.variant == 1 ? block_fwd<1>(v, pg, blk) : block_fwd<kPlanar>(v, pg, blk);
+    qs[hh][4 * blk] = t.x;
+    qs[hh][4 * blk + 1] = t.y;
+    qs[hh][4 * blk + 2] = t.z;
+    qs[hh][4 * blk + 3] = t.w;
+  }
+  for (int idx = threadIdx.x; idx < G * ROPE; idx += kPrepThreads) {
+    const int hh = idx / (ROPE > 0 ? ROPE : 1), i = D + idx % (ROPE > 0 ? ROPE : 1);
+    qs[hh][i] *= a.rmul;
+  }
+  __syncthreads();
+  // Power-of-two scale 2^f bringing the largest |q~| into [2^13, 2^14): the
+  // fp16 hi and lo parts then hold every coordinate down to 2^-17 of the
+  // largest to 22 bits (unscaled, the small coordinates' lo parts fall into
+  // the fp16 subnormals and lose most of their bits); the partial kernel
+  // works in scores times 2^f and applies 2^-f where it needs true units.
+  __shared__ float redm[kPrepThreads / 64];
+  float m = 0.f;
+  for (int idx = threadIdx.x; idx < G * DQ; idx += kPrepThreads) m = fmaxf(m, fabsf(qs[idx / DQ][idx % DQ]));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) redm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+  const int f = m > 0.f ? 13 - ilogbf(m) : 0;
+  const float up = ldexpf(1.f, f);
+  _Float16 *dst = reinterpret_cast<_Float16 *>(a.qrot) + (size_t)r * 2 * G * DQ;
+  for (int idx = threadIdx.x; idx < G * DQ; idx += kPrepThreads) {
+    const int hh = idx / DQ, i = idx % DQ;
+    const float v = qs[hh][i] * up;
+    const _Float16 hi = static_cast<_Float16>(v);
+    dst[hh * DQ + i] = hi;
+    dst[(G + hh) * DQ + i] = static_cast<_Float16>(v - static_cast<float>(hi));
+  }
+  if (threadIdx.x == 0) a.qscale[r] = ldexpf(1.f, -f);
+}
+
+template <int D, int ROPE, int G>
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(DecodeArgs a) {
+  if (blockIdx.x == 0)
+    plan_work(a);
+  else
+    rotate_queries<D, ROPE, G>(a, (int)blockIdx.x - 1);
+}
+
+// ---------------------------------------------------------------------------
+// partial kernel
+// ---------------------------------------------------------------------------
+
 template <int D, int BITS, int G, bool ARGMAX, int ROPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(partial_waves<D, BITS, ROPE>(G * (D + ROPE) * 4))))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(partial_waves<D, BITS, ROPE, ARGMAX>())))
 void partial_kernel(DecodeArgs a) {
   constexpr int NLEV = 1 << BITS;
   constexpr int KS = D / 32;                 // k-steps of the score product
@@ -273,61 +407,64 @@ void partial_kernel(DecodeArgs a) {
   constexpr int VX = (VCB + 31) / 32;        // dwords after extraction
   constexpr int NROW = 2 * G;                // live rows/columns (hi + lo)
   using S = Stage<D, BITS, ROPE>;
-  constexpr int RK = ROPE / 32;                                     // k-steps of the RoPE score product
-  constexpr int DQ = D + ROPE;                                      // query coordinates
-  constexpr int PRO_B = G * DQ * 4;                                 // prologue q~ staging
-  constexpr int NST = stage_count<D, BITS, ROPE>(PRO_B);
+  constexpr int RK = ROPE / 32;              // k-steps of the RoPE score product
+  constexpr int DQ = D + ROPE;               // query coordinates
+  constexpr int NST = stage_count<D, BITS, ROPE>();
   static_assert((NST - 1) * S::LOADS < 64, "in-flight loads exceed the vmcnt range");
-  constexpr int STG_B = kDecodeWaves * NST * S::BYTES;              // ring of stages per wave
-  constexpr int RED_B = kDecodeWaves * G * (D + 4) * 4;             // wave states at the end
-  constexpr int MAIN_B = STG_B > RED_B ? STG_B : RED_B;
+  constexpr bool REG_TABLE = pair_table_in_register<BITS>();
+  constexpr int TB = lds_table_bytes<BITS>();
 
-  // Grid (KV head, rank): workgroups are handed to the 8 dies (XCDs) in turn
-  // by linear index, KV head fastest, so every die gets an even mix.  With an
-  // order table (a.order) rank P runs the (sequence, split) of P-th most
-  // tokens, so each die works longest-first; without one, rank
-  // (sequence + batch * split) runs that pair (first splits, the fullest,
-  // first).
-  const int kvh = blockIdx.x;
-  int b, split, T;
-  if (a.order) {
-    const int2 o = a.order[blockIdx.y + gridDim.y * blockIdx.z];
-    b = __builtin_amdgcn_readfirstlane(o.x & 0xffff);
-    split = __builtin_amdgcn_readfirstlane(o.x >> 16);
-    T = __builtin_amdgcn_readfirstlane(o.y);
-  } else {
-    b = blockIdx.y;
-    split = blockIdx.z;
-    T = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
-  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  constexpr int REPL = lut_repl<BITS>();
-  constexpr int LSH = ilog2<REPL * 4>();     // table entry -> byte offset shift
-  // aligned to its own size, so that the entry offset can be OR-ed into the
-  // lane's replica offset (pair below)
-  __shared__ __attribute__((aligned(NLEV * NLEV * REPL * 4))) uint32_t lut[NLEV * NLEV * REPL];
-  __shared__ __attribute__((aligned(16))) char smem[MAIN_B];
-  // q~ staging in LDS of its own where it fits (then the first stages load
-  // during the prologue), else in the stage memory (loads after it)
-  constexpr bool EARLY = MAIN_B + NLEV * NLEV * REPL * 4 + PRO_B <= 160 * 1024;
-  __shared__ float qs_own[EARLY ? G : 1][EARLY ? DQ : 1];
-  float (*qs)[DQ] = EARLY ? reinterpret_cast<float (*)[DQ]>(&qs_own[0][0]) : reinterpret_cast<float (*)[DQ]>(smem);
+  // the code-pair table: one register (entry lane mod 2^(2b)), or LDS replicas
+  __shared__ __attribute__((aligned(TB > 0 ? TB : 4))) uint32_t lut[TB > 0 ? TB / 4 : 1];
+  __shared__ __attribute__((aligned(16))) char smem[kDecodeWaves * NST * S::BYTES];
+  uint32_t tbl = 0;
+  if constexpr (REG_TABLE) {
+    tbl = a.lut[lane & (NLEV * NLEV - 1)];
+  } else {
+    for (int i = threadIdx.x; i < TB / 4; i += kThreads) lut[i] = a.lut[i / 8];
+    __syncthreads();                         // the kernel's only barrier: before any wave leaves
+  }
 
-  // The workgroup's tokens [base, end) are dealt to the waves tile by tile
-  // (tile i to wave i mod 4), so that its waves finish together whatever the
-  // length: the workgroup holds its compute unit until its slowest wave ends.
-  const int base = split * a.chunk;
-  const int end = min(T, base + a.chunk);
-  const int len = end > base ? end - base : 0;
-  auto tile_t0 = [&](int k) { return base + (wave + kDecodeWaves * k) * kDecodeStep; };
-  const long long hrow = (long long)b * a.hkv + kvh;
-  const int32x4_t kr = make_rsrc(a.kc + hrow * a.kcap * ROWB, (uint32_t)(a.kcap * ROWB));
-  const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
-  const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
-  const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
-  const int32x4_t rr = ROPE ? make_rsrc(a.krope + hrow * a.kcap * ROPE, (uint32_t)(a.kcap * ROPE * 2)) : kr;
+  // this wave's share of the tiles: [t_begin, t_end)
+  const int w = (int)blockIdx.x * kDecodeWaves + wave;
+  const int total = a.plan->total, W = a.plan->per_wave;
+  const int t_begin = w * W;
+  if (t_begin >= total) return;
+  const int t_end = min(total, t_begin + W);
+  const int *seg_base = reinterpret_cast<const int *>(a.plan + 1);
+  const int *start_seg = seg_base + a.batch + 1;
+
+  // A position in the tile sequence: sequence b, KV head h, tile i of the
+  // segment's n tiles (len tokens).  Wave-uniform.
+  struct Cursor {
+    int b, h, i, n, len;
+  };
+  auto seq_len = [&](int b) { return __builtin_amdgcn_readfirstlane(a.kv_len[b]); };
+  Cursor c0;
+  {
+    const int s = __builtin_amdgcn_readfirstlane(start_seg[w]);
+    c0.b = s / a.hkv;
+    c0.h = s - c0.b * a.hkv;
+    c0.len = seq_len(c0.b);
+    c0.n = (c0.len + kDecodeStep - 1) / kDecodeStep;
+    c0.i = t_begin - (__builtin_amdgcn_readfirstlane(seg_base[c0.b]) + c0.h * c0.n);
+  }
+  // the next tile (one exists whenever this is called)
+  auto advance = [&](Cursor &c) {
+    if (++c.i < c.n) return;
+    c.i = 0;
+    if (++c.h < a.hkv) return;
+    c.h = 0;
+    do {
+      ++c.b;
+      c.len = seq_len(c.b);
+    } while (c.len == 0);
+    c.n = (c.len + kDecodeStep - 1) / kDecodeStep;
+  };
+
   char *stages = smem + wave * NST * S::BYTES;
   const uint32_t stages_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(stages));
   uint32_t goff[S::ROW_LOADS];
@@ -336,57 +473,17 @@ void partial_kernel(DecodeArgs a) {
   uint32_t groff[S::R_LOADS > 0 ? S::R_LOADS : 1];
 #pragma unroll
   for (int c = 0; c < S::R_LOADS; ++c) groff[c] = rope_granule_offset<D, BITS, ROPE>(c, lane);
-  // this wave's tiles k = 0, 1, ...: workgroup tiles wave + 4k
-  auto count = [&](int tiles) { return tiles > wave ? (tiles - wave + kDecodeWaves - 1) / kDecodeWaves : 0; };
-  const int n_tiles = count((len + kDecodeStep - 1) / kDecodeStep);
-  const int n_full = count(len / kDecodeStep);
-  // The first NST - 1 stages are requested before the prologue, whose work
-  // then overlaps their memory latency.
-  auto first_stages = [&] {
-    if (n_tiles > 0) {
-#pragma unroll
-      for (int i = 0; i < NST - 1; ++i)
-        load_stage<D, BITS, ROPE>(stages_lds + i * S::BYTES, kr, vr, knr, vnr, rr, tile_t0(i), i < n_tiles, lane,
-                                  goff, groff);
-    }
+  // loads of the stage of tile c (out of range when !valid) into ring slot
+  auto issue = [&](const Cursor &c, bool valid, int slot) {
+    const long long hrow = (long long)c.b * a.hkv + c.h;
+    const int32x4_t kr = make_rsrc(a.kc + hrow * a.kcap * ROWB, (uint32_t)(a.kcap * ROWB));
+    const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
+    const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
+    const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
+    const int32x4_t rr = ROPE ? make_rsrc(a.krope + hrow * a.kcap * ROPE, (uint32_t)(a.kcap * ROPE * 2)) : kr;
+    load_stage<D, BITS, ROPE>(stages_lds + slot * S::BYTES, kr, vr, knr, vnr, rr, c.i * kDecodeStep, valid, lane,
+                              goff, groff);
   };
-  if constexpr (EARLY) first_stages();
-
-  // ---- prologue: q~ = R q for this KV head's query heads --------------------
-  for (int i = threadIdx.x; i < NLEV * NLEV * REPL; i += kThreads) lut[i] = a.lut[i / REPL];
-  for (int idx = threadIdx.x; idx < G * DQ; idx += kThreads) {
-    const int hh = idx / DQ, i = idx % DQ;
-    const size_t off = ((size_t)b * a.hq + kvh * G + hh) * DQ + i;
-    qs[hh][i] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[off])
-                        : static_cast<const float *>(a.q)[off];
-  }
-  __syncthreads();
-  for (int st = 1; st < D; st <<= 1) {
-    for (int p = threadIdx.x; p < G * D / 2; p += kThreads) {
-      const int hh = p / (D / 2), pp = p % (D / 2);
-      const int i = (pp / st) * 2 * st + (pp % st);
-      const float x0 = qs[hh][i], x1 = qs[hh][i + st];
-      qs[hh][i] = x0 + x1;
-      qs[hh][i + st] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  {
-    const float scale = a.qmul / sqrtf((float)D);
-    const float *pg = a.quats + (size_t)kvh * (D / 4) * block_param_floats(a.variant);
-    for (int p = threadIdx.x; p < G * D / 4; p += kThreads) {
-      const int hh = p / (D / 4), blk = p % (D / 4);
-      float4 v = make_float4(qs[hh][4 * blk] * scale, qs[hh][4 * blk + 1] * scale,
-                             qs[hh][4 * blk + 2] * scale, qs[hh][4 * blk + 3] * scale);
-      float4 t = a.variant == 0 ? block_fwd<0>(v, pg, blk)
-                 : a.variant == 1 ? block_fwd<1>(v, pg, blk) : block_fwd<kPlanar>(v, pg, blk);
-      qs[hh][4 * blk] = t.x;
-      qs[hh][4 * blk + 1] = t.y;
-      qs[hh][4 * blk + 2] = t.z;
-      qs[hh][4 * blk + 3] = t.w;
-    }
-  }
-  __syncthreads();
 
   const int j = lane & 15;      // column of the score tile / row of the value operand
   const int g4 = lane >> 4;     // lane group: k-slice of the operands, row quad of results
@@ -394,39 +491,37 @@ void partial_kernel(DecodeArgs a) {
   const bool lo_lane = live && j >= G;
   const int head = j % G;
 
-  // B operand of the score product: k-step s of lane group g4 holds dims
-  // 8 (s mod SPU) .. +7 of row unit 4 (s / SPU) + g4 (the dims the K operand
-  // carries at the same k positions).
+  // B operands of the score products, from the prep kernel's rows: k-step s
+  // of lane group g4 holds dims 8 (s mod SPU) .. +7 of row unit 4 (s / SPU) +
+  // g4 (the dims the K operand carries at the same k positions); RoPE k-step
+  // s holds RoPE coordinates 32 s + 8 g4 .. +7.  Lanes past the live columns
+  // hold zeros.
   half8 qB[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dim = (4 * (s / SPU) + g4) * (8 * SPU) + 8 * (s % SPU) + e;
-      const float v = live ? qs[head][dim] : 0.f;
-      const _Float16 hi = static_cast<_Float16>(v);
-      qB[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
-    }
-  }
-  // B operand of the RoPE score product: k-step s of lane group g4 holds RoPE
-  // coordinates 32 s + 8 g4 .. +7 (the natural order of the RoPE rows), times
-  // softmax_scale * log2(e), hi and lo fp16 parts as for qB.
   half8 qR[RK > 0 ? RK : 1];
+  // the segment's query scale 2^-f: scores s' = 2^f s (log2 units) come out
+  // of the products; the running maximum and its threshold stay in those
+  // units, the weights and the record's maximum are taken back to true ones
+  float qsc = 1.f, tau_s = kLazyTau, q4 = 0.25f;
+  auto load_query = [&](const Cursor &c) {
+    qsc = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                        __builtin_bit_cast(int, a.qscale[c.b * a.hkv + c.h])));
+    tau_s = kLazyTau / qsc;
+    q4 = 0.25f / qsc;
+    const _Float16 *row = reinterpret_cast<const _Float16 *>(a.qrot) +
+                          (((size_t)c.b * a.hkv + c.h) * 2 * G + (live ? j : 0)) * DQ;
 #pragma unroll
-  for (int s = 0; s < RK; ++s) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = live ? qs[head][D + 32 * s + 8 * g4 + e] * a.rmul : 0.f;
-      const _Float16 hi = static_cast<_Float16>(v);
-      qR[s][e] = lo_lane ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
+    for (int s = 0; s < KS; ++s) {
+      const int dim = (4 * (s / SPU) + g4) * (8 * SPU) + 8 * (s % SPU);
+      const half8 v = *reinterpret_cast<const half8 *>(row + dim);
+      qB[s] = live ? v : half8{};
     }
-  }
-  if constexpr (!EARLY) {
-    __syncthreads();                         // qs is reused as stage memory
-    first_stages();
-  }
+#pragma unroll
+    for (int s = 0; s < RK; ++s) {
+      const half8 v = *reinterpret_cast<const half8 *>(row + D + 32 * s + 8 * g4);
+      qR[s] = live ? v : half8{};
+    }
+  };
 
-  // ---- main loop ---------------------------------------------------------------
   const int my_tile = lo_lane ? 1 : 0;
   const int vbit = VCB * j;                  // bit offset of this lane's codes in a row
   const float lo_mask = lo_lane ? 1.f : 0.f;
@@ -434,28 +529,44 @@ void partial_kernel(DecodeArgs a) {
   const int k_off = S::K_OFF + j * S::RS + g4 * UDW * 4;
   const int v_off = S::V_OFF + 4 * g4 * S::RS + (vbit >> 5) * 4;
   const int n_off = (16 * my_tile + 4 * g4) * 2;
-  // byte address of this lane's replica of table entry 0
-  const uint32_t lut_base = lds_addr(lut) | (uint32_t)(lane % REPL) * 4u;
-  // table entry at the 2*BITS-bit field at bit `pos` of w: the field is
-  // shifted to bit LSH and masked, and the lane's replica offset OR-ed in
-  // (the table is aligned to its size): a shift and one three-input bit
-  // operation, or the bit operation alone where pos = LSH
+  constexpr int LSH = REG_TABLE ? 2 : 5;     // bit position the pair field must reach
+  const uint32_t lut_base = REG_TABLE ? 0u : (lds_addr(lut) | (uint32_t)(lane & 7) * 4u);
+  // table entry of the 2*BITS-bit field at bit `pos` of w (any bits above
+  // the field are ignored by the lane permutation; the LDS table masks them)
   auto pair = [&](uint32_t w, auto pos) -> uint32_t {
     constexpr int P = decltype(pos)::value;
-    constexpr uint32_t M = ((1u << (2 * BITS)) - 1u) << LSH;
     const uint32_t f = P >= LSH ? (w >> (P - LSH)) : (w << (LSH - P));
-    const uint32_t addr = (f & M) | lut_base;
-    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
+    if constexpr (REG_TABLE) {
+      return bpermute(f, tbl);
+    } else {
+      constexpr uint32_t M = ((1u << (2 * BITS)) - 1u) << LSH;
+      const uint32_t addr = (f & M) | lut_base;
+      return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
+    }
   };
 
-  float Mh = -INFINITY, Mb = -INFINITY, Lh = 0.f, best_s = -INFINITY;
-  int best_j = -1;
+  float Mh, Mb, Lh, best_s;
+  int best_j;
   floatx4 O[NB];
+  auto reset = [&] {
+    Mh = -INFINITY;
+    Mb = -INFINITY;
+    Lh = 0.f;
+    best_s = -INFINITY;
+    best_j = -1;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
 
-  auto process = [&](const char *cur, const int t0, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  // this lane's token of the tile for score row r is 16 my_tile + 4 g4 + r;
+  // lanes of dead columns take no token (their scores stay -inf)
+  const int tok0 = live ? 16 * my_tile + 4 * g4 : (1 << 30);
+
+  // One 32-token tile from stage `cur`: tokens t0 .. t0 + 31 of a segment of
+  // `end` tokens (those at and past `end`, in a segment's last tile, are
+  // masked).  One code path for full and partial tiles: a second inlined
+  // copy of this body for the partial tile would not fit the register budget.
+  auto process = [&](const char *cur, const int t0, const int end) {
     // packed K rows of the two 16-token tiles (lane: token j, dims slice g4)
     uint32_t kw[2][CW];
 #pragma unroll
@@ -481,7 +592,7 @@ void partial_kernel(DecodeArgs a) {
     const u16x4 kb = *reinterpret_cast<const u16x4 *>(cur + S::KN_OFF + n_off);
     const u16x4 vb = *reinterpret_cast<const u16x4 *>(cur + S::VN_OFF + n_off);
 
-    // Table reads for both operands are issued up front, so that their LDS
+    // Table reads for both operands are issued up front, so that their
     // latency overlaps the score products and the softmax.
     // K operand: lane (token j, dims slice g4), k-step s holds dims 8s..8s+7
     // of the slice as 4 code pairs.
@@ -490,15 +601,15 @@ void partial_kernel(DecodeArgs a) {
     for (int tile = 0; tile < 2; ++tile) {
       static_for<KS>([&](auto s) {
         static_for<4>([&](auto p) {
-          constexpr int W = 2 * BITS;
+          constexpr int Wd = 2 * BITS;
           constexpr int sv = decltype(s)::value;
           constexpr int pos = (sv / SPU) * UDW * 32 + (8 * (sv % SPU) + 2 * decltype(p)::value) * BITS;
           constexpr int wd = pos >> 5, off = pos & 31;
-          if constexpr (off + W <= 32 || wd + 1 >= CW)
+          if constexpr (off + Wd <= 32 || wd + 1 >= CW)
             ka[tile][s][p] = pair(kw[tile][wd], std::integral_constant<int, off>{});
           else {
             // a pair across two dwords: the funnel shift also moves the field
-            // to bit LSH, where the table offset wants it
+            // to bit LSH, where the table read wants it
             static_assert(off >= LSH, "straddling field below the table shift");
             ka[tile][s][p] = pair(__builtin_amdgcn_alignbit(kw[tile][wd + 1], kw[tile][wd], off - LSH),
                                   std::integral_constant<int, LSH>{});
@@ -584,14 +695,9 @@ void partial_kernel(DecodeArgs a) {
         const float rgive = my_tile ? SR[0][r] : SR[1][r];
         c += rown + xor_g<G>(rgive);
       }
-      if constexpr (!FULL) {
-        const int tok = t0 + 16 * my_tile + 4 * g4 + r;
-        c = (live && tok < end) ? c : -INFINITY;
-      } else {
-        c = live ? c : -INFINITY;
-      }
+      c = tok0 + r < end - t0 ? c : -INFINITY;
       sig[r] = c;
-      u[r] = fmaf((float)((vb[r] >> 8) & 0xFF), 0.25f, c);
+      u[r] = fmaf((float)((vb[r] >> 8) & 0xFF), q4, c);
     }
     if constexpr (ARGMAX) {
 #pragma unroll
@@ -603,15 +709,15 @@ void partial_kernel(DecodeArgs a) {
       }
     }
     const float lmax = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-    if (__any(lmax > Mh + kLazyTau)) {
+    if (__any(lmax > Mh + tau_s)) {
       float umax = fmaxf(lmax, xor_g<G>(lmax));
       umax = fmaxf(umax, __shfl_xor(umax, 16, 64));
       umax = fmaxf(umax, __shfl_xor(umax, 32, 64));
       const float mnew = fmaxf(Mh, umax);
-      const float alpha = (Mh == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mh - mnew);
+      const float alpha = (Mh == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Mh - mnew) * qsc);
       Lh *= alpha;
       Mh = mnew;
-      Mb = mnew - kWeightBias;
+      Mb = mnew * qsc - kWeightBias;
       // rows 4*g4 + i of the value accumulators belong to head (4*g4 + i) % G
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -624,7 +730,7 @@ void partial_kernel(DecodeArgs a) {
     float y[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float x = __builtin_amdgcn_exp2f(sig[r] - Mb);   // 2^(s - M + bias); 0 for masked tokens
+      const float x = __builtin_amdgcn_exp2f(fmaf(sig[r], qsc, -Mb));   // 2^(s - M + bias); 0 for masked tokens
       Lh += x;
       y[r] = live ? x * half_bits_to_float(vb[r]) : 0.f;
     }
@@ -660,117 +766,126 @@ void partial_kernel(DecodeArgs a) {
                                                      O[nb], 0, 0, 0);
   };
 
-  // Ring of NST stages per wave: the next NST - 1 tiles are in flight while
-  // one is processed.  Every iteration issues one stage (out of range past
-  // the wave's last tile), so one fixed wait finds the oldest stage landed.
-  if (n_tiles > 0) {
-    int slot = 0;                            // stage of tile `it`
-    for (int it = 0; it < n_full; ++it) {
-      const int ahead = it + NST - 1;
-      const int aslot = slot == 0 ? NST - 1 : slot - 1;     // (it + NST - 1) mod NST, processed last iteration
-      load_stage<D, BITS, ROPE>(stages_lds + aslot * S::BYTES, kr, vr, knr, vnr, rr, tile_t0(ahead), ahead < n_tiles,
-                                lane, goff, groff);
-      wait_vmem<(NST - 1) * S::LOADS>();
-      process(stages + slot * S::BYTES, tile_t0(it), std::true_type{});
-      slot = slot == NST - 1 ? 0 : slot + 1;
+  // The record of the piece of segment (c.b, c.h) this wave has covered: per
+  // query head the softmax state and o~ (hi + lo rows added), straight from
+  // registers.  Record index: segment + wave.
+  auto write_record = [&](const Cursor &c) {
+    float lsum = live ? Lh : 0.f;
+    lsum += xor_g<G>(lsum);
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    float bs = live ? best_s : -INFINITY;
+    int bj = live ? best_j : -1;
+    if constexpr (ARGMAX) {
+      // the larger score; on equal scores the lower position
+      auto take = [&](float os, int oj) {
+        if (os > bs || (os == bs && oj >= 0 && (bj < 0 || oj < bj))) {
+          bs = os;
+          bj = oj;
+        }
+      };
+      take(xor_g<G>(bs), __builtin_bit_cast(int, xor_g<G>(__builtin_bit_cast(float, bj))));
+      take(__shfl_xor(bs, 16, 64), __shfl_xor(bj, 16, 64));
+      take(__shfl_xor(bs, 32, 64), __shfl_xor(bj, 32, 64));
     }
-    wait_vmem<0>();                          // also drains the out-of-range stages before LDS is reused
-    if (n_full < n_tiles)                    // the last, partial tile
-      process(stages + slot * S::BYTES, tile_t0(n_full), std::false_type{});
-  }
-  __syncthreads();                           // stage memory is reused for the wave states below
-  float (*red_o)[G][D + 4] = reinterpret_cast<float (*)[G][D + 4]>(smem);
-
-  // ---- wave state -> LDS -----------------------------------------------------------
-  // softmax denominator and argmax per head: lanes (head, head + G) x 4 groups
-  float lsum = live ? Lh : 0.f;
-  lsum += xor_g<G>(lsum);
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  float bs = live ? best_s : -INFINITY;
-  int bj = live ? best_j : -1;
-  {
-    auto take = [&](float os, int oj) {
-      if (os > bs || (os == bs && oj >= 0 && (bj < 0 || oj < bj))) {
-        bs = os;
-        bj = oj;
-      }
-    };
-    take(xor_g<G>(bs), __builtin_bit_cast(int, xor_g<G>(__builtin_bit_cast(float, bj))));
-    take(__shfl_xor(bs, 16, 64), __shfl_xor(bj, 16, 64));
-    take(__shfl_xor(bs, 32, 64), __shfl_xor(bj, 32, 64));
-  }
-  if (lane < G) {
-    red_o[wave][lane][D + 0] = Mh;
-    red_o[wave][lane][D + 1] = lsum;
-    red_o[wave][lane][D + 2] = bs;
-    red_o[wave][lane][D + 3] = __builtin_bit_cast(float, bj);
-  }
-  // value rows: hi row h + lo row h + G
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+    const long long piece = (long long)c.b * a.hkv + c.h + w;
+    float *rec = a.ws + piece * G * (D + kRecHeader);
+    // (the best score stays in the segment's scaled units: the merge only
+    // compares the pieces of one segment)
+    if (lane < G)
+      *reinterpret_cast<float4 *>(rec + lane * (D + kRecHeader)) =
+          make_float4(Mh * qsc, lsum, bs, __builtin_bit_cast(float, bj));
+    // value rows: hi row h + lo row h + G; lane (j, g4) holds rows 4 g4 + i,
+    // columns (D/16) j .. +NB-1; one row (i) at a time, four columns per store
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = O[nb][i];
-      float partner;
-      if constexpr (G >= 4)
-        partner = __shfl_xor(v, 16 * (G / 4), 64);
-      else
-        partner = O[nb][i ^ G];
       const int row = 4 * g4 + i;
-      if (row < G) red_o[wave][row][(D / 16) * j + nb] = v + partner;
-    }
-  }
-  __syncthreads();
-
-  // ---- combine the waves, write this split's records ---------------------------------
-  const int n_part = a.n_split;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int hh = idx / D, i = idx % D;
-    float M = -INFINITY;
+      float *dst = rec + row * (D + kRecHeader) + kRecHeader + (D / 16) * j;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w)
-      if (red_o[w][hh][D + 1] > 0.f) M = fmaxf(M, red_o[w][hh][D]);
-    float o = 0.f, L = 0.f, bsc = -INFINITY;
-    int bpos = -1;
+      for (int q = 0; q < NB / 4; ++q) {
+        float v4[4];
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      if (red_o[w][hh][D + 1] > 0.f) {
-        const float sc = exp2f(red_o[w][hh][D] - M);
-        o += red_o[w][hh][i] * sc;
-        L += red_o[w][hh][D + 1] * sc;
-        // the larger score; on equal scores the lower position (the waves
-        // hold interleaved tiles, so wave order is not position order)
-        const float ws = red_o[w][hh][D + 2];
-        const int wp = __builtin_bit_cast(int, red_o[w][hh][D + 3]);
-        if (ws > bsc || (ws == bsc && wp >= 0 && (bpos < 0 || wp < bpos))) {
-          bsc = ws;
-          bpos = wp;
+        for (int k = 0; k < 4; ++k) {
+          const float v = O[4 * q + k][i];
+          if constexpr (G >= 4)
+            v4[k] = v + __shfl_xor(v, 16 * (G / 4), 64);
+          else
+            v4[k] = v + O[4 * q + k][i ^ G];
         }
+        if (row < G) *reinterpret_cast<float4 *>(dst + 4 * q) = make_float4(v4[0], v4[1], v4[2], v4[3]);
       }
     }
-    float *rec = a.ws + (((size_t)b * a.hq + kvh * G + hh) * n_part + split) * (D + kRecHeader);
-    rec[kRecHeader + i] = o;
-    if (i == 0) {
-      rec[0] = M;
-      rec[1] = L;
-      rec[2] = bsc;
-      rec[3] = __builtin_bit_cast(float, bpos);
-    }
+  };
+
+  // ---- main loop ---------------------------------------------------------------
+  // Ring of NST stages: the next NST - 1 tiles are in flight while one is
+  // processed.  Every iteration issues one stage (out of range past the
+  // wave's last tile), so one fixed wait finds the oldest stage landed; other
+  // memory operations in between only make that wait longer, never short.
+  // At a segment boundary the next query rows are loaded and everything in
+  // flight is awaited.
+  Cursor cp = c0, ca = c0;                   // tile processed, tile loaded next
+  int ta = t_begin;
+  load_query(cp);
+  reset();
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) {
+    issue(ca, ta < t_end, i);
+    if (ta + 1 < t_end) advance(ca);
+    ++ta;
   }
+  int slot = 0;                              // stage of tile tp
+  for (int tp = t_begin; tp < t_end; ++tp) {
+    const int aslot = slot == 0 ? NST - 1 : slot - 1;       // (tp + NST - 1) mod NST, processed last iteration
+    issue(ca, ta < t_end, aslot);
+    if (ta + 1 < t_end) advance(ca);
+    ++ta;
+    wait_vmem<(NST - 1) * S::LOADS>();
+    const char *cur = stages + slot * S::BYTES;
+    const bool seg_last = cp.i == cp.n - 1;
+    process(cur, cp.i * kDecodeStep, cp.len);
+    if (seg_last || tp + 1 == t_end) write_record(cp);
+    if (tp + 1 < t_end) {
+      advance(cp);
+      if (seg_last) {
+        load_query(cp);
+        wait_vmem<0>();
+        reset();
+      }
+    }
+    slot = slot == NST - 1 ? 0 : slot + 1;
+  }
+  wait_vmem<0>();                            // no load into LDS may outlive the wave
 }
 
-constexpr int kMergeChunk = 1024;          // split records whose weights are staged in LDS at a time
+// ---------------------------------------------------------------------------
+// merge kernel
+// ---------------------------------------------------------------------------
+
+constexpr int kMergeChunk = 1024;          // records whose weights are staged in LDS at a time
 
 template <int D, int VARIANT>
 __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
   constexpr int RS = D + kRecHeader;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int g = h / a.group;
+  const int G = a.group;
+  const int g = h / G, hh = h - g * G;
   const int i = threadIdx.x;
-  const int n = a.n_part;
-  const float *recs = a.ws + ((size_t)b * a.hq + h) * n * RS;
+  // the records of this segment's pieces: s + first .. s + last, G records apart
+  const int *seg_base = reinterpret_cast<const int *>(a.plan + 1);
+  const int nt = (seg_base[b + 1] - seg_base[b]) / a.hkv;      // tiles per KV head of sequence b
+  const int W = a.plan->per_wave;
+  const long long s = (long long)b * a.hkv + g;
+  int n = 0;
+  const float *recs = a.ws;
+  if (nt > 0) {
+    const int S0 = seg_base[b] + g * nt;
+    const int first = S0 / W, last = (S0 + nt - 1) / W;
+    n = last - first + 1;
+    recs = a.ws + ((s + first) * G + hh) * RS;
+  }
+  const size_t stride = (size_t)G * RS;       // from one piece's record to the next
   constexpr int NW = D / 64;                 // waves of the workgroup
   __shared__ float redf[NW];
   __shared__ int redi[NW];
@@ -783,12 +898,12 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
 
   // Headers are read in parallel (thread t: records t, t + D, ...): the
   // running maximum and the best score with its position (ties: the lower
-  // position; splits cover increasing positions).  Reductions: across the
+  // position; pieces cover increasing positions).  Reductions: across the
   // wave by lane exchanges, then across the waves through LDS.
   float Mt = -INFINITY, bt = -INFINITY;
   int at = -1;
   for (int p = i; p < n; p += D) {
-    const float *rec = recs + (size_t)p * RS;
+    const float *rec = recs + (size_t)p * stride;
     if (rec[1] > 0.f) {
       Mt = fmaxf(Mt, rec[0]);
       const float sc = rec[2];
@@ -826,25 +941,25 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
   }
   __syncthreads();
 
-  // Weights 2^(M_p - M) (0 for empty splits) staged in LDS chunk by chunk;
-  // each thread then sums its coordinate over the records in split order,
-  // with independent loads.
+  // Weights 2^(M_p - M) (0 for empty pieces) staged in LDS chunk by chunk;
+  // each thread then sums its coordinate over the records in order, with
+  // independent loads.
   float Lt = 0.f, o = 0.f;
   for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
     const int cn = min(kMergeChunk, n - c0);
     for (int p = i; p < cn; p += D) {
-      const float *rec = recs + (size_t)(c0 + p) * RS;
+      const float *rec = recs + (size_t)(c0 + p) * stride;
       const float lp = rec[1];
       const float w = lp > 0.f ? exp2f(rec[0] - M) : 0.f;
       wbuf[p] = w;
       Lt += lp > 0.f ? lp * w : 0.f;
     }
     __syncthreads();
-    const float *col = recs + (size_t)c0 * RS + kRecHeader + i;
+    const float *col = recs + (size_t)c0 * stride + kRecHeader + i;
 #pragma unroll 8
     for (int p = 0; p < cn; ++p) {
       const float w = wbuf[p];
-      const float v = col[(size_t)p * RS];
+      const float v = col[(size_t)p * stride];
       o += w > 0.f ? v * w : 0.f;
     }
     __syncthreads();
@@ -896,9 +1011,34 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+// Whether the pair table and a ring of two stages per wave fit in one
+// compute unit's LDS (every shape without RoPE coordinates does; with them
+// head_dim 512 at 4 bits does not).
+template <int D, int BITS, int ROPE>
+constexpr bool partial_fits() {
+  return lds_table_bytes<BITS>() + kDecodeWaves * 2 * Stage<D, BITS, ROPE>::BYTES <= 160 * 1024;
+}
+
+template <int D, int ROPE>
+hipError_t prep_dispatch(const DecodeArgs &a, hipStream_t s) {
+  const dim3 grid(1 + (unsigned)(a.batch * a.hkv));
+  switch (a.group) {
+    case 1: hipLaunchKernelGGL((prep_kernel<D, ROPE, 1>), grid, dim3(kPrepThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((prep_kernel<D, ROPE, 2>), grid, dim3(kPrepThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((prep_kernel<D, ROPE, 4>), grid, dim3(kPrepThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((prep_kernel<D, ROPE, 8>), grid, dim3(kPrepThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D, int BITS, bool ARGMAX, int ROPE>
 hipError_t partial_dispatch_group(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)a.hkv, (unsigned)a.batch, (unsigned)a.n_split);
+  const dim3 grid((unsigned)(a.n_waves / kDecodeWaves));
   switch (a.group) {
     case 1: hipLaunchKernelGGL((partial_kernel<D, BITS, 1, ARGMAX, ROPE>), grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((partial_kernel<D, BITS, 2, ARGMAX, ROPE>), grid, dim3(kThreads), 0, s, a); break;
@@ -911,16 +1051,10 @@ hipError_t partial_dispatch_group(const DecodeArgs &a, hipStream_t s) {
 
 template <int D, int BITS, int ROPE>
 hipError_t partial_dispatch_argmax(const DecodeArgs &a, hipStream_t s) {
+  hipError_t e = prep_dispatch<D, ROPE>(a, s);
+  if (e != hipSuccess) return e;
   return a.argmax ? partial_dispatch_group<D, BITS, true, ROPE>(a, s)
                   : partial_dispatch_group<D, BITS, false, ROPE>(a, s);
-}
-
-// Whether the pair table and a ring of two stages per wave fit in one
-// compute unit's LDS (every shape without RoPE coordinates does; with them
-// head_dim 512 at 4 bits does not).
-template <int D, int BITS, int ROPE>
-constexpr bool partial_fits() {
-  return (1 << (2 * BITS)) * lut_repl<BITS>() * 4 + kDecodeWaves * 2 * Stage<D, BITS, ROPE>::BYTES <= 160 * 1024;
 }
 
 // ROPE: the RoPE coordinates per key these instantiations take (0: none).
@@ -935,6 +1069,25 @@ hipError_t partial_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
       break;
   }
   return hipErrorInvalidValue;
+}
+
+// Workgroups of the partial kernel resident on one compute unit (one wave
+// per SIMD each): the smaller of what LDS and the register budget allow.
+template <int D, int BITS, int ROPE>
+int groups_per_cu(bool argmax) {
+  const int lds = resident_groups<D, BITS, ROPE>();
+  const int regs = argmax ? partial_waves<D, BITS, ROPE, true>() : partial_waves<D, BITS, ROPE, false>();
+  return lds < regs ? lds : regs;
+}
+
+template <int D, int ROPE = 0>
+int partial_groups_per_cu(int bits, bool argmax) {
+  switch (bits) {
+    case 2: return groups_per_cu<D, 2, ROPE>(argmax);
+    case 3: return groups_per_cu<D, 3, ROPE>(argmax);
+    case 4: return groups_per_cu<D, 4, ROPE>(argmax);
+  }
+  return 1;
 }
 
 template <int D>

@@ -244,25 +244,19 @@ def test_partial_and_merge_validation():
 
 
 def expected_workspace(batch, hq, hkv, d, max_len):
-    """Workspace bytes from the documented split rule: about 2048 workgroups,
-    chunks of at least 8192 tokens while that still gives 512 workgroups,
-    whole 128-token blocks; records of d + 4 floats per (sequence, query
-    head, split), then (256-byte aligned) 8 bytes per (sequence, split) of
-    work order when there are at most 4096 such pairs."""
-    T = max(max_len, 1)
-    pairs = batch * hkv
-
-    def chunk_for(groups):
-        want = max(1, -(-groups // pairs))
-        return -(-T // want)
-
-    chunk = max(chunk_for(2048), min(8192, chunk_for(512)))
-    chunk = -(-chunk // 128) * 128
-    n_split = -(-T // chunk)
-    rec = batch * hq * n_split * (d + 4) * 4
-    if batch * n_split <= 4096:
-        return -(-rec // 256) * 256 + batch * n_split * 8
-    return rec
+    """Workspace bytes from the documented layout, each part rounded up to
+    256 bytes: the plan (a 16-byte header, batch + 1 segment bases and 4096
+    per-wave start segments, int32), the rotated queries (2 fp16 rows of
+    d + 64 coordinates per query head), their scales (one float per query
+    head), then the records: d + 4 floats per query head of a group for each
+    of batch x H_kv + 4096 pieces.  No term grows with max_len."""
+    up = lambda x: -(-x // 256) * 256
+    group = hq // hkv
+    plan = up(16 + 4 * (batch + 1 + 4096))
+    qrot = up(batch * hq * 2 * (d + 64) * 2)
+    qscale = up(batch * hq * 4)
+    records = (batch * hkv + 4096) * group * (d + 4) * 4
+    return plan + qrot + qscale + records
 
 
 @pytest.mark.parametrize("batch,hq,hkv,d,max_len", [
@@ -270,7 +264,7 @@ def expected_workspace(batch, hq, hkv, d, max_len):
     (1, 32, 4, 128, 32768), (16, 32, 4, 128, 32768),
     (4200, 2, 1, 128, 40), (3, 8, 2, 512, 1), (256, 8, 8, 256, 32768), (2, 4, 4, 128, 0)])
 def test_decode_workspace_geometry(batch, hq, hkv, d, max_len):
-    """The host's split geometry, observed through the workspace size."""
+    """The workspace layout, observed through its size."""
     L = B.lib()
     c = cfg(d=d, hkv=hkv)
     cc = c.c()

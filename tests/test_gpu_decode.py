@@ -19,8 +19,8 @@ import pytest
 import oracle as O
 from compressed_space_attention_isoquant_amd import binding as B
 from compressed_space_attention_isoquant_amd import inputs
-from tests.gpu_helpers import (DEV, host_cache, make_config, oracle_cache, quantize_rows, say,
-                               scale_for, torch)
+from tests.gpu_helpers import (DEV, host_cache, make_config, oracle_cache, quantize_rows, reconcile_codes,
+                               reconcile_norms, say, scale_for, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -217,7 +217,7 @@ def test_argmax_ties_lowest_position():
     case = inputs.decode_case(seed=31, kv_len=T, num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
     k, q = case["k"], case["q"]
     med = float(np.median(np.linalg.norm(k[:, 0].astype(np.float64), axis=-1)))
-    ties = {0: (128, 32), 1: (20, 5), 2: (6, 1), 3: (20000, 300), 4: (32767, 300, 20000), 5: (159, 129, 33)}
+    ties = {0: (128, 32), 1: (20, 5), 2: (6, 1), 3: (20000, 300), 4: (32767, 4000, 24000), 5: (159, 129, 33)}
     for h, positions in ties.items():
         qh = q[h].astype(np.float64)
         key = (1.5 * med * qh / np.linalg.norm(qh)).astype(np.float16)
@@ -306,10 +306,10 @@ def test_split_geometry_invariance():
 
 
 def test_many_short_sequences():
-    """4200 short ragged sequences (0..40 tokens): more (sequence, split)
-    pairs than the device-side longest-first ordering handles, so the
-    workgroups take their pairs in grid order.  Sampled sequences (first,
-    last, empty ones and a spread) against the oracle."""
+    """4200 short ragged sequences (0..40 tokens, some empty): each wave's
+    share covers many whole segments, with empty sequences skipped in the
+    walk.  Sampled sequences (first, last, empty ones and a spread) against
+    the oracle."""
     d, bits, hq, hkv, batch, cap = 128, 3, 2, 1, 4200, 40
     rng = np.random.default_rng(21)
     lens = rng.integers(0, cap + 1, size=batch)
@@ -409,20 +409,17 @@ def test_distinct_k_and_v_capacities():
     del t
 
 
-def test_sorted_work_order_batch():
-    """300 ragged sequences up to 32K tokens, one KV head: 4 splits each, so
-    1200 (sequence, split) pairs, which the order kernel sorts (more than
-    1024 pairs: the sorting network rather than the counting rank).  Every
-    pair must run exactly once: sampled sequences against the oracle."""
+def test_ragged_batch_shares_cross_segments():
+    """300 ragged sequences of 1..32K tokens, one KV head: the waves' equal
+    shares of the tiles start and end inside segments of every length, so
+    most sequences are split between several waves and most waves cover the
+    ends of several sequences.  Every tile must be attended exactly once:
+    sampled sequences (the longest, the shortest and three more) against the
+    oracle, argmax included."""
     t = torch()
     d, bits, hq, hkv, batch, cap = 128, 3, 2, 1, 300, 32768
     lens = inputs.batch_lengths(25, batch, 1, cap)
     T = int(lens.max())
-    # the split rule (about 2048 workgroups, chunks of at least 8192 tokens
-    # while that still gives 512, whole 128-token blocks)
-    chunk = max(-(-T // -(-2048 // batch)), min(8192, -(-T // -(-512 // batch))))
-    n_split = -(-T // (-(-chunk // 128) * 128))
-    assert 1024 < batch * n_split <= 4096, batch * n_split
     rng = np.random.default_rng(25)
     ch_k = inputs.outlier_channels(rng, hkv, d)
     ch_v = inputs.outlier_channels(rng, hkv, d)
