@@ -423,7 +423,7 @@ static int decode_partial_impl(const iq_config *cfg, const void *q, int32_t q_dt
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     return IQ_ERR_HIP;
-  const int groups = iq::decode_groups_per_cu(cfg->head_dim, cfg->bits, rope_dim, track_argmax != 0);
+  const int groups = iq::decode_groups_per_cu(cfg->head_dim, cfg->bits, rope_dim);
   const int e = centroid_exponent(cfg);
   iq::DecodeArgs a;
   a.q = q;

@@ -9,9 +9,9 @@ hipError_t launch_decode_512(int bits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge_128(int variant, const MergeArgs &a, hipStream_t s);
 hipError_t launch_merge_256(int variant, const MergeArgs &a, hipStream_t s);
 hipError_t launch_merge_512(int variant, const MergeArgs &a, hipStream_t s);
-int decode_groups_per_cu_128(int bits, int rope, bool argmax);
-int decode_groups_per_cu_256(int bits, int rope, bool argmax);
-int decode_groups_per_cu_512(int bits, int rope, bool argmax);
+int decode_groups_per_cu_128(int bits, int rope);
+int decode_groups_per_cu_256(int bits, int rope);
+int decode_groups_per_cu_512(int bits, int rope);
 
 hipError_t launch_decode(int d, int bits, const DecodeArgs &a, hipStream_t s) {
   switch (d) {
@@ -31,11 +31,11 @@ hipError_t launch_merge(int d, int variant, const MergeArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-int decode_groups_per_cu(int d, int bits, int rope, bool argmax) {
+int decode_groups_per_cu(int d, int bits, int rope) {
   switch (d) {
-    case 128: return decode_groups_per_cu_128(bits, rope, argmax);
-    case 256: return decode_groups_per_cu_256(bits, rope, argmax);
-    case 512: return decode_groups_per_cu_512(bits, rope, argmax);
+    case 128: return decode_groups_per_cu_128(bits, rope);
+    case 256: return decode_groups_per_cu_256(bits, rope);
+    case 512: return decode_groups_per_cu_512(bits, rope);
   }
   return 1;
 }

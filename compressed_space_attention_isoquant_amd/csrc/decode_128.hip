@@ -13,9 +13,8 @@ hipError_t launch_merge_128(int variant, const MergeArgs &a, hipStream_t s) {
   return merge_dispatch<128>(variant, a, s);
 }
 
-int decode_groups_per_cu_128(int bits, int rope, bool argmax) {
-  return rope == kDecodeRope ? partial_groups_per_cu<128, kDecodeRope>(bits, argmax)
-                             : partial_groups_per_cu<128>(bits, argmax);
+int decode_groups_per_cu_128(int bits, int rope) {
+  return rope == kDecodeRope ? partial_groups_per_cu<128, kDecodeRope>(bits) : partial_groups_per_cu<128>(bits);
 }
 
 }  // namespace iq

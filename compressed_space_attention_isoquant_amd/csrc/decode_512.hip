@@ -13,9 +13,8 @@ hipError_t launch_merge_512(int variant, const MergeArgs &a, hipStream_t s) {
   return merge_dispatch<512>(variant, a, s);
 }
 
-int decode_groups_per_cu_512(int bits, int rope, bool argmax) {
-  return rope == kDecodeRope ? partial_groups_per_cu<512, kDecodeRope>(bits, argmax)
-                             : partial_groups_per_cu<512>(bits, argmax);
+int decode_groups_per_cu_512(int bits, int rope) {
+  return rope == kDecodeRope ? partial_groups_per_cu<512, kDecodeRope>(bits) : partial_groups_per_cu<512>(bits);
 }
 
 }  // namespace iq

@@ -36,7 +36,7 @@ constexpr int kRecHeader = 4;              // M, L, best score, best position
 constexpr float kLazyTau = 4.0f;           // rescale only when the max grows by more than this
 constexpr float kWeightBias = 25.0f;       // weights 2^(s - M + bias) * ||v|| stay below 2^15
 constexpr int kDecodeRope = 64;            // RoPE coordinates per key the decode kernels take
-constexpr int kMinTilesPerWave = 4;        // a wave's share is at least this many tiles
+constexpr int kMinTilesPerWave = 8;        // a wave's share is at least this many tiles
 constexpr int kMaxDecodeWaves = 4096;      // waves of the partial launch at most (256 CUs x 16)
 constexpr int kPrepThreads = 256;
 

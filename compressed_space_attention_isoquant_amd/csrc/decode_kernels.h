@@ -15,8 +15,7 @@
 //             G + j holds q~_lo of head j, so S_hi + S_lo is the full-precision
 //             score.  C_K comes from the packed K rows through a 2-code table
 //             of exact fp16 centroid pairs (each level times 2^e is an fp16
-//             number), read by lane permutation (ds_bpermute) from a register
-//             holding the table at 2 and 3 bits, from LDS at 4 bits.
+//             number) replicated in LDS.
 //     softmax online, base 2, with a lazily raised running maximum (only
 //             rescaled when a score exceeds it by more than kLazyTau).
 //     values  O~ (16 rows x d) += P (16 x 32 tokens) . C_V (32 x d); row j < G
@@ -208,24 +207,24 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Lane permutation: the value that lane (addr / 4) mod 64 holds in v (the
-// address's bits above 7 and below 2 are ignored).
-__device__ __forceinline__ uint32_t bpermute(uint32_t addr, uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)addr, (int)v);
-}
-
-// Where the code-pair table lives: at 2 and 3 bits (16 and 64 pairs) in one
-// register, lane e holding entry e mod 2^(2b), read by lane permutation, so
-// that an entry's address is the pair's bit field anywhere in bits 2..7; at 4
-// bits (256 pairs) in LDS, replicated 8 times so that a wave's reads fall in
-// distinct banks whatever the codes (lane l reads replica l mod 8).
+// The code-pair table lives in LDS, replicated so that a wave's reads fall
+// in distinct banks whatever the codes: lane l reads replica l mod REPL
+// (entry e at dword e * REPL + l mod REPL); 32 replicas of the 16 or 64
+// pairs at 2 and 3 bits, 8 of the 256 pairs at 4 bits.  (Reading the table
+// from a register by lane permutation instead saves an instruction per read
+// but ran a quarter slower: the permutes cost more than conflict-free reads.)
 template <int BITS>
-constexpr bool pair_table_in_register() {
-  return BITS <= 3;
+constexpr int lut_repl() {
+  return BITS <= 3 ? 32 : 8;
 }
 template <int BITS>
 constexpr int lds_table_bytes() {
-  return pair_table_in_register<BITS>() ? 0 : (1 << (2 * BITS)) * 8 * 4;
+  return (1 << (2 * BITS)) * lut_repl<BITS>() * 4;
+}
+
+template <int N>
+constexpr int ilog2() {
+  return N <= 1 ? 0 : 1 + ilog2<N / 2>();
 }
 
 // LDS layout: workgroups per CU (each holds one wave per SIMD) and stages
@@ -254,13 +253,11 @@ constexpr int stage_count() {
 // Waves per SIMD the register allocation is held to, matching the LDS
 // layout: three where three workgroups share a CU (at most 168 registers per
 // lane), two where the LDS of two fits (head_dim <= 256; 256 registers),
-// else no constraint.  Tracking the argmax needs more registers than 168:
-// those instantiations run two waves per SIMD.
-template <int D, int BITS, int ROPE = 0, bool ARGMAX = false>
+// else no constraint.
+template <int D, int BITS, int ROPE = 0>
 constexpr int partial_waves() {
   const int lds = lds_table_bytes<BITS>() + kDecodeWaves * stage_count<D, BITS, ROPE>() * Stage<D, BITS, ROPE>::BYTES;
-  const int w = resident_groups<D, BITS, ROPE>() == 3 ? 3 : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
-  return ARGMAX && w > 2 ? 2 : w;
+  return resident_groups<D, BITS, ROPE>() == 3 ? 3 : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,7 +385,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 
 template <int D, int BITS, int G, bool ARGMAX, int ROPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(partial_waves<D, BITS, ROPE, ARGMAX>())))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(partial_waves<D, BITS, ROPE>())))
 void partial_kernel(DecodeArgs a) {
   constexpr int NLEV = 1 << BITS;
   constexpr int KS = D / 32;                 // k-steps of the score product
@@ -411,22 +408,18 @@ void partial_kernel(DecodeArgs a) {
   constexpr int DQ = D + ROPE;               // query coordinates
   constexpr int NST = stage_count<D, BITS, ROPE>();
   static_assert((NST - 1) * S::LOADS < 64, "in-flight loads exceed the vmcnt range");
-  constexpr bool REG_TABLE = pair_table_in_register<BITS>();
+  constexpr int REPL = lut_repl<BITS>();
   constexpr int TB = lds_table_bytes<BITS>();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // the code-pair table: one register (entry lane mod 2^(2b)), or LDS replicas
-  __shared__ __attribute__((aligned(TB > 0 ? TB : 4))) uint32_t lut[TB > 0 ? TB / 4 : 1];
+  // the code-pair table, aligned to its own size so that an entry's offset
+  // can be OR-ed into the lane's replica address
+  __shared__ __attribute__((aligned(TB))) uint32_t lut[TB / 4];
   __shared__ __attribute__((aligned(16))) char smem[kDecodeWaves * NST * S::BYTES];
-  uint32_t tbl = 0;
-  if constexpr (REG_TABLE) {
-    tbl = a.lut[lane & (NLEV * NLEV - 1)];
-  } else {
-    for (int i = threadIdx.x; i < TB / 4; i += kThreads) lut[i] = a.lut[i / 8];
-    __syncthreads();                         // the kernel's only barrier: before any wave leaves
-  }
+  for (int i = threadIdx.x; i < TB / 4; i += kThreads) lut[i] = a.lut[i / REPL];
+  __syncthreads();                           // the kernel's only barrier: before any wave leaves
 
   // this wave's share of the tiles: [t_begin, t_end)
   const int w = (int)blockIdx.x * kDecodeWaves + wave;
@@ -473,16 +466,27 @@ void partial_kernel(DecodeArgs a) {
   uint32_t groff[S::R_LOADS > 0 ? S::R_LOADS : 1];
 #pragma unroll
   for (int c = 0; c < S::R_LOADS; ++c) groff[c] = rope_granule_offset<D, BITS, ROPE>(c, lane);
+  // buffer resources of the segment the loads are in (rebuilt when the
+  // loads move to the next segment)
+  int32x4_t kr, vr, knr, vnr, rr;
+  auto resources = [&](const Cursor &c) {
+    const long long hrow = (long long)c.b * a.hkv + c.h;
+    kr = make_rsrc(a.kc + hrow * a.kcap * ROWB, (uint32_t)(a.kcap * ROWB));
+    vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
+    knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
+    vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
+    rr = ROPE ? make_rsrc(a.krope + hrow * a.kcap * ROPE, (uint32_t)(a.kcap * ROPE * 2)) : kr;
+  };
   // loads of the stage of tile c (out of range when !valid) into ring slot
   auto issue = [&](const Cursor &c, bool valid, int slot) {
-    const long long hrow = (long long)c.b * a.hkv + c.h;
-    const int32x4_t kr = make_rsrc(a.kc + hrow * a.kcap * ROWB, (uint32_t)(a.kcap * ROWB));
-    const int32x4_t vr = make_rsrc(a.vc + hrow * a.vcap * ROWB, (uint32_t)(a.vcap * ROWB));
-    const int32x4_t knr = make_rsrc(a.kn + hrow * a.kcap, (uint32_t)(a.kcap * 2));
-    const int32x4_t vnr = make_rsrc(a.vn + hrow * a.vcap, (uint32_t)(a.vcap * 2));
-    const int32x4_t rr = ROPE ? make_rsrc(a.krope + hrow * a.kcap * ROPE, (uint32_t)(a.kcap * ROPE * 2)) : kr;
     load_stage<D, BITS, ROPE>(stages_lds + slot * S::BYTES, kr, vr, knr, vnr, rr, c.i * kDecodeStep, valid, lane,
                               goff, groff);
+  };
+  // the load cursor's next tile (rebuilding the resources on a new segment)
+  auto advance_loads = [&](Cursor &c) {
+    const bool seg_end = c.i == c.n - 1;
+    advance(c);
+    if (seg_end) resources(c);
   };
 
   const int j = lane & 15;      // column of the score tile / row of the value operand
@@ -529,20 +533,19 @@ void partial_kernel(DecodeArgs a) {
   const int k_off = S::K_OFF + j * S::RS + g4 * UDW * 4;
   const int v_off = S::V_OFF + 4 * g4 * S::RS + (vbit >> 5) * 4;
   const int n_off = (16 * my_tile + 4 * g4) * 2;
-  constexpr int LSH = REG_TABLE ? 2 : 5;     // bit position the pair field must reach
-  const uint32_t lut_base = REG_TABLE ? 0u : (lds_addr(lut) | (uint32_t)(lane & 7) * 4u);
-  // table entry of the 2*BITS-bit field at bit `pos` of w (any bits above
-  // the field are ignored by the lane permutation; the LDS table masks them)
+  constexpr int LSH = ilog2<REPL * 4>();     // table entry -> byte offset shift
+  // byte address of this lane's replica of table entry 0
+  const uint32_t lut_base = lds_addr(lut) | (uint32_t)(lane % REPL) * 4u;
+  // table entry at the 2*BITS-bit field at bit `pos` of w: the field is
+  // shifted to bit LSH and masked, and the lane's replica offset OR-ed in: a
+  // shift and one three-input bit operation, or the bit operation alone
+  // where pos = LSH
   auto pair = [&](uint32_t w, auto pos) -> uint32_t {
     constexpr int P = decltype(pos)::value;
+    constexpr uint32_t M = ((1u << (2 * BITS)) - 1u) << LSH;
     const uint32_t f = P >= LSH ? (w >> (P - LSH)) : (w << (LSH - P));
-    if constexpr (REG_TABLE) {
-      return bpermute(f, tbl);
-    } else {
-      constexpr uint32_t M = ((1u << (2 * BITS)) - 1u) << LSH;
-      const uint32_t addr = (f & M) | lut_base;
-      return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
-    }
+    const uint32_t addr = (f & M) | lut_base;
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
   };
 
   float Mh, Mb, Lh, best_s;
@@ -558,15 +561,24 @@ void partial_kernel(DecodeArgs a) {
     for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // this lane's token of the tile for score row r is 16 my_tile + 4 g4 + r;
-  // lanes of dead columns take no token (their scores stay -inf)
+  // Masking: score row r of this lane is token 16 my_tile + 4 g4 + r of the
+  // tile; the score is fma(product, key norm, mbias[r]) with mbias 0 for a
+  // live token and -inf otherwise (dead columns always; tokens past the end
+  // of a segment in its last tile).  The biases change only at a segment's
+  // last tile, so full tiles pay nothing for masking and one code path
+  // serves both (a second inlined copy of the tile body would not fit the
+  // register budget).
   const int tok0 = live ? 16 * my_tile + 4 * g4 : (1 << 30);
+  float mbias[4];
+  auto set_mask = [&](int limit) {          // tokens of the tile below `limit` are live
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mbias[r] = tok0 + r < limit ? 0.f : -INFINITY;
+  };
+  set_mask(kDecodeStep);
 
-  // One 32-token tile from stage `cur`: tokens t0 .. t0 + 31 of a segment of
-  // `end` tokens (those at and past `end`, in a segment's last tile, are
-  // masked).  One code path for full and partial tiles: a second inlined
-  // copy of this body for the partial tile would not fit the register budget.
-  auto process = [&](const char *cur, const int t0, const int end) {
+  // One 32-token tile from stage `cur`: tokens t0 .. t0 + 31 of a segment
+  // (masked by mbias).
+  auto process = [&](const char *cur, const int t0) {
     // packed K rows of the two 16-token tiles (lane: token j, dims slice g4)
     uint32_t kw[2][CW];
 #pragma unroll
@@ -689,13 +701,12 @@ void partial_kernel(DecodeArgs a) {
     for (int r = 0; r < 4; ++r) {
       const float own = my_tile ? S2[1][r] : S2[0][r];
       const float give = my_tile ? S2[0][r] : S2[1][r];      // what the partner lane needs
-      float c = (own + xor_g<G>(give)) * half_bits_to_float(kb[r]);
+      float c = fmaf(own + xor_g<G>(give), half_bits_to_float(kb[r]), mbias[r]);
       if constexpr (ROPE > 0) {
         const float rown = my_tile ? SR[1][r] : SR[0][r];
         const float rgive = my_tile ? SR[0][r] : SR[1][r];
         c += rown + xor_g<G>(rgive);
       }
-      c = tok0 + r < end - t0 ? c : -INFINITY;
       sig[r] = c;
       u[r] = fmaf((float)((vb[r] >> 8) & 0xFF), q4, c);
     }
@@ -828,26 +839,29 @@ void partial_kernel(DecodeArgs a) {
   int ta = t_begin;
   load_query(cp);
   reset();
+  resources(ca);
 #pragma unroll
   for (int i = 0; i < NST - 1; ++i) {
     issue(ca, ta < t_end, i);
-    if (ta + 1 < t_end) advance(ca);
+    if (ta + 1 < t_end) advance_loads(ca);
     ++ta;
   }
   int slot = 0;                              // stage of tile tp
   for (int tp = t_begin; tp < t_end; ++tp) {
     const int aslot = slot == 0 ? NST - 1 : slot - 1;       // (tp + NST - 1) mod NST, processed last iteration
     issue(ca, ta < t_end, aslot);
-    if (ta + 1 < t_end) advance(ca);
+    if (ta + 1 < t_end) advance_loads(ca);
     ++ta;
     wait_vmem<(NST - 1) * S::LOADS>();
-    const char *cur = stages + slot * S::BYTES;
     const bool seg_last = cp.i == cp.n - 1;
-    process(cur, cp.i * kDecodeStep, cp.len);
+    const int tail = cp.len - cp.i * kDecodeStep;       // tokens of the segment from this tile on
+    if (seg_last && tail < kDecodeStep) set_mask(tail);
+    process(stages + slot * S::BYTES, cp.i * kDecodeStep);
     if (seg_last || tp + 1 == t_end) write_record(cp);
     if (tp + 1 < t_end) {
       advance(cp);
       if (seg_last) {
+        if (tail < kDecodeStep) set_mask(kDecodeStep);
         load_query(cp);
         wait_vmem<0>();
         reset();
@@ -864,14 +878,24 @@ void partial_kernel(DecodeArgs a) {
 
 constexpr int kMergeChunk = 1024;          // records whose weights are staged in LDS at a time
 
+// Threads of a merge workgroup: head_dim columns times NP parts, each part
+// summing every NP-th piece, so that many records' loads are in flight.
+template <int D>
+constexpr int merge_threads() {
+  return D < 256 ? 256 : D;
+}
+
 template <int D, int VARIANT>
-__global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(MergeArgs a) {
   constexpr int RS = D + kRecHeader;
+  constexpr int NT = merge_threads<D>();
+  constexpr int NP = NT / D;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int G = a.group;
   const int g = h / G, hh = h - g * G;
-  const int i = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int i = tid % D, part = tid / D;
   // the records of this segment's pieces: s + first .. s + last, G records apart
   const int *seg_base = reinterpret_cast<const int *>(a.plan + 1);
   const int nt = (seg_base[b + 1] - seg_base[b]) / a.hkv;      // tiles per KV head of sequence b
@@ -886,23 +910,24 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
     recs = a.ws + ((s + first) * G + hh) * RS;
   }
   const size_t stride = (size_t)G * RS;       // from one piece's record to the next
-  constexpr int NW = D / 64;                 // waves of the workgroup
+  constexpr int NW = NT / 64;                // waves of the workgroup
   __shared__ float redf[NW];
   __shared__ int redi[NW];
   __shared__ float wbuf[kMergeChunk];
-  const int lane = i & 63, wave = i >> 6;
+  __shared__ float part_o[NP][D];
+  const int lane = tid & 63, wave = tid >> 6;
   // (score, position) pairs: the larger score, ties to the lower valid position
   auto better = [](float s1, int p1, float s0, int p0) {
     return s1 > s0 || (s1 == s0 && p1 >= 0 && (p0 < 0 || p1 < p0));
   };
 
-  // Headers are read in parallel (thread t: records t, t + D, ...): the
+  // Headers are read in parallel (thread t: records t, t + NT, ...): the
   // running maximum and the best score with its position (ties: the lower
   // position; pieces cover increasing positions).  Reductions: across the
   // wave by lane exchanges, then across the waves through LDS.
   float Mt = -INFINITY, bt = -INFINITY;
   int at = -1;
-  for (int p = i; p < n; p += D) {
+  for (int p = tid; p < n; p += NT) {
     const float *rec = recs + (size_t)p * stride;
     if (rec[1] > 0.f) {
       Mt = fmaxf(Mt, rec[0]);
@@ -942,12 +967,12 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
   __syncthreads();
 
   // Weights 2^(M_p - M) (0 for empty pieces) staged in LDS chunk by chunk;
-  // each thread then sums its coordinate over the records in order, with
-  // independent loads.
+  // each thread then sums its coordinate over its part's records, with
+  // independent loads, and the parts are added in LDS.
   float Lt = 0.f, o = 0.f;
   for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
     const int cn = min(kMergeChunk, n - c0);
-    for (int p = i; p < cn; p += D) {
+    for (int p = tid; p < cn; p += NT) {
       const float *rec = recs + (size_t)(c0 + p) * stride;
       const float lp = rec[1];
       const float w = lp > 0.f ? exp2f(rec[0] - M) : 0.f;
@@ -957,24 +982,29 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
     __syncthreads();
     const float *col = recs + (size_t)c0 * stride + kRecHeader + i;
 #pragma unroll 8
-    for (int p = 0; p < cn; ++p) {
+    for (int p = part; p < cn; p += NP) {
       const float w = wbuf[p];
       const float v = col[(size_t)p * stride];
       o += w > 0.f ? v * w : 0.f;
     }
     __syncthreads();
   }
+  part_o[part][i] = o;
   for (int m = 32; m > 0; m >>= 1) Lt += __shfl_xor(Lt, m, 64);
   if (lane == 0) redf[wave] = Lt;
   __syncthreads();
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) L += redf[w];
+  if (part == 0) {
+#pragma unroll
+    for (int q = 1; q < NP; ++q) o += part_o[q][i];
+  }
 
   __shared__ float y[D];
-  y[i] = L > 0.f ? o * a.oscale / L : 0.f;
+  if (part == 0) y[i] = L > 0.f ? o * a.oscale / L : 0.f;
   __syncthreads();
-  if (i < D / 4) {
+  if (tid < D / 4) {
     const float *pg = a.quats + (size_t)g * (D / 4) * block_param_floats(VARIANT);
     float4 u = block_inv<VARIANT>(make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]), pg, i);
     y[4 * i] = u.x;
@@ -986,18 +1016,19 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeArgs a) {
   for (int st = 1; st < D; st <<= 1) {
     float x0 = 0.f, x1 = 0.f;
     int lo = 0;
-    if (i < D / 2) {
-      lo = (i / st) * 2 * st + (i % st);
+    if (tid < D / 2) {
+      lo = (tid / st) * 2 * st + (tid % st);
       x0 = y[lo];
       x1 = y[lo + st];
     }
     __syncthreads();
-    if (i < D / 2) {
+    if (tid < D / 2) {
       y[lo] = x0 + x1;
       y[lo + st] = x0 - x1;
     }
     __syncthreads();
   }
+  if (part != 0) return;
   const float val = y[i] / sqrtf((float)D);
   const size_t off = ((size_t)b * a.hq + h) * D + i;
   if (a.out_f16)
@@ -1074,18 +1105,17 @@ hipError_t partial_dispatch_bits(int bits, const DecodeArgs &a, hipStream_t s) {
 // Workgroups of the partial kernel resident on one compute unit (one wave
 // per SIMD each): the smaller of what LDS and the register budget allow.
 template <int D, int BITS, int ROPE>
-int groups_per_cu(bool argmax) {
-  const int lds = resident_groups<D, BITS, ROPE>();
-  const int regs = argmax ? partial_waves<D, BITS, ROPE, true>() : partial_waves<D, BITS, ROPE, false>();
-  return lds < regs ? lds : regs;
+constexpr int groups_per_cu() {
+  return resident_groups<D, BITS, ROPE>() < partial_waves<D, BITS, ROPE>() ? resident_groups<D, BITS, ROPE>()
+                                                                             : partial_waves<D, BITS, ROPE>();
 }
 
 template <int D, int ROPE = 0>
-int partial_groups_per_cu(int bits, bool argmax) {
+int partial_groups_per_cu(int bits) {
   switch (bits) {
-    case 2: return groups_per_cu<D, 2, ROPE>(argmax);
-    case 3: return groups_per_cu<D, 3, ROPE>(argmax);
-    case 4: return groups_per_cu<D, 4, ROPE>(argmax);
+    case 2: return groups_per_cu<D, 2, ROPE>();
+    case 3: return groups_per_cu<D, 3, ROPE>();
+    case 4: return groups_per_cu<D, 4, ROPE>();
   }
   return 1;
 }
@@ -1094,9 +1124,9 @@ template <int D>
 hipError_t merge_dispatch(int variant, const MergeArgs &a, hipStream_t s) {
   dim3 grid((unsigned)a.hq, (unsigned)a.batch);
   switch (variant) {
-    case 0: hipLaunchKernelGGL((merge_kernel<D, 0>), grid, dim3(D), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(D), 0, s, a); break;
-    case kPlanar: hipLaunchKernelGGL((merge_kernel<D, kPlanar>), grid, dim3(D), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((merge_kernel<D, 0>), grid, dim3(merge_threads<D>()), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(merge_threads<D>()), 0, s, a); break;
+    case kPlanar: hipLaunchKernelGGL((merge_kernel<D, kPlanar>), grid, dim3(merge_threads<D>()), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

