@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.iq_decode_attention_merge.argtypes = [ctypes.POINTER(IQConfigC), i32, i32, i64, P, i32, P, P,
                                                 P, ctypes.c_size_t, P]
         L.iq_decode_attention_merge.restype = ctypes.c_int
+        L.iq_decode_attention_noalloc.argtypes = [ctypes.POINTER(IQConfigC), P, i32, i32, i32,
+                                                  ctypes.POINTER(IQCacheC), ctypes.POINTER(IQCacheC), P, i64,
+                                                  ctypes.c_float, P, i32, P, P, P]
+        L.iq_decode_attention_noalloc.restype = ctypes.c_int
         L.iq_status_string.argtypes = [ctypes.c_int]
         L.iq_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -301,3 +305,15 @@ def iq_decode_attention_merge(cfg: Config, batch: int, num_q_heads: int, max_kv_
     _check(lib().iq_decode_attention_merge(ctypes.byref(cc), int(batch), int(num_q_heads), int(max_kv_len),
                                            _ptr(out), _dtype_code(out), _ptr(lse), _ptr(argmax),
                                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def iq_decode_attention_noalloc(cfg: Config, q, k: PackedCache, v: PackedCache, kv_len, max_kv_len: int,
+                                softmax_scale: float, out, lse=None, argmax=None, stream=None) -> None:
+    """iq_decode_attention with the library's own fixed workspace (no
+    workspace argument, nothing allocated)."""
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    cc, kc, vc = cfg.c(), k.c(), v.c()
+    _check(lib().iq_decode_attention_noalloc(ctypes.byref(cc), _ptr(q), _dtype_code(q), batch, hq,
+                                             ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_len), int(max_kv_len),
+                                             float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse),
+                                             _ptr(argmax), _stream(stream)))

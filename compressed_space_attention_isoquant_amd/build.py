@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libiq.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "decode_128.hip", "decode_256.hip", "decode_512.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "decode_128.hip", "decode_256.hip", "decode_512.hip",
+           "noalloc.hip"]
 
 # Matrix-core accumulators kept in the unified VGPR file (no AGPR copies around
 # the value accumulators).  Not for head_dim 512, whose register pressure makes

@@ -364,6 +364,24 @@ size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch, int32_t nu
   return iq::decode_workspace_total(batch, cfg->num_kv_heads, num_q_heads, cfg->head_dim);
 }
 
+extern "C++" {
+namespace iq {
+int decode_workspace_check(const iq_config *cfg, int32_t batch, int32_t num_q_heads, int64_t max_kv_len,
+                           size_t *need) {
+  int st = check_config(cfg);
+  if (st != IQ_OK) return st;
+  if (!decode_codebook_exact(cfg)) return IQ_ERR_UNSUPPORTED;
+  if (batch < 1 || num_q_heads < 1 || max_kv_len < 0) return IQ_ERR_INVALID_ARG;
+  if (batch > kMaxDecodeBatch) return IQ_ERR_UNSUPPORTED;
+  if (num_q_heads % cfg->num_kv_heads) return IQ_ERR_INVALID_ARG;
+  const int group = num_q_heads / cfg->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return IQ_ERR_UNSUPPORTED;
+  *need = iq_decode_workspace_bytes(cfg, batch, num_q_heads, max_kv_len);
+  return *need > 0 ? IQ_OK : IQ_ERR_UNSUPPORTED;
+}
+}  // namespace iq
+}
+
 static int check_decode_common(const iq_config *cfg, int32_t batch, int32_t num_q_heads,
                                int64_t max_kv_len, const void *workspace, size_t workspace_bytes,
                                int *group) {

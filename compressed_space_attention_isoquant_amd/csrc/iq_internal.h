@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "decode_args.h"
+#include "iq.h"
 
 namespace iq {
 
@@ -83,6 +84,11 @@ hipError_t launch_dequantize(int d, int bits, int variant, int out_f16, const De
 hipError_t launch_rope_copy(int in_f16, const RopeArgs &a, hipStream_t s);
 hipError_t launch_decode(int d, int bits, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge(int d, int variant, const MergeArgs &a, hipStream_t s);
+// Validation of the decode sizes shared by every decode entry point: the
+// status iq_decode_attention would return for them, and the workspace bytes
+// they need.
+int decode_workspace_check(const iq_config *cfg, int32_t batch, int32_t num_q_heads, int64_t max_kv_len,
+                           size_t *need);
 // Workgroups of the partial (split) kernel one compute unit holds at once.
 int decode_groups_per_cu(int d, int bits, int rope);
 

@@ -27,7 +27,9 @@
  * Conventions shared by every entry point
  *   - Every pointer is DEVICE memory owned by the caller unless marked HOST.
  *     The library never allocates device memory and keeps no mutable global
- *     state; calls on different streams may run concurrently.
+ *     state (except iq_decode_attention_noalloc's fixed workspace array and
+ *     its per-device address); calls on different streams may run
+ *     concurrently (except iq_decode_attention_noalloc calls, see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without host synchronisation.
  *   - Arguments are validated before anything is enqueued; a negative
@@ -277,6 +279,26 @@ int iq_decode_attention_merge(const iq_config *cfg, int32_t batch, int32_t num_q
                               float *lse_out, int32_t *argmax_out,
                               const void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* iq_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without the workspace, which
+ * comes from a fixed array of 64 MiB inside this library, one per GPU,
+ * held from the library's load until the process ends (its device address is
+ * looked up on the first call on each device).  The call allocates nothing.
+ * Sizes whose iq_decode_workspace_bytes exceeds 64 MiB return
+ * IQ_ERR_WORKSPACE (64 sequences x 32 query / 4 KV heads at d = 128 need
+ * about 20 MiB); other errors as iq_decode_attention, IQ_ERR_HIP if the
+ * array's address cannot be found.  All calls on one GPU share the array:
+ * calls that overlap on one GPU (on different streams, or from several
+ * threads) race and must not be made; calls on one stream run in order.
+ * Nothing in the array needs to start at zero. */
+int iq_decode_attention_noalloc(const iq_config *cfg, const void *q, int32_t q_dtype,
+                                int32_t batch, int32_t num_q_heads,
+                                const iq_cache *k, const iq_cache *v,
+                                const int32_t *kv_len, int64_t max_kv_len,
+                                float softmax_scale, void *out, int32_t out_dtype,
+                                float *lse_out, int32_t *argmax_out, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *iq_status_string(int status);
