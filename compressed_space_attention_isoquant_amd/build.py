@@ -75,6 +75,50 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# The host-side argument checks of api.cpp built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (host code only, by the LLVM that ships with
+# ROCm, as plain C++), linked with the device objects of build().  Loaded into
+# a Python process, it needs the sanitizer runtime preloaded (LD_PRELOAD).
+HOSTSAN_LIB = os.path.join(BUILD, "libiq_hostsan.so")
+
+
+def _rocm_clang() -> str:
+    for cand in ("/opt/rocm/llvm/bin/clang++", "/opt/rocm/lib/llvm/bin/clang++"):
+        if os.path.exists(cand):
+            return cand
+    raise RuntimeError("ROCm clang++ not found")
+
+
+def hostsan_runtime() -> str:
+    """Path of the ASan runtime the sanitized library links against."""
+    r = subprocess.run([_rocm_clang(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True, check=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("ASan runtime not found")
+    return path
+
+
+def build_host_sanitized() -> str:
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s != "api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose=False)
+    clang = _rocm_clang()
+    api_obj = os.path.join(BUILD, "api_hostsan.o")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libsan"]
+    cmd = [clang, "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{INCLUDE}", f"-I{CSRC}",
+           "-fPIC", "-g", "-O1", "-fno-omit-frame-pointer", *san, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized compile of api.cpp failed:\n{r.stderr}")
+    cmd = [clang, "-shared", "-fPIC", *san, api_obj, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", HOSTSAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr}")
+    return HOSTSAN_LIB
+
+
 if __name__ == "__main__":
     build()
     sys.exit(0)

@@ -39,16 +39,23 @@ constexpr int kDecodeRope = 64;            // RoPE coordinates per key the decod
 constexpr int kMinTilesPerWave = 8;        // a wave's share is at least this many tiles
 constexpr int kMaxDecodeWaves = 4096;      // waves of the partial launch at most (256 CUs x 16)
 constexpr int kPrepThreads = 256;
+static_assert(kMaxDecodeWaves % kPrepThreads == 0 && (kPrepThreads & (kPrepThreads - 1)) == 0, "plan lookup");
 
 // Plan written by the prep kernel at the start of the workspace.
 struct DecodePlan {
   int total;          // tiles of all segments
   int per_wave;       // W, tiles per wave (the last busy wave may have fewer)
   int pad_[2];
-  // then: int seg_base[batch + 1] (tile index of segment (b, 0); the last
-  //       entry is total, so sequence b has (seg_base[b + 1] - seg_base[b]) /
-  //       H_kv tiles per KV head), and
-  //       int start_seg[kMaxDecodeWaves] (the segment holding tile w W)
+  // then: WaveShare share[kMaxDecodeWaves], and int seg_base[batch + 1]
+  //       (tile index of segment (b, 0); the last entry is total, so
+  //       sequence b has (seg_base[b + 1] - seg_base[b]) / H_kv tiles per KV
+  //       head)
+};
+
+// Where wave w starts: segment s = b H_kv + h, tile i0 of that segment, its
+// `count` tiles (0 for a wave without work), and the sequence's length.
+struct WaveShare {
+  int seg, i0, count, len;
 };
 
 struct DecodeArgs {
@@ -69,7 +76,7 @@ struct DecodeArgs {
   int n_waves;             // waves of the partial launch
   float qmul;              // softmax_scale * log2(e) / 2^cexp, applied to R q
   int argmax;              // track the position of the largest score
-  DecodePlan *plan;        // workspace: plan, segment bases, start segments
+  DecodePlan *plan;        // workspace: plan header, wave shares, segment bases
   uint16_t *qrot;          // workspace: [batch][H_kv][2G][d + rope] fp16, hi rows then lo rows
   float *qscale;           // workspace: [batch][H_kv] 2^-f, the scale of the rows of q~
   float *ws;               // workspace: records [(batch H_kv + n_waves) G][d + kRecHeader]
@@ -88,13 +95,13 @@ struct MergeArgs {
   float oscale;            // 2^-cexp
 };
 
-// Workspace layout: the plan (header, segment bases, start segments), the
+// Workspace layout: the plan (header, wave shares, segment bases), the
 // rotated queries (sized for kDecodeRope RoPE coordinates whether or not a
 // call has them), their scales (batch x Hq floats, at least batch x H_kv),
 // the records; each part 256-byte aligned.
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 inline size_t decode_plan_bytes(int32_t batch) {
-  return align256(sizeof(DecodePlan) + sizeof(int) * ((size_t)batch + 1 + kMaxDecodeWaves));
+  return align256(sizeof(DecodePlan) + sizeof(WaveShare) * kMaxDecodeWaves + sizeof(int) * ((size_t)batch + 1));
 }
 inline size_t decode_qrot_bytes(int32_t batch, int32_t hq, int d, int rope) {
   return align256((size_t)batch * hq * 2 * (d + rope) * sizeof(uint16_t));

@@ -265,19 +265,23 @@ constexpr int partial_waves() {
 // ---------------------------------------------------------------------------
 
 // Workgroup 0: tiles per segment, their prefix over the sequences (segment
-// (b, h) starts at seg_base[b] + h * tiles(b)), the per-wave share W and, for
-// every busy wave w, the segment holding its first tile w W.
+// (b, h) starts at seg_base[b] + h * tiles(b)), the per-wave share W and
+// every wave's starting point, so that a partial wave begins with one load.
+// Thread t owns sequences [t per, (t + 1) per); the inclusive scan of the
+// threads' tile counts locates the owner of any tile by binary search.
 __device__ void plan_work(const DecodeArgs &a) {
   __shared__ int part[kPrepThreads];
-  int *seg_base = reinterpret_cast<int *>(a.plan + 1);
-  int *start_seg = seg_base + a.batch + 1;
+  __shared__ int first_len[kPrepThreads];
+  WaveShare *share = reinterpret_cast<WaveShare *>(a.plan + 1);
+  int *seg_base = reinterpret_cast<int *>(share + kMaxDecodeWaves);
   const int t = threadIdx.x;
   const int per = (a.batch + kPrepThreads - 1) / kPrepThreads;
   const int b0 = min(a.batch, t * per), b1 = min(a.batch, b0 + per);
-  auto tiles = [&](int b) { return (a.kv_len[b] + kDecodeStep - 1) / kDecodeStep; };
+  auto tiles = [](int len) { return (len + kDecodeStep - 1) / kDecodeStep; };
   int mine = 0;
-  for (int b = b0; b < b1; ++b) mine += a.hkv * tiles(b);
+  for (int b = b0; b < b1; ++b) mine += a.hkv * tiles(a.kv_len[b]);
   part[t] = mine;
+  first_len[t] = b0 < b1 ? a.kv_len[b0] : 0;
   __syncthreads();
   // inclusive scan of the per-thread sums (Hillis-Steele)
   for (int off = 1; off < kPrepThreads; off <<= 1) {
@@ -290,18 +294,38 @@ __device__ void plan_work(const DecodeArgs &a) {
   const int W = max(kMinTilesPerWave, (total + a.n_waves - 1) / a.n_waves);
   int base = part[t] - mine;
   for (int b = b0; b < b1; ++b) {
-    const int n = tiles(b);
     seg_base[b] = base;
-    for (int h = 0; h < a.hkv && n > 0; ++h) {
-      const int s0 = base + h * n;
-      for (int w = (s0 + W - 1) / W; w * W < s0 + n; ++w) start_seg[w] = b * a.hkv + h;
-    }
-    base += a.hkv * n;
+    base += a.hkv * tiles(a.kv_len[b]);
   }
   if (t == 0) {
     a.plan->total = total;
     a.plan->per_wave = W;
     seg_base[a.batch] = total;
+  }
+  // wave w starts at tile T = w W (no work when T >= total)
+#pragma unroll
+  for (int k = 0; k < kMaxDecodeWaves / kPrepThreads; ++k) {
+    const int w = t + k * kPrepThreads;
+    if (w >= a.n_waves) break;
+    const int T = w * W;
+    WaveShare sh{0, 0, 0, 0};
+    if (T < total) {
+      // owner u: the first thread whose inclusive sum exceeds T
+      int u = 0;
+#pragma unroll
+      for (int step = kPrepThreads / 2; step > 0; step >>= 1)
+        if (part[u + step - 1] <= T) u += step;
+      int b = u * per, at = u > 0 ? part[u - 1] : 0, len = first_len[u];
+      int n = tiles(len);
+      while (T >= at + a.hkv * n) {         // only when a thread owns several sequences
+        at += a.hkv * n;
+        len = a.kv_len[++b];
+        n = tiles(len);
+      }
+      const int off = T - at, h = off / n;
+      sh = WaveShare{b * a.hkv + h, off - h * n, min(W, total - T), len};
+    }
+    share[w] = sh;
   }
 }
 
@@ -421,14 +445,12 @@ void partial_kernel(DecodeArgs a) {
   for (int i = threadIdx.x; i < TB / 4; i += kThreads) lut[i] = a.lut[i / REPL];
   __syncthreads();                           // the kernel's only barrier: before any wave leaves
 
-  // this wave's share of the tiles: [t_begin, t_end)
+  // this wave's share of the tiles: `count` tiles from tile i0 of segment seg
   const int w = (int)blockIdx.x * kDecodeWaves + wave;
-  const int total = a.plan->total, W = a.plan->per_wave;
-  const int t_begin = w * W;
-  if (t_begin >= total) return;
-  const int t_end = min(total, t_begin + W);
-  const int *seg_base = reinterpret_cast<const int *>(a.plan + 1);
-  const int *start_seg = seg_base + a.batch + 1;
+  const WaveShare my = reinterpret_cast<const WaveShare *>(a.plan + 1)[w];
+  const int count = __builtin_amdgcn_readfirstlane(my.count);
+  if (count <= 0) return;
+  const int t_begin = 0, t_end = count;      // the share's tiles, counted from its first
 
   // A position in the tile sequence: sequence b, KV head h, tile i of the
   // segment's n tiles (len tokens).  Wave-uniform.
@@ -438,12 +460,12 @@ void partial_kernel(DecodeArgs a) {
   auto seq_len = [&](int b) { return __builtin_amdgcn_readfirstlane(a.kv_len[b]); };
   Cursor c0;
   {
-    const int s = __builtin_amdgcn_readfirstlane(start_seg[w]);
+    const int s = __builtin_amdgcn_readfirstlane(my.seg);
     c0.b = s / a.hkv;
     c0.h = s - c0.b * a.hkv;
-    c0.len = seq_len(c0.b);
+    c0.len = __builtin_amdgcn_readfirstlane(my.len);
     c0.n = (c0.len + kDecodeStep - 1) / kDecodeStep;
-    c0.i = t_begin - (__builtin_amdgcn_readfirstlane(seg_base[c0.b]) + c0.h * c0.n);
+    c0.i = __builtin_amdgcn_readfirstlane(my.i0);
   }
   // the next tile (one exists whenever this is called)
   auto advance = [&](Cursor &c) {
@@ -882,7 +904,7 @@ constexpr int kMergeChunk = 1024;          // records whose weights are staged i
 // summing every NP-th piece, so that many records' loads are in flight.
 template <int D>
 constexpr int merge_threads() {
-  return D < 256 ? 256 : D;
+  return 512;
 }
 
 template <int D, int VARIANT>
@@ -897,7 +919,8 @@ __global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(MergeArgs a) 
   const int tid = threadIdx.x;
   const int i = tid % D, part = tid / D;
   // the records of this segment's pieces: s + first .. s + last, G records apart
-  const int *seg_base = reinterpret_cast<const int *>(a.plan + 1);
+  const int *seg_base = reinterpret_cast<const int *>(reinterpret_cast<const WaveShare *>(a.plan + 1) +
+                                                      kMaxDecodeWaves);
   const int nt = (seg_base[b + 1] - seg_base[b]) / a.hkv;      // tiles per KV head of sequence b
   const int W = a.plan->per_wave;
   const long long s = (long long)b * a.hkv + g;

@@ -191,9 +191,11 @@ int iq_dequantize(const iq_config *cfg, const iq_cache *in, int32_t batch,
                   int32_t out_dtype, hipStream_t stream);
 
 /* Bytes of workspace iq_decode_attention needs for these sizes.  Returns 0 if
- * the arguments are invalid.  O(batch * Hq * splits * d) floats of split
- * records plus 8 bytes per (sequence, split) for the work order: never
- * O(T * d) -- the decode path writes no dequantized K or V, the
+ * the arguments are invalid.  A work plan (64 KiB plus 4 bytes per sequence),
+ * the rotated queries (about 4 (d + 64) bytes per query head), and
+ * (batch * H_kv + 4096) * (Hq / H_kv) partial records of d + 4 floats; the
+ * size does not depend on max_kv_len and is never O(T * d) -- the decode
+ * path writes no dequantized K or V, the
  * zero-materialization property RotaryQuant Appendix D confirms with its
  * instrumentation counters (no decompress or key-read calls). */
 size_t iq_decode_workspace_bytes(const iq_config *cfg, int32_t batch,
@@ -253,11 +255,12 @@ int iq_decode_attention_rope(const iq_config *cfg, const void *q, int32_t q_dtyp
                              void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* Split phase of iq_decode_attention (the context is cut into splits, as in
+/* Split phase of iq_decode_attention (the context is cut into pieces, as in
  * FlashAttention's tiling that RotaryQuant §2 cites): rotates each query once,
  * scores the packed K rows and accumulates the packed V rows in rotated space,
- * and leaves one partial softmax state per (sequence, query head, split) in
- * `workspace`.  Arguments as for iq_decode_attention; track_argmax != 0 also
+ * and leaves one partial softmax state per (query head, piece) in
+ * `workspace`, where the pieces are equal shares of all sequences' 32-token
+ * tiles, cut at sequence and KV-head boundaries.  Arguments as for iq_decode_attention; track_argmax != 0 also
  * records the position of the largest score (otherwise the merge reports -1
  * as every argmax).  The workspace content is opaque and valid only for a
  * merge call with the same cfg, batch, num_q_heads and max_kv_len. */

@@ -10,6 +10,12 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
+# Another build of the same library (the host-sanitized one of
+# test_host_sanitizers.py) may stand in for lib/libiq.so.
+if os.environ.get("IQ_TEST_LIBRARY"):
+    from compressed_space_attention_isoquant_amd import binding as _binding
+    _binding.LIB_PATH = os.environ["IQ_TEST_LIBRARY"]
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

@@ -245,14 +245,14 @@ def test_partial_and_merge_validation():
 
 def expected_workspace(batch, hq, hkv, d, max_len):
     """Workspace bytes from the documented layout, each part rounded up to
-    256 bytes: the plan (a 16-byte header, batch + 1 segment bases and 4096
-    per-wave start segments, int32), the rotated queries (2 fp16 rows of
+    256 bytes: the plan (a 16-byte header, 4096 per-wave shares of four
+    int32 and batch + 1 int32 segment bases), the rotated queries (2 fp16 rows of
     d + 64 coordinates per query head), their scales (one float per query
     head), then the records: d + 4 floats per query head of a group for each
     of batch x H_kv + 4096 pieces.  No term grows with max_len."""
     up = lambda x: -(-x // 256) * 256
     group = hq // hkv
-    plan = up(16 + 4 * (batch + 1 + 4096))
+    plan = up(16 + 16 * 4096 + 4 * (batch + 1))
     qrot = up(batch * hq * 2 * (d + 64) * 2)
     qscale = up(batch * hq * 4)
     records = (batch * hkv + 4096) * group * (d + 4) * 4
