@@ -36,7 +36,8 @@ constexpr int kRecHeader = 4;              // M, L, best score, best position
 constexpr float kLazyTau = 4.0f;           // rescale only when the max grows by more than this
 constexpr float kWeightBias = 25.0f;       // weights 2^(s - M + bias) * ||v|| stay below 2^15
 constexpr int kDecodeRope = 64;            // RoPE coordinates per key the decode kernels take
-constexpr int kMinTilesPerWave = 8;        // a wave's share is at least this many tiles
+constexpr int kMinTilesPerWave = 2;        // a wave's share is at least this many tiles
+constexpr int kMaxPiecesPerSegment = 256;  // and large enough that no segment has more pieces
 constexpr int kMaxDecodeWaves = 4096;      // waves of the partial launch at most (256 CUs x 16)
 constexpr int kPrepThreads = 256;
 static_assert(kMaxDecodeWaves % kPrepThreads == 0 && (kPrepThreads & (kPrepThreads - 1)) == 0, "plan lookup");

@@ -271,6 +271,7 @@ constexpr int partial_waves() {
 // threads' tile counts locates the owner of any tile by binary search.
 __device__ void plan_work(const DecodeArgs &a) {
   __shared__ int part[kPrepThreads];
+  __shared__ int most[kPrepThreads];
   __shared__ int first_len[kPrepThreads];
   WaveShare *share = reinterpret_cast<WaveShare *>(a.plan + 1);
   int *seg_base = reinterpret_cast<int *>(share + kMaxDecodeWaves);
@@ -278,20 +279,30 @@ __device__ void plan_work(const DecodeArgs &a) {
   const int per = (a.batch + kPrepThreads - 1) / kPrepThreads;
   const int b0 = min(a.batch, t * per), b1 = min(a.batch, b0 + per);
   auto tiles = [](int len) { return (len + kDecodeStep - 1) / kDecodeStep; };
-  int mine = 0;
-  for (int b = b0; b < b1; ++b) mine += a.hkv * tiles(a.kv_len[b]);
+  int mine = 0, longest = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int n = tiles(a.kv_len[b]);
+    mine += a.hkv * n;
+    longest = max(longest, n);
+  }
   part[t] = mine;
+  most[t] = longest;
   first_len[t] = b0 < b1 ? a.kv_len[b0] : 0;
   __syncthreads();
-  // inclusive scan of the per-thread sums (Hillis-Steele)
+  // inclusive scans of the per-thread sums and maxima (Hillis-Steele)
   for (int off = 1; off < kPrepThreads; off <<= 1) {
     const int v = t >= off ? part[t - off] : 0;
+    const int m = t >= off ? most[t - off] : 0;
     __syncthreads();
     part[t] += v;
+    most[t] = max(most[t], m);
     __syncthreads();
   }
   const int total = part[kPrepThreads - 1];
-  const int W = max(kMinTilesPerWave, (total + a.n_waves - 1) / a.n_waves);
+  // W: every tile within n_waves shares, no segment cut into more than
+  // kMaxPiecesPerSegment pieces (the merge reads one record per piece)
+  const int W = max(max(kMinTilesPerWave, (total + a.n_waves - 1) / a.n_waves),
+                    (most[kPrepThreads - 1] + kMaxPiecesPerSegment - 1) / kMaxPiecesPerSegment);
   int base = part[t] - mine;
   for (int b = b0; b < b1; ++b) {
     seg_base[b] = base;
