@@ -35,6 +35,7 @@ deferred-prefill compression.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -240,7 +241,12 @@ def workload_record(w, r, traffic_name):
                                      "median": round(float(np.median(per)), 5),
                                      "max": round(float(np.max(per)), 5),
                                      "cv": round(float(np.std(per) / np.mean(per)), 4),
-                                     "first_steps": [round(float(x), 5) for x in per[:5]]},
+                                     "first_steps": [round(float(x), 5) for x in per[:5]],
+                                     # the slowest steps with the host time their enqueue took
+                                     "slowest_steps": [{"step": int(i), "ms": round(float(per[i]), 5),
+                                                        "host_enqueue_ms": round(float(r["host_enqueue_ms"][i]), 4)}
+                                                       for i in np.argsort(per)[::-1][:3]],
+                                     "host_enqueue_ms_median": round(float(np.median(r["host_enqueue_ms"])), 4)},
         "roofline": {
             "bound": "hbm",
             "achieved": round(r["achieved"], 2),
@@ -317,16 +323,24 @@ def run_decode_workload(torch, dev, w, steps, warmup):
     # the step's K and V appends in one launch (same rotation, two caches)
     append_kv = [B.prepare_append_many([cfg, cfg], [knew[s], vnew[s]], [kc, vc]) for s in range(P)]
 
+    # host time spent enqueuing each timed split phase: a step whose events
+    # are far apart while its enqueue took long was held up by the host, not
+    # by the GPU
+    host_ms = []
+    step_events = [_events(torch) for _ in range(steps)]
+
     def step(g, record):
         s = g % P
         append_kv[s](pos_dev[g])
         if record:
-            e0, e1 = _events(torch)
+            e0, e1 = step_events[g - warmup]
             e0.record(stream)
+            h0 = time.perf_counter()
         # the two phases of iq_decode_attention, so that the events bracket the
         # split (dominant) phase alone
         B.iq_decode_attention_partial(cfg, qs[s], kc, vc, len_dev[g], max_len[g], scale, ws, track_argmax=False)
         if record:
+            host_ms.append((time.perf_counter() - h0) * 1e3)
             e1.record(stream)
             events.append((e0, e1))
         B.iq_decode_attention_merge(cfg, batch, hq, max_len[g], out, lse, None, ws)
@@ -334,11 +348,16 @@ def run_decode_workload(torch, dev, w, steps, warmup):
     for g in range(warmup):
         step(g, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for g in range(warmup, n_total):
-        step(g, True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    gc.collect()
+    gc.disable()                             # no collector pauses inside the timed steps
+    try:
+        t0 = time.perf_counter()
+        for g in range(warmup, n_total):
+            step(g, True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    finally:
+        gc.enable()
     ms_per_step = (t1 - t0) * 1e3 / steps
     per_step = np.array([a.elapsed_time(b) for a, b in events])
     partial_ms = float(per_step.mean())
@@ -353,7 +372,7 @@ def run_decode_workload(torch, dev, w, steps, warmup):
     del kc, vc, ws
     return dict(value=value, ms_per_step=ms_per_step, partial_ms=partial_ms, achieved=achieved,
                 attn_bytes_per_step=attn_bytes.mean(), partial_bytes_per_launch=partial_bytes.mean(),
-                lengths=lens, per_step_ms=per_step)
+                lengths=lens, per_step_ms=per_step, host_enqueue_ms=np.array(host_ms))
 
 
 def run_fresh_headline(steps, warmup):

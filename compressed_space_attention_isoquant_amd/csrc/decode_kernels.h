@@ -910,25 +910,24 @@ void partial_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int kMergeChunk = 1024;          // records whose weights are staged in LDS at a time
+constexpr int kMergeThreads = 256;
 
-// Threads of a merge workgroup: head_dim columns times NP parts, each part
-// summing every NP-th piece, so that many records' loads are in flight.
-template <int D>
-constexpr int merge_threads() {
-  return 512;
-}
-
+// One workgroup per (query head, sequence).  Thread t sums four neighbouring
+// coordinates (one 16-byte load per record) over every NP-th piece, so that
+// many loads are in flight however few or many pieces the segment has.
 template <int D, int VARIANT>
-__global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   constexpr int RS = D + kRecHeader;
-  constexpr int NT = merge_threads<D>();
-  constexpr int NP = NT / D;
+  constexpr int NT = kMergeThreads;
+  constexpr int C4 = D / 4;                  // float4 columns of o~
+  constexpr int NP = NT / C4;                // parts
+  static_assert(NT % C4 == 0 && RS % 4 == 0, "merge geometry");
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int G = a.group;
   const int g = h / G, hh = h - g * G;
   const int tid = threadIdx.x;
-  const int i = tid % D, part = tid / D;
+  const int c = tid % C4, part = tid / C4;
   // the records of this segment's pieces: s + first .. s + last, G records apart
   const int *seg_base = reinterpret_cast<const int *>(reinterpret_cast<const WaveShare *>(a.plan + 1) +
                                                       kMaxDecodeWaves);
@@ -948,7 +947,8 @@ __global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(MergeArgs a) 
   __shared__ float redf[NW];
   __shared__ int redi[NW];
   __shared__ float wbuf[kMergeChunk];
-  __shared__ float part_o[NP][D];
+  __shared__ __attribute__((aligned(16))) float part_o[NP][D];
+  __shared__ float y[D];
   const int lane = tid & 63, wave = tid >> 6;
   // (score, position) pairs: the larger score, ties to the lower valid position
   auto better = [](float s1, int p1, float s0, int p0) {
@@ -962,13 +962,12 @@ __global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(MergeArgs a) 
   float Mt = -INFINITY, bt = -INFINITY;
   int at = -1;
   for (int p = tid; p < n; p += NT) {
-    const float *rec = recs + (size_t)p * stride;
-    if (rec[1] > 0.f) {
-      Mt = fmaxf(Mt, rec[0]);
-      const float sc = rec[2];
-      const int pos = __builtin_bit_cast(int, rec[3]);
-      if (better(sc, pos, bt, at)) {
-        bt = sc;
+    const float4 hd = *reinterpret_cast<const float4 *>(recs + (size_t)p * stride);
+    if (hd.y > 0.f) {
+      Mt = fmaxf(Mt, hd.x);
+      const int pos = __builtin_bit_cast(int, hd.w);
+      if (better(hd.z, pos, bt, at)) {
+        bt = hd.z;
         at = pos;
       }
     }
@@ -1001,52 +1000,55 @@ __global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(MergeArgs a) 
   __syncthreads();
 
   // Weights 2^(M_p - M) (0 for empty pieces) staged in LDS chunk by chunk;
-  // each thread then sums its coordinate over its part's records, with
+  // each thread then sums its four coordinates over its part's records with
   // independent loads, and the parts are added in LDS.
-  float Lt = 0.f, o = 0.f;
+  float Lt = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
     const int cn = min(kMergeChunk, n - c0);
     for (int p = tid; p < cn; p += NT) {
-      const float *rec = recs + (size_t)(c0 + p) * stride;
-      const float lp = rec[1];
-      const float w = lp > 0.f ? exp2f(rec[0] - M) : 0.f;
+      const float2 hd = *reinterpret_cast<const float2 *>(recs + (size_t)(c0 + p) * stride);
+      const float w = hd.y > 0.f ? exp2f(hd.x - M) : 0.f;
       wbuf[p] = w;
-      Lt += lp > 0.f ? lp * w : 0.f;
+      Lt += hd.y > 0.f ? hd.y * w : 0.f;
     }
     __syncthreads();
-    const float *col = recs + (size_t)c0 * stride + kRecHeader + i;
-#pragma unroll 8
+    const float4 *col = reinterpret_cast<const float4 *>(recs + (size_t)c0 * stride + kRecHeader) + c;
+#pragma unroll 4
     for (int p = part; p < cn; p += NP) {
       const float w = wbuf[p];
-      const float v = col[(size_t)p * stride];
-      o += w > 0.f ? v * w : 0.f;
+      const float4 v = col[(size_t)p * (stride / 4)];
+      o.x += w > 0.f ? v.x * w : 0.f;
+      o.y += w > 0.f ? v.y * w : 0.f;
+      o.z += w > 0.f ? v.z * w : 0.f;
+      o.w += w > 0.f ? v.w * w : 0.f;
     }
     __syncthreads();
   }
-  part_o[part][i] = o;
+  *reinterpret_cast<float4 *>(&part_o[part][4 * c]) = o;
   for (int m = 32; m > 0; m >>= 1) Lt += __shfl_xor(Lt, m, 64);
   if (lane == 0) redf[wave] = Lt;
   __syncthreads();
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) L += redf[w];
-  if (part == 0) {
+  for (int i = tid; i < D; i += NT) {
+    float sum = 0.f;
 #pragma unroll
-    for (int q = 1; q < NP; ++q) o += part_o[q][i];
+    for (int q = 0; q < NP; ++q) sum += part_o[q][i];
+    y[i] = L > 0.f ? sum * a.oscale / L : 0.f;
   }
-
-  __shared__ float y[D];
-  if (part == 0) y[i] = L > 0.f ? o * a.oscale / L : 0.f;
   __syncthreads();
   if (tid < D / 4) {
     const float *pg = a.quats + (size_t)g * (D / 4) * block_param_floats(VARIANT);
-    float4 u = block_inv<VARIANT>(make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]), pg, i);
-    y[4 * i] = u.x;
-    y[4 * i + 1] = u.y;
-    y[4 * i + 2] = u.z;
-    y[4 * i + 3] = u.w;
+    float4 u = block_inv<VARIANT>(make_float4(y[4 * tid], y[4 * tid + 1], y[4 * tid + 2], y[4 * tid + 3]), pg, tid);
+    y[4 * tid] = u.x;
+    y[4 * tid + 1] = u.y;
+    y[4 * tid + 2] = u.z;
+    y[4 * tid + 3] = u.w;
   }
   __syncthreads();
+  static_assert(D / 2 <= NT, "one butterfly per thread");
   for (int st = 1; st < D; st <<= 1) {
     float x0 = 0.f, x1 = 0.f;
     int lo = 0;
@@ -1062,15 +1064,15 @@ __global__ __launch_bounds__(merge_threads<D>()) void merge_kernel(MergeArgs a) 
     }
     __syncthreads();
   }
-  if (part != 0) return;
-  const float val = y[i] / sqrtf((float)D);
-  const size_t off = ((size_t)b * a.hq + h) * D + i;
-  if (a.out_f16)
-    static_cast<_Float16 *>(a.out)[off] = static_cast<_Float16>(val);
-  else
-    static_cast<float *>(a.out)[off] = val;
-  if (i == 0) {
-    const size_t oh = (size_t)b * a.hq + h;
+  const size_t oh = (size_t)b * a.hq + h;
+  for (int i = tid; i < D; i += NT) {
+    const float val = y[i] / sqrtf((float)D);
+    if (a.out_f16)
+      static_cast<_Float16 *>(a.out)[oh * D + i] = static_cast<_Float16>(val);
+    else
+      static_cast<float *>(a.out)[oh * D + i] = val;
+  }
+  if (tid == 0) {
     if (a.lse) a.lse[oh] = L > 0.f ? (M - kWeightBias + log2f(L)) * 0.69314718055994531f : -INFINITY;
     if (a.argmax) a.argmax[oh] = L > 0.f ? arg : -1;
   }
@@ -1158,9 +1160,9 @@ template <int D>
 hipError_t merge_dispatch(int variant, const MergeArgs &a, hipStream_t s) {
   dim3 grid((unsigned)a.hq, (unsigned)a.batch);
   switch (variant) {
-    case 0: hipLaunchKernelGGL((merge_kernel<D, 0>), grid, dim3(merge_threads<D>()), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(merge_threads<D>()), 0, s, a); break;
-    case kPlanar: hipLaunchKernelGGL((merge_kernel<D, kPlanar>), grid, dim3(merge_threads<D>()), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((merge_kernel<D, 0>), grid, dim3(kMergeThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(kMergeThreads), 0, s, a); break;
+    case kPlanar: hipLaunchKernelGGL((merge_kernel<D, kPlanar>), grid, dim3(kMergeThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
