@@ -313,28 +313,38 @@ __device__ void plan_work(const DecodeArgs &a) {
     a.plan->per_wave = W;
     seg_base[a.batch] = total;
   }
-  // wave w starts at tile T = w W (no work when T >= total)
+  // Wave w starts at tile T = w W (no work when T >= total).  Thread t
+  // serves waves t + k kPrepThreads; the owners of its KP starting tiles are
+  // found by binary searches run in lockstep, so that their LDS reads overlap.
+  constexpr int KP = kMaxDecodeWaves / kPrepThreads;
+  int T[KP], u[KP];
 #pragma unroll
-  for (int k = 0; k < kMaxDecodeWaves / kPrepThreads; ++k) {
+  for (int k = 0; k < KP; ++k) {
+    T[k] = min(t + k * kPrepThreads, a.n_waves) * W;    // n_waves W stays below 2^31
+    u[k] = 0;
+  }
+#pragma unroll
+  for (int step = kPrepThreads / 2; step > 0; step >>= 1) {
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+      if (part[u[k] + step - 1] <= T[k]) u[k] += step;   // the first thread whose inclusive sum exceeds T
+  }
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
     const int w = t + k * kPrepThreads;
     if (w >= a.n_waves) break;
-    const int T = w * W;
     WaveShare sh{0, 0, 0, 0};
-    if (T < total) {
-      // owner u: the first thread whose inclusive sum exceeds T
-      int u = 0;
-#pragma unroll
-      for (int step = kPrepThreads / 2; step > 0; step >>= 1)
-        if (part[u + step - 1] <= T) u += step;
-      int b = u * per, at = u > 0 ? part[u - 1] : 0, len = first_len[u];
+    if (T[k] < total) {
+      const int o = u[k];
+      int b = o * per, at = o > 0 ? part[o - 1] : 0, len = first_len[o];
       int n = tiles(len);
-      while (T >= at + a.hkv * n) {         // only when a thread owns several sequences
+      while (T[k] >= at + a.hkv * n) {      // only when a thread owns several sequences
         at += a.hkv * n;
         len = a.kv_len[++b];
         n = tiles(len);
       }
-      const int off = T - at, h = off / n;
-      sh = WaveShare{b * a.hkv + h, off - h * n, min(W, total - T), len};
+      const int off = T[k] - at, h = off / n;
+      sh = WaveShare{b * a.hkv + h, off - h * n, min(W, total - T[k]), len};
     }
     share[w] = sh;
   }
@@ -346,7 +356,13 @@ __device__ void rotate_queries(const DecodeArgs &a, int r) {
   static_assert(kPrepThreads == 256, "four waves");
   constexpr int DQ = D + ROPE;
   __shared__ float qs[G][DQ];
+  __shared__ __attribute__((aligned(16))) float qp[D / 4 * 8];    // the KV head's block parameters
   const int b = r / a.hkv, kvh = r - b * a.hkv;
+  {
+    const int np = D / 4 * block_param_floats(a.variant);
+    const float *src = a.quats + (size_t)kvh * np;
+    for (int idx = threadIdx.x; idx < np; idx += kPrepThreads) qp[idx] = src[idx];
+  }
   for (int idx = threadIdx.x; idx < G * DQ; idx += kPrepThreads) {
     const int hh = idx / DQ, i = idx % DQ;
     const size_t off = ((size_t)b * a.hq + kvh * G + hh) * DQ + i;
@@ -365,7 +381,7 @@ __device__ void rotate_queries(const DecodeArgs &a, int r) {
     __syncthreads();
   }
   const float scale = a.qmul / sqrtf((float)D);
-  const float *pg = a.quats + (size_t)kvh * (D / 4) * block_param_floats(a.variant);
+  const float *pg = qp;
   for (int p = threadIdx.x; p < G * D / 4; p += kPrepThreads) {
     const int hh = p / (D / 4), blk = p % (D / 4);
     float4 v = make_float4(qs[hh][4 * blk] * scale, qs[hh][4 * blk + 1] * scale, qs[hh][4 * blk + 2] * scale,
