@@ -116,6 +116,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// A load from an LDS byte address (the constant part of an address folds
+// into the instruction's offset field).
+template <typename T>
+__device__ __forceinline__ T lds_ld(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T *>(addr);
+}
+
 // Layout of one wave's LDS stage: 32 packed K rows, 32 packed V rows, 32 K
 // norms, 32 V norms, and with ROPE > 0 the keys' 32 fp16 RoPE rows.  Rows sit
 // RS = ROWB + PAD bytes apart; PAD (0 or one 16-byte granule) is chosen per
@@ -264,55 +271,69 @@ constexpr int partial_waves() {
 // prep kernel
 // ---------------------------------------------------------------------------
 
-// Workgroup 0: tiles per segment, their prefix over the sequences (segment
-// (b, h) starts at seg_base[b] + h * tiles(b)), the per-wave share W and
-// every wave's starting point, so that a partial wave begins with one load.
-// Thread t owns sequences [t per, (t + 1) per); the inclusive scan of the
-// threads' tile counts locates the owner of any tile by binary search.
+// Workgroup 0: tiles per segment, their prefix (segment s = b H_kv + h starts
+// at seg_base[b] + h tiles(b)), the per-wave share W and every wave's
+// starting point, so that a partial wave begins with one load.  Thread t owns
+// segments [t per, (t + 1) per); the inclusive scan of the threads' tile
+// counts (lane exchanges within each wave, one barrier across the waves)
+// locates the owner of any tile by binary search.
 __device__ void plan_work(const DecodeArgs &a) {
+  static_assert(kPrepThreads == 256, "four waves");
   __shared__ int part[kPrepThreads];
-  __shared__ int most[kPrepThreads];
   __shared__ int first_len[kPrepThreads];
+  __shared__ int wsum[4], wmax[4];
   WaveShare *share = reinterpret_cast<WaveShare *>(a.plan + 1);
   int *seg_base = reinterpret_cast<int *>(share + kMaxDecodeWaves);
-  const int t = threadIdx.x;
-  const int per = (a.batch + kPrepThreads - 1) / kPrepThreads;
-  const int b0 = min(a.batch, t * per), b1 = min(a.batch, b0 + per);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int nseg = a.batch * a.hkv;
+  const int per = (nseg + kPrepThreads - 1) / kPrepThreads;
+  const int s0 = min(nseg, t * per), s1 = min(nseg, s0 + per);
   auto tiles = [](int len) { return (len + kDecodeStep - 1) / kDecodeStep; };
-  int mine = 0, longest = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int n = tiles(a.kv_len[b]);
-    mine += a.hkv * n;
-    longest = max(longest, n);
+  int mine = 0, longest = 0, len0 = 0;
+  for (int sg = s0, len = 0; sg < s1; ++sg) {
+    if (sg == s0 || sg % a.hkv == 0) len = a.kv_len[sg / a.hkv];
+    if (sg == s0) len0 = len;
+    mine += tiles(len);
+    longest = max(longest, len);
   }
-  part[t] = mine;
-  most[t] = longest;
-  first_len[t] = b0 < b1 ? a.kv_len[b0] : 0;
+  first_len[t] = len0;
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) longest = max(longest, __shfl_xor(longest, o, 64));
+  if (lane == 63) wsum[wave] = incl;
+  if (lane == 0) wmax[wave] = longest;
   __syncthreads();
-  // inclusive scans of the per-thread sums and maxima (Hillis-Steele)
-  for (int off = 1; off < kPrepThreads; off <<= 1) {
-    const int v = t >= off ? part[t - off] : 0;
-    const int m = t >= off ? most[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    most[t] = max(most[t], m);
-    __syncthreads();
-  }
-  const int total = part[kPrepThreads - 1];
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < wave ? wsum[w] : 0;
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const int most = tiles(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+  part[t] = before + incl;
   // W: every tile within n_waves shares, no segment cut into more than
   // kMaxPiecesPerSegment pieces (the merge reads one record per piece)
   const int W = max(max(kMinTilesPerWave, (total + a.n_waves - 1) / a.n_waves),
-                    (most[kPrepThreads - 1] + kMaxPiecesPerSegment - 1) / kMaxPiecesPerSegment);
-  int base = part[t] - mine;
-  for (int b = b0; b < b1; ++b) {
-    seg_base[b] = base;
-    base += a.hkv * tiles(a.kv_len[b]);
+                    (most + kMaxPiecesPerSegment - 1) / kMaxPiecesPerSegment);
+  {
+    int base = before + incl - mine;
+    for (int sg = s0, len = len0; sg < s1; ++sg) {
+      if (sg % a.hkv == 0) {
+        if (sg != s0) len = a.kv_len[sg / a.hkv];
+        seg_base[sg / a.hkv] = base;
+      }
+      base += tiles(len);
+    }
   }
   if (t == 0) {
     a.plan->total = total;
     a.plan->per_wave = W;
     seg_base[a.batch] = total;
   }
+  __syncthreads();
   // Wave w starts at tile T = w W (no work when T >= total).  Thread t
   // serves waves t + k kPrepThreads; the owners of its KP starting tiles are
   // found by binary searches run in lockstep, so that their LDS reads overlap.
@@ -336,89 +357,131 @@ __device__ void plan_work(const DecodeArgs &a) {
     WaveShare sh{0, 0, 0, 0};
     if (T[k] < total) {
       const int o = u[k];
-      int b = o * per, at = o > 0 ? part[o - 1] : 0, len = first_len[o];
-      int n = tiles(len);
-      while (T[k] >= at + a.hkv * n) {      // only when a thread owns several sequences
-        at += a.hkv * n;
-        len = a.kv_len[++b];
-        n = tiles(len);
+      int sg = o * per, at = o > 0 ? part[o - 1] : 0, len = first_len[o];
+      while (T[k] >= at + tiles(len)) {    // only when a thread owns several segments
+        at += tiles(len);
+        ++sg;
+        if (sg % a.hkv == 0) len = a.kv_len[sg / a.hkv];
       }
-      const int off = T[k] - at, h = off / n;
-      sh = WaveShare{b * a.hkv + h, off - h * n, min(W, total - T[k]), len};
+      sh = WaveShare{sg, T[k] - at, min(W, total - T[k]), len};
     }
     share[w] = sh;
   }
 }
 
-// Other workgroups: q~ for the G query heads of (sequence, KV head) r.
+// Other workgroups: q~ for the G query heads of (sequence, KV head) r.  Each
+// half-wave rotates one query head in registers: lane l of the half holds the
+// D/32 consecutive coordinates from l D/32 (the SO(4) blocks stay inside a
+// lane), the WHT runs its in-lane butterflies and then five lane-exchange
+// stages, lower index first at every stage as in the Sylvester order.  One
+// barrier, for the scale below.
 template <int D, int ROPE, int G>
 __device__ void rotate_queries(const DecodeArgs &a, int r) {
-  static_assert(kPrepThreads == 256, "four waves");
+  static_assert(kPrepThreads == 256 && G <= 8, "four waves, two heads each");
   constexpr int DQ = D + ROPE;
-  __shared__ float qs[G][DQ];
-  __shared__ __attribute__((aligned(16))) float qp[D / 4 * 8];    // the KV head's block parameters
+  constexpr int E = D / 32;                  // content coordinates per lane
+  constexpr int ER = ROPE / 32;              // RoPE coordinates per lane
+  constexpr int NBL = E / 4;                 // SO(4) blocks per lane
+  static_assert(E % 4 == 0 && ROPE % 32 == 0, "lane layout");
   const int b = r / a.hkv, kvh = r - b * a.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31;
+  const int hh = 2 * wave + (lane >> 5);     // query head of the group
+  const bool act = hh < G;
+  const size_t qoff = ((size_t)b * a.hq + kvh * G + (act ? hh : 0)) * DQ;
+  float x[E], xr[ER > 0 ? ER : 1];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const size_t o = qoff + li * E + e;
+    const float v = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[o]) : static_cast<const float *>(a.q)[o];
+    x[e] = act ? v : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < ER; ++e) {
+    const size_t o = qoff + D + li * ER + e;
+    const float v = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[o]) : static_cast<const float *>(a.q)[o];
+    xr[e] = act ? v * a.rmul : 0.f;
+  }
+  // this lane's block parameters (Full/Fast: q_L, q_R; Planar: two pair rotations)
+  float4 prm[NBL][2];
   {
-    const int np = D / 4 * block_param_floats(a.variant);
-    const float *src = a.quats + (size_t)kvh * np;
-    for (int idx = threadIdx.x; idx < np; idx += kPrepThreads) qp[idx] = src[idx];
-  }
-  for (int idx = threadIdx.x; idx < G * DQ; idx += kPrepThreads) {
-    const int hh = idx / DQ, i = idx % DQ;
-    const size_t off = ((size_t)b * a.hq + kvh * G + hh) * DQ + i;
-    qs[hh][i] = a.q_f16 ? static_cast<float>(static_cast<const _Float16 *>(a.q)[off])
-                        : static_cast<const float *>(a.q)[off];
-  }
-  __syncthreads();
-  for (int st = 1; st < D; st <<= 1) {
-    for (int p = threadIdx.x; p < G * D / 2; p += kPrepThreads) {
-      const int hh = p / (D / 2), pp = p % (D / 2);
-      const int i = (pp / st) * 2 * st + (pp % st);
-      const float x0 = qs[hh][i], x1 = qs[hh][i + st];
-      qs[hh][i] = x0 + x1;
-      qs[hh][i + st] = x0 - x1;
+    const float4 *pg = reinterpret_cast<const float4 *>(a.quats + (size_t)kvh * (D / 4) * block_param_floats(a.variant));
+#pragma unroll
+    for (int k = 0; k < NBL; ++k) {
+      const int blk = li * NBL + k;
+      if (a.variant == kPlanar) {
+        prm[k][0] = pg[blk];
+        prm[k][1] = prm[k][0];
+      } else {
+        prm[k][0] = pg[2 * blk];
+        prm[k][1] = pg[2 * blk + 1];
+      }
     }
-    __syncthreads();
+  }
+#pragma unroll
+  for (int st = 1; st < E; st <<= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (!(e & st)) {
+        const float x0 = x[e], x1 = x[e + st];
+        x[e] = x0 + x1;
+        x[e + st] = x0 - x1;
+      }
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    const bool upper = li & m;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float y = __shfl_xor(x[e], m, 64);
+      x[e] = upper ? y - x[e] : x[e] + y;
+    }
   }
   const float scale = a.qmul / sqrtf((float)D);
-  const float *pg = qp;
-  for (int p = threadIdx.x; p < G * D / 4; p += kPrepThreads) {
-    const int hh = p / (D / 4), blk = p % (D / 4);
-    float4 v = make_float4(qs[hh][4 * blk] * scale, qs[hh][4 * blk + 1] * scale, qs[hh][4 * blk + 2] * scale,
-                           qs[hh][4 * blk + 3] * scale);
-    float4 t = a.variant == 0 ? block_fwd<0>(v, pg, blk)
-               : a.variant == 1 ? block_fwd<1>(v, pg, blk) : block_fwd<kPlanar>(v, pg, blk);
-    qs[hh][4 * blk] = t.x;
-    qs[hh][4 * blk + 1] = t.y;
-    qs[hh][4 * blk + 2] = t.z;
-    qs[hh][4 * blk + 3] = t.w;
+#pragma unroll
+  for (int k = 0; k < NBL; ++k) {
+    const float4 v = make_float4(x[4 * k] * scale, x[4 * k + 1] * scale, x[4 * k + 2] * scale, x[4 * k + 3] * scale);
+    const float4 t = a.variant == 0   ? so4_fwd<0>(v, prm[k][0], prm[k][1])
+                     : a.variant == 1 ? so4_fwd<1>(v, prm[k][0], prm[k][1])
+                                      : planar_fwd(v, prm[k][0]);
+    x[4 * k] = t.x;
+    x[4 * k + 1] = t.y;
+    x[4 * k + 2] = t.z;
+    x[4 * k + 3] = t.w;
   }
-  for (int idx = threadIdx.x; idx < G * ROPE; idx += kPrepThreads) {
-    const int hh = idx / (ROPE > 0 ? ROPE : 1), i = D + idx % (ROPE > 0 ? ROPE : 1);
-    qs[hh][i] *= a.rmul;
-  }
-  __syncthreads();
-  // Power-of-two scale 2^f bringing the largest |q~| into [2^13, 2^14): the
-  // fp16 hi and lo parts then hold every coordinate down to 2^-17 of the
-  // largest to 22 bits (unscaled, the small coordinates' lo parts fall into
-  // the fp16 subnormals and lose most of their bits); the partial kernel
-  // works in scores times 2^f and applies 2^-f where it needs true units.
+  // Power-of-two scale 2^f bringing the largest |q~| of the G heads into
+  // [2^13, 2^14): the fp16 hi and lo parts then hold every coordinate down to
+  // 2^-17 of the largest to 22 bits (unscaled, the small coordinates' lo
+  // parts fall into the fp16 subnormals and lose most of their bits); the
+  // partial kernel works in scores times 2^f and applies 2^-f where it needs
+  // true units.
   __shared__ float redm[kPrepThreads / 64];
   float m = 0.f;
-  for (int idx = threadIdx.x; idx < G * DQ; idx += kPrepThreads) m = fmaxf(m, fabsf(qs[idx / DQ][idx % DQ]));
+#pragma unroll
+  for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+  for (int e = 0; e < ER; ++e) m = fmaxf(m, fabsf(xr[e]));
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((threadIdx.x & 63) == 0) redm[threadIdx.x >> 6] = m;
+  if (lane == 0) redm[wave] = m;
   __syncthreads();
   m = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
   const int f = m > 0.f ? 13 - ilogbf(m) : 0;
   const float up = ldexpf(1.f, f);
   _Float16 *dst = reinterpret_cast<_Float16 *>(a.qrot) + (size_t)r * 2 * G * DQ;
-  for (int idx = threadIdx.x; idx < G * DQ; idx += kPrepThreads) {
-    const int hh = idx / DQ, i = idx % DQ;
-    const float v = qs[hh][i] * up;
-    const _Float16 hi = static_cast<_Float16>(v);
-    dst[hh * DQ + i] = hi;
-    dst[(G + hh) * DQ + i] = static_cast<_Float16>(v - static_cast<float>(hi));
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float v = x[e] * up;
+      const _Float16 hi = static_cast<_Float16>(v);
+      dst[hh * DQ + li * E + e] = hi;
+      dst[(G + hh) * DQ + li * E + e] = static_cast<_Float16>(v - static_cast<float>(hi));
+    }
+#pragma unroll
+    for (int e = 0; e < ER; ++e) {
+      const float v = xr[e] * up;
+      const _Float16 hi = static_cast<_Float16>(v);
+      dst[hh * DQ + D + li * ER + e] = hi;
+      dst[(G + hh) * DQ + D + li * ER + e] = static_cast<_Float16>(v - static_cast<float>(hi));
+    }
   }
   if (threadIdx.x == 0) a.qscale[r] = ldexpf(1.f, -f);
 }
@@ -625,33 +688,37 @@ void partial_kernel(DecodeArgs a) {
   };
   set_mask(kDecodeStep);
 
-  // One 32-token tile from stage `cur`: tokens t0 .. t0 + 31 of a segment
-  // (masked by mbias).
-  auto process = [&](const char *cur, const int t0) {
+  // One 32-token tile from the stage at LDS address `cur`: tokens t0 .. t0 +
+  // 31 of a segment (masked by mbias).  Each operand's reads share one lane
+  // base address, their constant offsets going into the instructions.
+  auto process = [&](const uint32_t cur, const int t0) {
     // packed K rows of the two 16-token tiles (lane: token j, dims slice g4)
+    const uint32_t kbase = cur + k_off;
     uint32_t kw[2][CW];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + k_off + tile * 16 * S::RS);
 #pragma unroll
       for (int m = 0; m < CW / UDW; ++m)
 #pragma unroll
-        for (int t = 0; t < UDW; ++t) kw[tile][m * UDW + t] = src[4 * m * UDW + t];
+        for (int t = 0; t < UDW; ++t)
+          kw[tile][m * UDW + t] = lds_ld<uint32_t>(kbase + tile * 16 * S::RS + (4 * m * UDW + t) * 4);
     }
     // the 8 tokens of this lane in the operand/result layouts: 4*g4 + r of each tile
+    const uint32_t vbase = cur + v_off;
     uint32_t vch[8][VX];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(cur + v_off + (16 * (r >> 2) + (r & 3)) * S::RS);
       uint32_t w[VW];
 #pragma unroll
-      for (int i = 0; i < VW; ++i) w[i] = src[i];            // may read one dword past the row: still in LDS
+      for (int i = 0; i < VW; ++i)                           // may read one dword past the row: still in LDS
+        w[i] = lds_ld<uint32_t>(vbase + (16 * (r >> 2) + (r & 3)) * S::RS + 4 * i);
 #pragma unroll
       for (int i = 0; i < VX; ++i) vch[r][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], vbit & 31);
     }
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-    const u16x4 kb = *reinterpret_cast<const u16x4 *>(cur + S::KN_OFF + n_off);
-    const u16x4 vb = *reinterpret_cast<const u16x4 *>(cur + S::VN_OFF + n_off);
+    const uint32_t nbase = cur + n_off;
+    const u16x4 kb = lds_ld<u16x4>(nbase + S::KN_OFF);
+    const u16x4 vb = lds_ld<u16x4>(nbase + S::VN_OFF);
 
     // Table reads for both operands are issued up front, so that their
     // latency overlaps the score products and the softmax.
@@ -735,8 +802,7 @@ void partial_kernel(DecodeArgs a) {
         SR[tile] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < RK; ++s) {
-          const half8 kr8 = *reinterpret_cast<const half8 *>(cur + S::R_OFF + (16 * tile + j) * S::RRS +
-                                                             (32 * s + 8 * g4) * 2);
+          const half8 kr8 = lds_ld<half8>(cur + S::R_OFF + (16 * tile + j) * S::RRS + (32 * s + 8 * g4) * 2);
           SR[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr8, qR[s], SR[tile], 0, 0, 0);
         }
       }
@@ -905,7 +971,7 @@ void partial_kernel(DecodeArgs a) {
     const bool seg_last = cp.i == cp.n - 1;
     const int tail = cp.len - cp.i * kDecodeStep;       // tokens of the segment from this tile on
     if (seg_last && tail < kDecodeStep) set_mask(tail);
-    process(stages + slot * S::BYTES, cp.i * kDecodeStep);
+    process(stages_lds + slot * S::BYTES, cp.i * kDecodeStep);
     if (seg_last || tp + 1 == t_end) write_record(cp);
     if (tp + 1 < t_end) {
       advance(cp);
@@ -925,7 +991,8 @@ void partial_kernel(DecodeArgs a) {
 // merge kernel
 // ---------------------------------------------------------------------------
 
-constexpr int kMergeChunk = 1024;          // records whose weights are staged in LDS at a time
+constexpr int kMergeChunk = 1024;          // pieces of one segment the merge holds in LDS
+static_assert(kMaxPiecesPerSegment + 1 <= kMergeChunk, "a segment's pieces fit the merge's LDS");
 constexpr int kMergeThreads = 256;
 
 // One workgroup per (query head, sequence).  Thread t sums four neighbouring
@@ -955,14 +1022,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   if (nt > 0) {
     const int S0 = seg_base[b] + g * nt;
     const int first = S0 / W, last = (S0 + nt - 1) / W;
-    n = last - first + 1;
+    n = min(last - first + 1, kMergeChunk);   // at most kMaxPiecesPerSegment + 1 by the plan's W
     recs = a.ws + ((s + first) * G + hh) * RS;
   }
   const size_t stride = (size_t)G * RS;       // from one piece's record to the next
   constexpr int NW = NT / 64;                // waves of the workgroup
   __shared__ float redf[NW];
   __shared__ int redi[NW];
-  __shared__ float wbuf[kMergeChunk];
+  __shared__ float reds[NW];
+  __shared__ float hm[kMergeChunk], hl[kMergeChunk];      // each piece's M and L
   __shared__ __attribute__((aligned(16))) float part_o[NP][D];
   __shared__ float y[D];
   const int lane = tid & 63, wave = tid >> 6;
@@ -970,15 +1038,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   auto better = [](float s1, int p1, float s0, int p0) {
     return s1 > s0 || (s1 == s0 && p1 >= 0 && (p0 < 0 || p1 < p0));
   };
+  // the coordinates of this thread's first KPF records, requested before the
+  // headers are reduced (they do not depend on them)
+  constexpr int KPF = 4;
+  const float4 *col = reinterpret_cast<const float4 *>(recs + kRecHeader) + c;
+  const size_t stride4 = stride / 4;
+  float4 pre[KPF];
+#pragma unroll
+  for (int k = 0; k < KPF; ++k) {
+    const int p = part + k * NP;
+    pre[k] = p < n ? col[(size_t)p * stride4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 
-  // Headers are read in parallel (thread t: records t, t + NT, ...): the
-  // running maximum and the best score with its position (ties: the lower
-  // position; pieces cover increasing positions).  Reductions: across the
-  // wave by lane exchanges, then across the waves through LDS.
+  // Headers are read in parallel (thread t: records t, t + NT, ...) and kept
+  // in LDS: the running maximum and the best score with its position (ties:
+  // the lower position; pieces cover increasing positions).  Reductions:
+  // across the wave by lane exchanges, then across the waves through LDS.
   float Mt = -INFINITY, bt = -INFINITY;
   int at = -1;
   for (int p = tid; p < n; p += NT) {
     const float4 hd = *reinterpret_cast<const float4 *>(recs + (size_t)p * stride);
+    hm[p] = hd.x;
+    hl[p] = hd.y;
     if (hd.y > 0.f) {
       Mt = fmaxf(Mt, hd.x);
       const int pos = __builtin_bit_cast(int, hd.w);
@@ -1000,47 +1081,41 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   if (lane == 0) {
     redf[wave] = Mt;
     redi[wave] = at;
-    wbuf[wave] = bt;                         // wbuf is free until the weights below
+    reds[wave] = bt;
   }
   __syncthreads();
-  float M = redf[0], bsc = wbuf[0];
+  float M = redf[0], bsc = reds[0];
   int arg = redi[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
     M = fmaxf(M, redf[w]);
-    if (better(wbuf[w], redi[w], bsc, arg)) {
-      bsc = wbuf[w];
+    if (better(reds[w], redi[w], bsc, arg)) {
+      bsc = reds[w];
       arg = redi[w];
     }
   }
-  __syncthreads();
+  __syncthreads();                           // redf is reused below
 
-  // Weights 2^(M_p - M) (0 for empty pieces) staged in LDS chunk by chunk;
-  // each thread then sums its four coordinates over its part's records with
-  // independent loads, and the parts are added in LDS.
+  // Weights 2^(M_p - M) (0 for empty pieces) from the headers in LDS; each
+  // thread sums its four coordinates over its part's records, and the parts
+  // are added in LDS.
+  auto weight = [&](int p) { return hl[p] > 0.f ? exp2f(hm[p] - M) : 0.f; };
   float Lt = 0.f;
+  for (int p = tid; p < n; p += NT) Lt += hl[p] > 0.f ? hl[p] * weight(p) : 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
-    const int cn = min(kMergeChunk, n - c0);
-    for (int p = tid; p < cn; p += NT) {
-      const float2 hd = *reinterpret_cast<const float2 *>(recs + (size_t)(c0 + p) * stride);
-      const float w = hd.y > 0.f ? exp2f(hd.x - M) : 0.f;
-      wbuf[p] = w;
-      Lt += hd.y > 0.f ? hd.y * w : 0.f;
-    }
-    __syncthreads();
-    const float4 *col = reinterpret_cast<const float4 *>(recs + (size_t)c0 * stride + kRecHeader) + c;
-#pragma unroll 4
-    for (int p = part; p < cn; p += NP) {
-      const float w = wbuf[p];
-      const float4 v = col[(size_t)p * (stride / 4)];
-      o.x += w > 0.f ? v.x * w : 0.f;
-      o.y += w > 0.f ? v.y * w : 0.f;
-      o.z += w > 0.f ? v.z * w : 0.f;
-      o.w += w > 0.f ? v.w * w : 0.f;
-    }
-    __syncthreads();
+  auto add = [&](float w, const float4 &v) {
+    o.x += w > 0.f ? v.x * w : 0.f;
+    o.y += w > 0.f ? v.y * w : 0.f;
+    o.z += w > 0.f ? v.z * w : 0.f;
+    o.w += w > 0.f ? v.w * w : 0.f;
+  };
+#pragma unroll
+  for (int k = 0; k < KPF; ++k) {
+    const int p = part + k * NP;
+    if (p < n) add(weight(p), pre[k]);
   }
+#pragma unroll 4
+  for (int p = part + KPF * NP; p < n; p += NP) add(weight(p), col[(size_t)p * stride4]);
   *reinterpret_cast<float4 *>(&part_o[part][4 * c]) = o;
   for (int m = 32; m > 0; m >>= 1) Lt += __shfl_xor(Lt, m, 64);
   if (lane == 0) redf[wave] = Lt;

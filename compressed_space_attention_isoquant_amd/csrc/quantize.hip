@@ -148,12 +148,19 @@ __device__ __forceinline__ void dpp_fmac8(float (&r)[32], float sign) {
 }
 #undef IQ_DPP_FMAC8
 
+// In-lane strides below 2^F of the transform are applied inside the block
+// matrices (F = 2 for Full and Fast: the 4-point transform of each block; 1 for
+// Planar, whose 2x2 blocks absorb the stride-1 butterflies and stay 2x2):
+// the butterflies of every stride commute, so x -> M H4 (rest of H) x is the
+// same map, and the block's 16 multiply-adds replace two butterfly stages.
+__host__ __device__ constexpr int fold_stages(int variant) { return variant == kPlanar ? 1 : 2; }
+
 // Lane distances 1, 2 and 8 ride on the multiply-add (DPP operand), 4 and 16
-// go through the swizzle.
-template <int LPV>
+// go through the swizzle.  In-lane strides start at H0.
+template <int LPV, int H0>
 __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
 #pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
+  for (int h = H0; h < 32; h <<= 1) {
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       if ((k & h) == 0) {
@@ -181,19 +188,27 @@ __device__ __forceinline__ void wht_butterflies(float (&r)[32], int j) {
   });
 }
 
-// Columns of the 4x4 matrices of the forward block rotations: column c of
-// block gb = 8 j + blk (held by lane j of a vector) is block_fwd(e_c), times
-// lane_sign(j) when SIGNED, stored at qm[blk][c][j] so that the lanes of a
-// vector read consecutive 16-byte words (no LDS bank conflicts).  The inverse
-// rotation is the transpose of the unsigned matrix.
+// Columns of the 4x4 matrices M H_F of the forward block rotations M after
+// the folded butterflies H_F (the 2^F-point transform on each 2^F-element
+// sub-block): column c of block gb = 8 j + blk (held by lane j of a vector)
+// is block_fwd(H_F e_c), times lane_sign(j) when SIGNED, stored at
+// qm[blk][c][j] so that the lanes of a vector read consecutive 16-byte words
+// (no LDS bank conflicts).  The inverse is the transpose of the unsigned
+// matrix: (M H_F)^T = H_F M^T, the inverse block rotation followed by the
+// folded butterflies.
 template <int LPV>
 using BlockMatrices = float4[8][4][LPV];
 
 template <int D, int VARIANT, bool SIGNED>
 __device__ __forceinline__ void load_block_matrices(BlockMatrices<D / 32> &qm, const float *params) {
+  constexpr int F = fold_stages(VARIANT), SUB = (1 << F) - 1;
   for (int i = threadIdx.x; i < D; i += blockDim.x) {
     const int gb = i >> 2, c = i & 3;
-    const float4 e = make_float4(c == 0, c == 1, c == 2, c == 3);
+    // column c of H_F: (-1)^popcount(k & c) inside c's sub-block, 0 outside
+    auto hf = [&](int k) {
+      return (k & ~SUB) == (c & ~SUB) ? ((__builtin_popcount(k & c & SUB) & 1) ? -1.f : 1.f) : 0.f;
+    };
+    const float4 e = make_float4(hf(0), hf(1), hf(2), hf(3));
     float4 col = block_fwd<VARIANT>(e, params, gb);
     if (SIGNED && lane_sign<D / 32>(gb >> 3) < 0.f) col = make_float4(-col.x, -col.y, -col.z, -col.w);
     qm[gb & 7][c][gb >> 3] = col;
@@ -277,15 +292,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   cur.init((int)blockIdx.x * VPB + wave * VPW + lane / LPV, n);
   nxt = cur;
   nxt.advance(sq, sr, n);
-  TIn xn[32];
-  int spn;
-  fetch(cur, xn, spn);
-  for (long long v0 = (long long)blockIdx.x * VPB; v0 < nvec; v0 += stride) {
-    TIn xin[32];
-#pragma unroll
-    for (int k = 0; k < 32; ++k) xin[k] = xn[k];
-    const int sp = spn;
-    fetch(nxt, xn, spn);
+  // One vector (input xin, append position sp) at cur; the next one's loads
+  // go to the other buffer before this one's stores.
+  auto body = [&](const TIn (&xin)[32], const int sp) {
 
     // s = ||x||_2 (fp32 sum of squares: four interleaved partial sums per
     // lane, then a tree over the vector's lanes)
@@ -295,16 +304,20 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     float ss = (sp4[0] + sp4[1]) + (sp4[2] + sp4[3]);
 #pragma unroll
     for (int m = 1; m < LPV; m <<= 1) ss += shfl_xor(ss, m);
-    const float s = sqrtf(ss);
+    // the hardware square root and reciprocal (within an ulp or so): the norm
+    // is rounded to fp16 anyway, and codes are exact only up to the fp32
+    // rounding of the transform
+    const float s = __builtin_amdgcn_sqrtf(ss);
     // x^ = x / s folded with the 1/sqrt(d) of the normalised transform
-    const float inv = s > 0.f ? 1.0f / (s * sqrtf((float)D)) : 0.f;
+    const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s * sqrtf((float)D)) : 0.f;
     float r[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) r[k] = (float)xin[k] * inv;
 
-    wht_butterflies<LPV>(r, j);
+    wht_butterflies<LPV, (1 << fold_stages(VARIANT))>(r, j);
 
-    // block rotations; the matrices carry the butterflies' lane sign
+    // block rotations after the folded butterflies; the matrices carry the
+    // butterflies' lane sign
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       float4 t = mat_vec<VARIANT>(qm[blk][0][j], qm[blk][1][j], qm[blk][2][j], qm[blk][3][j],
@@ -371,6 +384,17 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     T.norms[row] = float_to_half_bits(s);
     cur = nxt;
     nxt.advance(sq, sr, n);
+  };
+  // two input buffers in turn, so that no registers are copied per vector
+  TIn xa[32], xb[32];
+  int spa, spb;
+  fetch(cur, xa, spa);
+  for (long long v0 = (long long)blockIdx.x * VPB; v0 < nvec; v0 += 2 * (long long)stride) {
+    fetch(nxt, xb, spb);
+    body(xa, spa);
+    if (v0 + stride >= nvec) break;
+    fetch(nxt, xa, spa);
+    body(xb, spb);
   }
 }
 
@@ -469,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
       r[4 * blk + 3] = u.w;
     }
 
-    wht_butterflies<LPV>(r, j);
+    wht_butterflies<LPV, (1 << fold_stages(VARIANT))>(r, j);
 
     const float scale = lane_sign<LPV>(j) * s16 / sqrtf((float)D);
 #pragma unroll
