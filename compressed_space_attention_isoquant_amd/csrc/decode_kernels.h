@@ -486,12 +486,78 @@ __device__ void rotate_queries(const DecodeArgs &a, int r) {
   if (threadIdx.x == 0) a.qscale[r] = ldexpf(1.f, -f);
 }
 
+// The plan for at most kPrepThreads segments, computed by every workgroup of
+// the prep launch (thread t takes segment t; the segment lengths are a few
+// cached loads): workgroup r of nwg writes the starts of waves r, r + nwg,
+// ..., and the segment base of segment r's sequence if r is its first
+// segment, so that no workgroup waits for another.
+__device__ void plan_small(const DecodeArgs &a, int r, int nwg) {
+  static_assert(kPrepThreads == 256, "four waves");
+  __shared__ int part[kPrepThreads], lens[kPrepThreads];
+  __shared__ int wsum[4], wmax[4];
+  WaveShare *share = reinterpret_cast<WaveShare *>(a.plan + 1);
+  int *seg_base = reinterpret_cast<int *>(share + kMaxDecodeWaves);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int nseg = a.batch * a.hkv;
+  auto tiles = [](int len) { return (len + kDecodeStep - 1) / kDecodeStep; };
+  const int len = t < nseg ? a.kv_len[t / a.hkv] : 0;
+  const int mine = tiles(len);
+  int incl = mine, longest = len;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) longest = max(longest, __shfl_xor(longest, o, 64));
+  if (lane == 63) wsum[wave] = incl;
+  if (lane == 0) wmax[wave] = longest;
+  lens[t] = len;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < wave ? wsum[w] : 0;
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const int most = tiles(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+  part[t] = before + incl;
+  const int W = max(max(kMinTilesPerWave, (total + a.n_waves - 1) / a.n_waves),
+                    (most + kMaxPiecesPerSegment - 1) / kMaxPiecesPerSegment);
+  if (t == r && r % a.hkv == 0) seg_base[r / a.hkv] = before + incl - mine;
+  if (r == 0 && t == 0) {
+    a.plan->total = total;
+    a.plan->per_wave = W;
+    seg_base[a.batch] = total;
+  }
+  __syncthreads();
+  for (int w = r + nwg * t; w < a.n_waves; w += nwg * kPrepThreads) {
+    const int T = w * W;
+    WaveShare sh{0, 0, 0, 0};
+    if (T < total) {
+      int u = 0;                             // the first segment whose inclusive sum exceeds T
+#pragma unroll
+      for (int step = kPrepThreads / 2; step > 0; step >>= 1)
+        if (part[u + step - 1] <= T) u += step;
+      sh = WaveShare{u, T - (part[u] - tiles(lens[u])), min(W, total - T), lens[u]};
+    }
+    share[w] = sh;
+  }
+}
+
+// Up to kPrepThreads segments every workgroup plans (its share of the wave
+// starts) and rotates the queries of one segment; beyond that workgroup 0
+// plans alone.
+__host__ __device__ inline bool plan_in_every_group(int batch, int hkv) { return batch * hkv <= kPrepThreads; }
+
 template <int D, int ROPE, int G>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(DecodeArgs a) {
-  if (blockIdx.x == 0)
+  if (plan_in_every_group(a.batch, a.hkv)) {
+    plan_small(a, (int)blockIdx.x, (int)gridDim.x);
+    rotate_queries<D, ROPE, G>(a, (int)blockIdx.x);
+  } else if (blockIdx.x == 0) {
     plan_work(a);
-  else
+  } else {
     rotate_queries<D, ROPE, G>(a, (int)blockIdx.x - 1);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1183,7 +1249,7 @@ constexpr bool partial_fits() {
 
 template <int D, int ROPE>
 hipError_t prep_dispatch(const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid(1 + (unsigned)(a.batch * a.hkv));
+  const dim3 grid((plan_in_every_group(a.batch, a.hkv) ? 0u : 1u) + (unsigned)(a.batch * a.hkv));
   switch (a.group) {
     case 1: hipLaunchKernelGGL((prep_kernel<D, ROPE, 1>), grid, dim3(kPrepThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((prep_kernel<D, ROPE, 2>), grid, dim3(kPrepThreads), 0, s, a); break;
