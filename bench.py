@@ -364,7 +364,7 @@ def run_decode_workload(torch, dev, w, steps, warmup):
     kv = np.array([float((lens + grow * g).sum()) * hkv * 2 * (rb + 2) for g in range(warmup, n_total)])
     qo = batch * hq * d * 2
     attn_bytes = kv + 2 * qo                 # packed K/V with norms read, q read, o written
-    partial_bytes = kv + qo                  # the split phase reads K/V and q; its partial states are O(splits*d)
+    partial_bytes = kv + qo                  # the split phase reads K/V and q; its partial states are O(pieces*d)
     value = attn_bytes.sum() / (t1 - t0) / 1e9
     achieved = partial_bytes.mean() / (partial_ms * 1e-3) / 1e9
     print(f"[bench] {w['name']}: step {ms_per_step:.4f} ms, split phase {partial_ms:.4f} ms, "

@@ -140,7 +140,7 @@ def test_decode_validation():
     cc = c.c()
     need = L.iq_decode_workspace_bytes(ctypes.byref(cc), 1, 32, 16)
     assert need > 0
-    # workspace is O(splits x d) per query head, never O(T x d)
+    # workspace is O(pieces x d) per query head, never O(T x d)
     big = L.iq_decode_workspace_bytes(ctypes.byref(cc), 64, 32, 32768)
     assert big < 64 * 4 * 32768 * 128 * 2 // 16
     assert L.iq_decode_workspace_bytes(ctypes.byref(cc), 1, 30, 16) == 0

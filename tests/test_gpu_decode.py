@@ -209,10 +209,10 @@ def test_decode_fp32_io_sweep(d, bits, variant, group):
 def test_argmax_ties_lowest_position():
     """Exact score ties (identical K rows) resolve to the lowest position
     wherever the tied tokens meet in the kernel: in one tile on the two halves
-    of the score tile (5, 20), in different lane groups (1, 6), in different
-    tiles of one workgroup that different waves take (32, 128), and in
-    different context splits or work ranges (300, 20000, 32767).  One 32K
-    sequence, 32 query / 4 KV heads (the needle-search shape)."""
+    of the score tile (5, 20), in different lane groups (1, 6), in the shares
+    of different waves (32, 128; the merge compares their pieces), and far
+    apart in the context (300, 20000, 32767).  One 32K sequence, 32 query / 4
+    KV heads (the needle-search shape)."""
     d, bits, hq, hkv, T = 128, 3, 32, 4, 32768
     case = inputs.decode_case(seed=31, kv_len=T, num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
     k, q = case["k"], case["q"]
@@ -289,8 +289,9 @@ def test_decode_custom_codebook_at_range_edge(bits, io):
 
 
 def test_split_geometry_invariance():
-    """The same attention with different max_kv_len (hence different split-K
-    geometry) agrees with the oracle each time."""
+    """The same attention with different max_kv_len (a host-side bound only:
+    the work plan comes from the device-side lengths) agrees with the oracle
+    each time."""
     d, bits, hq, hkv, T = 128, 3, 16, 2, 5000
     case = inputs.decode_case(seed=13, kv_len=T, num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
     cfg, quats = make_config(d, bits, O.FAST, hkv)
