@@ -332,6 +332,29 @@ def test_many_short_sequences():
     assert np.all(got[lens == 0] == 0)
 
 
+@pytest.mark.parametrize("batch,hkv,hq", [(128, 2, 4), (257, 1, 2)])
+def test_plan_at_the_segment_count_boundary(batch, hkv, hq):
+    """256 (sequence, KV head) segments, planned by every prep workgroup,
+    and 257, planned by one: ragged lengths with empty sequences and a few
+    long ones (shares cross segment boundaries), every sequence against the
+    oracle, argmax included."""
+    d, bits, cap = 128, 3, 1024
+    rng = np.random.default_rng(29 + batch)
+    lens = rng.integers(0, 200, size=batch)
+    lens[rng.choice(batch, 8, replace=False)] = 0
+    lens[rng.choice(batch, 3, replace=False)] = rng.integers(600, cap + 1, size=3)
+    cfg, quats = make_config(d, bits, O.FULL, hkv)
+    k = rng.standard_normal((batch, cap, hkv, d)).astype(np.float16)
+    v = rng.standard_normal((batch, cap, hkv, d)).astype(np.float16)
+    q = rng.standard_normal((batch, hq, d)).astype(np.float16)
+    kc = quantize_rows(cfg, k)
+    vc = quantize_rows(cfg, v)
+    got, lse, arg = run_decode(cfg, q, kc, vc, lens, cap)
+    ref, rlse, rarg = oracle_decode(q, k, v, quats, cfg, lens, host_cache(kc), host_cache(vc))
+    check_outputs(f"plan boundary batch={batch} hkv={hkv}", got, lse, arg, ref, rlse, rarg, 2e-3, check_arg=True)
+    assert np.all(got[lens == 0] == 0) and np.all(arg[lens == 0] == -1)
+
+
 def test_max_decode_batch():
     """The largest batch a decode call takes (65535 sequences of 0..4
     tokens): sampled sequences against the oracle, the empty ones exact."""
