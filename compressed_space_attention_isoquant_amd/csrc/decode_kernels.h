@@ -1057,7 +1057,7 @@ void partial_kernel(DecodeArgs a) {
 // merge kernel
 // ---------------------------------------------------------------------------
 
-constexpr int kMergeChunk = 1024;          // pieces of one segment the merge holds in LDS
+constexpr int kMergeChunk = kMaxPiecesPerSegment + 8;   // pieces of one segment the merge holds in LDS
 static_assert(kMaxPiecesPerSegment + 1 <= kMergeChunk, "a segment's pieces fit the merge's LDS");
 constexpr int kMergeThreads = 256;
 
@@ -1105,7 +1105,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     return s1 > s0 || (s1 == s0 && p1 >= 0 && (p0 < 0 || p1 < p0));
   };
   // the coordinates of this thread's first KPF records, requested before the
-  // headers are reduced (they do not depend on them)
+  // headers are reduced (they do not depend on them); deeper prefetching
+  // costs registers, and below 64 per lane a one-round grid of 2,048
+  // workgroups (64 sequences x 32 heads) still fits the chip
   constexpr int KPF = 4;
   const float4 *col = reinterpret_cast<const float4 *>(recs + kRecHeader) + c;
   const size_t stride4 = stride / 4;
