@@ -374,9 +374,10 @@ __device__ void plan_work(const DecodeArgs &a) {
 // D/32 consecutive coordinates from l D/32 (the SO(4) blocks stay inside a
 // lane), the WHT runs its in-lane butterflies and then five lane-exchange
 // stages, lower index first at every stage as in the Sylvester order.  One
-// barrier, for the scale below.
-template <int D, int ROPE, int G>
-__device__ void rotate_queries(const DecodeArgs &a, int r) {
+// barrier, for the scale below.  `between` runs once the query and parameter
+// loads are issued (the plan, where every workgroup computes it).
+template <int D, int ROPE, int G, class Between>
+__device__ void rotate_queries(const DecodeArgs &a, int r, Between &&between) {
   static_assert(kPrepThreads == 256 && G <= 8, "four waves, two heads each");
   constexpr int DQ = D + ROPE;
   constexpr int E = D / 32;                  // content coordinates per lane
@@ -418,6 +419,7 @@ __device__ void rotate_queries(const DecodeArgs &a, int r) {
       }
     }
   }
+  between();                                 // other work while the loads are in flight
 #pragma unroll
   for (int st = 1; st < E; st <<= 1)
 #pragma unroll
@@ -551,12 +553,11 @@ __host__ __device__ inline bool plan_in_every_group(int batch, int hkv) { return
 template <int D, int ROPE, int G>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(DecodeArgs a) {
   if (plan_in_every_group(a.batch, a.hkv)) {
-    plan_small(a, (int)blockIdx.x, (int)gridDim.x);
-    rotate_queries<D, ROPE, G>(a, (int)blockIdx.x);
+    rotate_queries<D, ROPE, G>(a, (int)blockIdx.x, [&] { plan_small(a, (int)blockIdx.x, (int)gridDim.x); });
   } else if (blockIdx.x == 0) {
     plan_work(a);
   } else {
-    rotate_queries<D, ROPE, G>(a, (int)blockIdx.x - 1);
+    rotate_queries<D, ROPE, G>(a, (int)blockIdx.x - 1, [] {});
   }
 }
 
