@@ -26,15 +26,24 @@ def test_lloyd_max_matches_max_1960(golden, bits):
     c = O.lloyd_max_gaussian(bits)
     n = 1 << bits
     positive = c[n // 2:]
-    table = np.array(g["levels"][str(bits)])
-    # the table prints 4 significant digits
-    assert np.max(np.abs(positive - table) / np.maximum(1.0, table)) < 6e-4
+    table = g["levels"][str(bits)]
+    # each printed value is accurate to a unit in its fourth significant digit
+    for got, printed in zip(positive, table):
+        assert abs(got - printed) <= fourth_digit_unit(printed), (bits, got, printed)
     # symmetric and strictly ascending
     assert np.max(np.abs(c + c[::-1])) < 1e-14
     assert np.all(np.diff(c) > 0)
     if bits == 3:
         t = O.thresholds(c)[n // 2 - 1:]
-        assert np.max(np.abs(t - np.array(g["thresholds"]["3"]))) < 6e-4
+        for got, printed in zip(t, g["thresholds"]["3"]):
+            assert abs(got - printed) <= fourth_digit_unit(printed), (got, printed)
+
+
+def fourth_digit_unit(printed):
+    """One unit in the fourth significant digit of a value of the table (the
+    table's printed precision); the threshold 0 is printed as 0.0000."""
+    mag = max(abs(float(printed)), 0.1)
+    return 10.0 ** (np.floor(np.log10(mag)) - 3)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
