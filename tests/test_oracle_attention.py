@@ -104,6 +104,29 @@ def test_brute_force_tiny(variant, T):
         assert arg[h] == scores.index(m)
 
 
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_attend_dense_brute_force(T):
+    """The fidelity reference (unquantised attention) against scalar loops:
+    softmax of scale * q.k over the tokens, written out term by term, then
+    the weighted sum of the values; plus its closed cases (one token gives its
+    value, equal keys give the mean of the values)."""
+    rng = np.random.default_rng(90 + T)
+    d = 4
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d))
+    scale = 0.7
+    s = [scale * sum(q[i] * k[t][i] for i in range(d)) for t in range(T)]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    z = sum(w)
+    want = [sum(w[t] * v[t][i] for t in range(T)) / z for i in range(d)]
+    np.testing.assert_allclose(O.attend_dense(q, k, v, scale), want, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(O.attend_dense(q, k[:1], v[:1], scale), v[0], rtol=0, atol=1e-15)
+    same = np.repeat(k[:1], T, axis=0)
+    np.testing.assert_allclose(O.attend_dense(q, same, v, scale), v.mean(axis=0), rtol=0, atol=1e-13)
+
+
 def test_single_token_returns_its_value():
     c = make_case(1, 1, 8, 2, 128, 3, O.FULL)
     out, lse, arg = run(c)
