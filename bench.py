@@ -82,10 +82,17 @@ def row_bytes(d, bits):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments and blank space are left
+    out, so that a comment edit keeps the recorded counter readings."""
+    import re
+
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

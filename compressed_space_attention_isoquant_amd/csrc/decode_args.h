@@ -11,9 +11,11 @@ namespace iq {
 
 // Decode attention runs in three launches:
 //
-// prep    one workgroup plans the work (below); the others rotate the
-//         queries once per (sequence, KV head): q~ = R q, scaled, split into
-//         fp16 hi + lo parts (the score product's operand), in the workspace.
+// prep    one workgroup per (sequence, KV head) rotates its queries: q~ =
+//         R q, scaled, split into fp16 hi + lo parts (the score product's
+//         operand), in the workspace; the work plan (below) is computed by
+//         every one of them for up to 256 (sequence, KV head) pairs, each
+//         writing its share of it, else by one extra workgroup.
 // partial every wave streams its own equal share of the 32-token tiles of all
 //         (sequence, KV head) segments laid end to end (tiles of sequence b,
 //         KV head 0 first, then KV head 1, ..., then sequence b + 1), so that
