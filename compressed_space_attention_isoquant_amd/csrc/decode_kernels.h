@@ -594,6 +594,15 @@ void partial_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // lane exchanges at distances 16 and 32 without the lane index in the loop:
+  // a swizzle inside each half-wave, and a permute with a fixed address
+  const int xaddr32 = (lane ^ 32) << 2;
+  auto xor16 = [](auto v) {
+    return __builtin_bit_cast(decltype(v), __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  };
+  auto xor32 = [&](auto v) {
+    return __builtin_bit_cast(decltype(v), __builtin_amdgcn_ds_bpermute(xaddr32, __builtin_bit_cast(int, v)));
+  };
 
   // the code-pair table, aligned to its own size so that an entry's offset
   // can be OR-ed into the lane's replica address
@@ -727,11 +736,12 @@ void partial_kernel(DecodeArgs a) {
     return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(addr);
   };
 
-  float Mh, Mb, Lh, best_s;
+  float Mh, Mthr, Mb, Lh, best_s;           // Mthr = Mh + tau_s, the lazy rescale threshold
   int best_j;
   floatx4 O[NB];
   auto reset = [&] {
     Mh = -INFINITY;
+    Mthr = -INFINITY;
     Mb = -INFINITY;
     Lh = 0.f;
     best_s = -INFINITY;
@@ -902,20 +912,22 @@ void partial_kernel(DecodeArgs a) {
       }
     }
     const float lmax = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-    if (__any(lmax > Mh + tau_s)) {
+    if (__any(lmax > Mthr)) {
       float umax = fmaxf(lmax, xor_g<G>(lmax));
-      umax = fmaxf(umax, __shfl_xor(umax, 16, 64));
-      umax = fmaxf(umax, __shfl_xor(umax, 32, 64));
+      umax = fmaxf(umax, xor16(umax));
+      umax = fmaxf(umax, xor32(umax));
       const float mnew = fmaxf(Mh, umax);
       const float alpha = (Mh == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Mh - mnew) * qsc);
       Lh *= alpha;
       Mh = mnew;
+      Mthr = mnew + tau_s;
       Mb = mnew * qsc - kWeightBias;
       // rows 4*g4 + i of the value accumulators belong to head (4*g4 + i) % G
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * g4 + i;
-        const float ar = __shfl(alpha, row < NROW ? row % G : 0, 64);
+        const float ar = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute((row < NROW ? row % G : 0) << 2, __builtin_bit_cast(int, alpha)));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) O[nb][i] *= ar;
       }
@@ -925,7 +937,7 @@ void partial_kernel(DecodeArgs a) {
     for (int r = 0; r < 4; ++r) {
       const float x = __builtin_amdgcn_exp2f(fmaf(sig[r], qsc, -Mb));   // 2^(s - M + bias); 0 for masked tokens
       Lh += x;
-      y[r] = live ? x * half_bits_to_float(vb[r]) : 0.f;
+      y[r] = live ? fmaf(x, half_bits_to_float(vb[r]), 0.f) : 0.f;   // x ||v||, one mixed-precision FMA
     }
     // A operand, k order = tile-0 tokens 4*g4..+3 then tile-1 tokens; hi lanes
     // carry fp16(y) (round toward zero), lo lanes the exact remainder.
@@ -965,8 +977,8 @@ void partial_kernel(DecodeArgs a) {
   auto write_record = [&](const Cursor &c) {
     float lsum = live ? Lh : 0.f;
     lsum += xor_g<G>(lsum);
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    lsum += xor16(lsum);
+    lsum += xor32(lsum);
     float bs = live ? best_s : -INFINITY;
     int bj = live ? best_j : -1;
     if constexpr (ARGMAX) {
@@ -978,8 +990,8 @@ void partial_kernel(DecodeArgs a) {
         }
       };
       take(xor_g<G>(bs), __builtin_bit_cast(int, xor_g<G>(__builtin_bit_cast(float, bj))));
-      take(__shfl_xor(bs, 16, 64), __shfl_xor(bj, 16, 64));
-      take(__shfl_xor(bs, 32, 64), __shfl_xor(bj, 32, 64));
+      take(xor16(bs), xor16(bj));
+      take(xor32(bs), xor32(bj));
     }
     const long long piece = (long long)c.b * a.hkv + c.h + w;
     float *rec = a.ws + piece * G * (D + kRecHeader);
@@ -1000,8 +1012,10 @@ void partial_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float v = O[4 * q + k][i];
-          if constexpr (G >= 4)
-            v4[k] = v + __shfl_xor(v, 16 * (G / 4), 64);
+          if constexpr (G == 4)
+            v4[k] = v + xor16(v);
+          else if constexpr (G == 8)
+            v4[k] = v + xor32(v);
           else
             v4[k] = v + O[4 * q + k][i ^ G];
         }
