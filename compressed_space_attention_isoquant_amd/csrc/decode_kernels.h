@@ -596,12 +596,16 @@ void partial_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // lane exchanges at distances 16 and 32 without the lane index in the loop:
   // a swizzle inside each half-wave, and a permute with a fixed address
+  // (head_dim 128 keeps the permute address in a register; at 256 and 512,
+  // where every register is taken, it is recomputed)
+  constexpr bool kSpare = D <= 128;          // registers to spare for such conveniences
   const int xaddr32 = (lane ^ 32) << 2;
   auto xor16 = [](auto v) {
     return __builtin_bit_cast(decltype(v), __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
   };
   auto xor32 = [&](auto v) {
-    return __builtin_bit_cast(decltype(v), __builtin_amdgcn_ds_bpermute(xaddr32, __builtin_bit_cast(int, v)));
+    const int addr = kSpare ? xaddr32 : (((int)threadIdx.x & 63) ^ 32) << 2;
+    return __builtin_bit_cast(decltype(v), __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, v)));
   };
 
   // the code-pair table, aligned to its own size so that an entry's offset
@@ -912,7 +916,7 @@ void partial_kernel(DecodeArgs a) {
       }
     }
     const float lmax = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-    if (__any(lmax > Mthr)) {
+    if (__any(lmax > (kSpare ? Mthr : Mh + tau_s))) {
       float umax = fmaxf(lmax, xor_g<G>(lmax));
       umax = fmaxf(umax, xor16(umax));
       umax = fmaxf(umax, xor32(umax));
