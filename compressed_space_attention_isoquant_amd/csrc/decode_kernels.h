@@ -3,10 +3,12 @@
 // (v_mfma_f32_16x16x32_f16) directly from the packed codes, the work of a
 // call spread evenly over the waves of one resident round.
 //
-// prep kernel: workgroup 0 plans the work (DecodePlan, decode_args.h); each
-//   other workgroup rotates the G query heads of one (sequence, KV head):
-//   q~ = R q (WHT butterflies and SO(4) blocks in LDS), scaled, split into
-//   fp16 hi + lo parts, stored as 2G rows (hi rows, then lo rows).
+// prep kernel: plans the work (DecodePlan, decode_args.h) and rotates the G
+//   query heads of each (sequence, KV head): q~ = R q (WHT butterflies in
+//   registers and across lanes, then the SO(4) blocks), scaled by a power of
+//   two, split into fp16 hi + lo parts, stored as 2G rows (hi rows, then lo
+//   rows).  Up to 256 segments every workgroup computes the plan and writes
+//   its share of it beside its rotation; beyond that workgroup 0 plans alone.
 // partial kernel: every wave owns W consecutive tiles of 32 tokens of the
 //   (sequence, KV head) segments laid end to end; waves never synchronise.
 //   Per tile:
@@ -17,7 +19,8 @@
 //             of exact fp16 centroid pairs (each level times 2^e is an fp16
 //             number) replicated in LDS.
 //     softmax online, base 2, with a lazily raised running maximum (only
-//             rescaled when a score exceeds it by more than kLazyTau).
+//             rescaled when a score plus a bound of its value norm's exponent
+//             exceeds it by more than kLazyTau).
 //     values  O~ (16 rows x d) += P (16 x 32 tokens) . C_V (32 x d); row j < G
 //             carries the fp16 hi part of p * ||v|| for head j, row G + j the
 //             lo part, so the fp32 accumulators see the weights to ~2^-22.
