@@ -70,14 +70,16 @@ template <int G>
 __device__ __forceinline__ float xor_g(float v) {
   const int x = __builtin_bit_cast(int, v);
   int r;
+  // (bound_ctrl set: every source lane of these patterns exists, and the
+  // compiler can then fold the move into the instruction that uses it)
   if constexpr (G == 8)
-    r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);      // row_ror:8 == lane ^ 8
+    r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);       // row_ror:8 == lane ^ 8
   else if constexpr (G == 4)
     r = __builtin_amdgcn_ds_swizzle(x, (4 << 10) | 0x1F);          // lane ^ 4
   else if constexpr (G == 2)
-    r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);       // quad_perm [2,3,0,1]
+    r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);        // quad_perm [2,3,0,1]
   else
-    r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);       // quad_perm [1,0,3,2]
+    r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);        // quad_perm [1,0,3,2]
   return __builtin_bit_cast(float, r);
 }
 
@@ -211,10 +213,14 @@ __device__ __forceinline__ void load_stage(uint32_t stage_lds, int32x4_t kr, int
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
+// Issued through the builtin, not inline asm, so that the compiler sees the
+// wait: its own loads before a vmcnt(0) count as done, and it inserts no
+// wait of its own for them later (a compiler-inserted vmcnt(0) in the tile
+// loop would also wait for every stage in flight).
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));   // expcnt, lgkmcnt at max
 }
 
 // The code-pair table lives in LDS, replicated so that a wave's reads fall
@@ -723,12 +729,21 @@ void partial_kernel(DecodeArgs a) {
 
   const int my_tile = lo_lane ? 1 : 0;
   const int vbit = VCB * j;                  // bit offset of this lane's codes in a row
-  const float lo_mask = lo_lane ? 1.f : 0.f;
+  // -1 held in a register rather than as a literal, so that a weight's
+  // remainder below stays one mixed-precision FMA (n_waves < 2^30)
+  const float neg1 = -1.f - static_cast<float>(a.n_waves >> 30);
+  constexpr int LSH = ilog2<REPL * 4>();     // table entry -> byte offset shift
+  // A lane's value codes are taken VS bits early, so that in the interleaved
+  // words below the first pair field already sits at the table shift (where
+  // a group of 8 codes still fits a dword after it and no more dwords are
+  // needed); the VS bits under it belong to the previous codes and are never
+  // read.
+  constexpr int VS = (LSH + 8 * BITS <= 32 && (VCB + LSH + 31) / 32 == VX) ? LSH : 0;
+  const int vbs = vbit - VS;                 // lane 0: -VS, the dword before the row (still in LDS)
   // per-lane LDS byte offsets inside a stage
   const int k_off = S::K_OFF + j * S::RS + g4 * UDW * 4;
-  const int v_off = S::V_OFF + 4 * g4 * S::RS + (vbit >> 5) * 4;
+  const int v_off = S::V_OFF + 4 * g4 * S::RS + (vbs >> 5) * 4;
   const int n_off = (16 * my_tile + 4 * g4) * 2;
-  constexpr int LSH = ilog2<REPL * 4>();     // table entry -> byte offset shift
   // byte address of this lane's replica of table entry 0
   const uint32_t lut_base = lds_addr(lut) | (uint32_t)(lane % REPL) * 4u;
   // table entry at the 2*BITS-bit field at bit `pos` of w: the field is
@@ -797,7 +812,7 @@ void partial_kernel(DecodeArgs a) {
       for (int i = 0; i < VW; ++i)                           // may read one dword past the row: still in LDS
         w[i] = lds_ld<uint32_t>(vbase + (16 * (r >> 2) + (r & 3)) * S::RS + 4 * i);
 #pragma unroll
-      for (int i = 0; i < VX; ++i) vch[r][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], vbit & 31);
+      for (int i = 0; i < VX; ++i) vch[r][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], vbs & 31);
     }
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
     const uint32_t nbase = cur + n_off;
@@ -838,14 +853,14 @@ void partial_kernel(DecodeArgs a) {
     {
       constexpr int NGRP = NB / 8;
       constexpr uint32_t M = (1u << BITS) - 1u;
-      constexpr uint32_t ME = M | (M << (2 * BITS)) | (M << (4 * BITS)) | (M << (6 * BITS));
+      constexpr uint32_t ME = (M | (M << (2 * BITS)) | (M << (4 * BITS)) | (M << (6 * BITS))) << VS;
       uint32_t X[NGRP][4][2];
       static_for<NGRP>([&](auto gi) {
         constexpr int bit0 = decltype(gi)::value * 8 * BITS, wd = bit0 >> 5, off = bit0 & 31;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           uint32_t ca, cb;
-          if constexpr (off + 8 * BITS <= 32) {
+          if constexpr (off + 8 * BITS + VS <= 32) {
             ca = vch[2 * p][wd] >> off;
             cb = vch[2 * p + 1][wd] >> off;
           } else {
@@ -854,14 +869,14 @@ void partial_kernel(DecodeArgs a) {
           }
           // bit-field inserts (one v_bfi_b32 each): the fields of ca under
           // ME, those of cb shifted into the gaps; only the group's 8 * BITS
-          // low bits are read afterwards
+          // bits from bit VS are read afterwards
           X[gi][p][0] = (ca & ME) | ((cb << BITS) & ~ME);
           X[gi][p][1] = ((ca >> BITS) & ME) | (cb & ~ME);
         }
       });
       static_for<NB>([&](auto nb) {
         constexpr int nbv = decltype(nb)::value;
-        constexpr int sh = ((nbv % 8) >> 1) * 2 * BITS;
+        constexpr int sh = ((nbv % 8) >> 1) * 2 * BITS + VS;
 #pragma unroll
         for (int p = 0; p < 4; ++p) vbw[nb][p] = pair(X[nbv / 8][p][nbv & 1], std::integral_constant<int, sh>{});
       });
@@ -946,28 +961,23 @@ void partial_kernel(DecodeArgs a) {
       Lh += x;
       y[r] = live ? fmaf(x, half_bits_to_float(vb[r]), 0.f) : 0.f;   // x ||v||, one mixed-precision FMA
     }
-    // A operand, k order = tile-0 tokens 4*g4..+3 then tile-1 tokens; hi lanes
-    // carry fp16(y) (round toward zero), lo lanes the exact remainder.
+    // A operand, k order = tile-0 tokens 4*g4..+3 then tile-1 tokens; row j
+    // < G carries the fp16 hi parts (round toward zero) of head j's weights,
+    // row G + j the exact remainders.  Each lane splits its own tile's two
+    // weight pairs once and hands its partner (lane ^ G, which owns the other
+    // tile) the part the partner's row carries.
     uint32_t pw[4];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
-      float pa[2], pb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = 2 * q2 + t;
-        const float other = xor_g<G>(y[r]);
-        pa[t] = my_tile ? other : y[r];      // tile 0 token 4*g4 + r
-        pb[t] = my_tile ? y[r] : other;      // tile 1 token 4*g4 + r
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const float e0 = half ? pb[0] : pa[0];
-        const float e1 = half ? pb[1] : pa[1];
-        const auto h = __builtin_amdgcn_cvt_pkrtz(e0, e1);
-        const float d0 = fmaf(-lo_mask, static_cast<float>(h[0]), e0);
-        const float d1 = fmaf(-lo_mask, static_cast<float>(h[1]), e1);
-        pw[2 * half + q2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(d0, d1));
-      }
+      const auto h = __builtin_amdgcn_cvt_pkrtz(y[2 * q2], y[2 * q2 + 1]);
+      const float d0 = fmaf(neg1, static_cast<float>(h[0]), y[2 * q2]);
+      const float d1 = fmaf(neg1, static_cast<float>(h[1]), y[2 * q2 + 1]);
+      const uint32_t hw = __builtin_bit_cast(uint32_t, h);
+      const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(d0, d1));
+      const uint32_t got =
+          __builtin_bit_cast(uint32_t, xor_g<G>(__builtin_bit_cast(float, lo_lane ? hw : lw)));
+      pw[q2] = lo_lane ? got : hw;         // tile 0: a hi lane's own, a lo lane's from its partner
+      pw[2 + q2] = lo_lane ? lw : got;     // tile 1: a lo lane's own, a hi lane's from its partner
     }
     const half8 P = as_half8(pw[0], pw[1], pw[2], pw[3]);
 
@@ -1040,7 +1050,6 @@ void partial_kernel(DecodeArgs a) {
   // flight is awaited.
   Cursor cp = c0, ca = c0;                   // tile processed, tile loaded next
   int ta = t_begin;
-  load_query(cp);
   reset();
   resources(ca);
 #pragma unroll
@@ -1049,6 +1058,10 @@ void partial_kernel(DecodeArgs a) {
     if (ta + 1 < t_end) advance_loads(ca);
     ++ta;
   }
+  // the first query rows, then one wait that the compiler sees (it also
+  // lands the first stages, which the first tile needs anyway)
+  load_query(cp);
+  wait_vmem<0>();
   int slot = 0;                              // stage of tile tp
   for (int tp = t_begin; tp < t_end; ++tp) {
     const int aslot = slot == 0 ? NST - 1 : slot - 1;       // (tp + NST - 1) mod NST, processed last iteration
