@@ -216,11 +216,14 @@ __device__ __forceinline__ void load_stage(uint32_t stage_lds, int32x4_t kr, int
 // Issued through the builtin, not inline asm, so that the compiler sees the
 // wait: its own loads before a vmcnt(0) count as done, and it inserts no
 // wait of its own for them later (a compiler-inserted vmcnt(0) in the tile
-// loop would also wait for every stage in flight).
+// loop would also wait for every stage in flight).  The builtin touches no
+// memory as far as the compiler knows, so an empty asm with a memory clobber
+// follows it: no LDS read of a stage may be scheduled above the wait.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));   // expcnt, lgkmcnt at max
+  asm volatile("" ::: "memory");
 }
 
 // The code-pair table lives in LDS, replicated so that a wave's reads fall
