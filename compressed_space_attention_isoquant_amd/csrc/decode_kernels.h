@@ -1136,7 +1136,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   __shared__ float reds[NW];
   __shared__ float hm[kMergeChunk], hl[kMergeChunk];      // each piece's M and L
   __shared__ __attribute__((aligned(16))) float part_o[NP][D];
-  __shared__ float y[D];
+  __shared__ __attribute__((aligned(16))) float y[D];
   const int lane = tid & 63, wave = tid >> 6;
   // (score, position) pairs: the larger score, ties to the lower valid position
   auto better = [](float s1, int p1, float s0, int p0) {
@@ -1236,38 +1236,50 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     y[i] = L > 0.f ? sum * a.oscale / L : 0.f;
   }
   __syncthreads();
-  if (tid < D / 4) {
-    const float *pg = a.quats + (size_t)g * (D / 4) * block_param_floats(VARIANT);
-    float4 u = block_inv<VARIANT>(make_float4(y[4 * tid], y[4 * tid + 1], y[4 * tid + 2], y[4 * tid + 3]), pg, tid);
-    y[4 * tid] = u.x;
-    y[4 * tid + 1] = u.y;
-    y[4 * tid + 2] = u.z;
-    y[4 * tid + 3] = u.w;
-  }
-  __syncthreads();
-  static_assert(D / 2 <= NT, "one butterfly per thread");
-  for (int st = 1; st < D; st <<= 1) {
-    float x0 = 0.f, x1 = 0.f;
-    int lo = 0;
-    if (tid < D / 2) {
-      lo = (tid / st) * 2 * st + (tid % st);
-      x0 = y[lo];
-      x1 = y[lo + st];
-    }
-    __syncthreads();
-    if (tid < D / 2) {
-      y[lo] = x0 + x1;
-      y[lo + st] = x0 - x1;
-    }
-    __syncthreads();
-  }
+  // R^T in one half-wave, in registers: lane l holds the D/32 consecutive
+  // coordinates from l D/32 (whole inverse blocks), then the WHT's in-lane
+  // butterflies and five lane-exchange stages, lower index first at every
+  // stage as in the Sylvester order; no barrier.
   const size_t oh = (size_t)b * a.hq + h;
-  for (int i = tid; i < D; i += NT) {
-    const float val = y[i] / sqrtf((float)D);
-    if (a.out_f16)
-      static_cast<_Float16 *>(a.out)[oh * D + i] = static_cast<_Float16>(val);
-    else
-      static_cast<float *>(a.out)[oh * D + i] = val;
+  if (tid < 32) {
+    constexpr int E = D / 32;
+    const float *pg = a.quats + (size_t)g * (D / 4) * block_param_floats(VARIANT);
+    float x[E];
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) {
+      const float4 u = block_inv<VARIANT>(*reinterpret_cast<const float4 *>(&y[tid * E + 4 * k]), pg,
+                                          tid * (E / 4) + k);
+      x[4 * k] = u.x;
+      x[4 * k + 1] = u.y;
+      x[4 * k + 2] = u.z;
+      x[4 * k + 3] = u.w;
+    }
+#pragma unroll
+    for (int st = 1; st < E; st <<= 1)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (!(e & st)) {
+          const float x0 = x[e], x1 = x[e + st];
+          x[e] = x0 + x1;
+          x[e + st] = x0 - x1;
+        }
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+      const bool upper = tid & m;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float v = __shfl_xor(x[e], m, 64);
+        x[e] = upper ? v - x[e] : x[e] + v;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float val = x[e] / sqrtf((float)D);
+      if (a.out_f16)
+        static_cast<_Float16 *>(a.out)[oh * D + tid * E + e] = static_cast<_Float16>(val);
+      else
+        static_cast<float *>(a.out)[oh * D + tid * E + e] = val;
+    }
   }
   if (tid == 0) {
     if (a.lse) a.lse[oh] = L > 0.f ? (M - kWeightBias + log2f(L)) * 0.69314718055994531f : -INFINITY;
