@@ -247,10 +247,14 @@ constexpr int ilog2() {
 }
 
 // LDS layout: workgroups per CU (each holds one wave per SIMD) and stages
-// per wave.  Three workgroups per CU where each can keep 3 stages per wave
-// (more waves hide latency better than a deeper ring), else two where each
-// keeps 2 stages, else one; then as many stages as fit, up to 4, at least 2
-// (double buffering).
+// per wave.  Four workgroups per CU at head_dim 128 without RoPE rows where
+// each keeps 2 stages per wave next to its table (these kernels fit 128
+// registers once the value operand is built after the softmax, and the
+// fourth wave per SIMD fills VALU issue slots the other three leave: 6%
+// faster than three waves with 3 stages); else three where each can keep 3
+// stages per wave (more waves hide latency better than a deeper ring), else
+// two where each keeps 2 stages, else one; then as many stages as fit, up
+// to 4, at least 2 (double buffering).
 template <int D, int BITS, int ROPE = 0>
 constexpr int stages_fitting(int budget) {
   return (budget - lds_table_bytes<BITS>()) / (kDecodeWaves * Stage<D, BITS, ROPE>::BYTES);
@@ -258,7 +262,8 @@ constexpr int stages_fitting(int budget) {
 
 template <int D, int BITS, int ROPE = 0>
 constexpr int resident_groups() {
-  return stages_fitting<D, BITS, ROPE>(160 * 1024 / 3) >= 3   ? 3
+  return (D == 128 && ROPE == 0 && stages_fitting<D, BITS, ROPE>(160 * 1024 / 4) >= 2) ? 4
+         : stages_fitting<D, BITS, ROPE>(160 * 1024 / 3) >= 3                           ? 3
          : stages_fitting<D, BITS, ROPE>(160 * 1024 / 2) >= 2 ? 2
                                                                : 1;
 }
@@ -270,13 +275,14 @@ constexpr int stage_count() {
 }
 
 // Waves per SIMD the register allocation is held to, matching the LDS
-// layout: three where three workgroups share a CU (at most 168 registers per
-// lane), two where the LDS of two fits (head_dim <= 256; 256 registers),
-// else no constraint.
+// layout: four or three where that many workgroups share a CU (at most 128
+// or 168 registers per lane), two where the LDS of two fits (head_dim <=
+// 256; 256 registers), else no constraint.
 template <int D, int BITS, int ROPE = 0>
 constexpr int partial_waves() {
   const int lds = lds_table_bytes<BITS>() + kDecodeWaves * stage_count<D, BITS, ROPE>() * Stage<D, BITS, ROPE>::BYTES;
-  return resident_groups<D, BITS, ROPE>() == 3 ? 3 : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
+  return resident_groups<D, BITS, ROPE>() >= 3 ? resident_groups<D, BITS, ROPE>()
+                                               : ((D <= 256 && lds <= 80 * 1024) ? 2 : 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -603,6 +609,7 @@ void partial_kernel(DecodeArgs a) {
   static_assert((NST - 1) * S::LOADS < 64, "in-flight loads exceed the vmcnt range");
   constexpr int REPL = lut_repl<BITS>();
   constexpr int TB = lds_table_bytes<BITS>();
+  constexpr bool kLateV = resident_groups<D, BITS, ROPE>() == 4;   // value operand after the softmax
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -805,25 +812,11 @@ void partial_kernel(DecodeArgs a) {
         for (int t = 0; t < UDW; ++t)
           kw[tile][m * UDW + t] = lds_ld<uint32_t>(kbase + tile * 16 * S::RS + (4 * m * UDW + t) * 4);
     }
-    // the 8 tokens of this lane in the operand/result layouts: 4*g4 + r of each tile
-    const uint32_t vbase = cur + v_off;
-    uint32_t vch[8][VX];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      uint32_t w[VW];
-#pragma unroll
-      for (int i = 0; i < VW; ++i)                           // may read one dword past the row: still in LDS
-        w[i] = lds_ld<uint32_t>(vbase + (16 * (r >> 2) + (r & 3)) * S::RS + 4 * i);
-#pragma unroll
-      for (int i = 0; i < VX; ++i) vch[r][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], vbs & 31);
-    }
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
     const uint32_t nbase = cur + n_off;
     const u16x4 kb = lds_ld<u16x4>(nbase + S::KN_OFF);
     const u16x4 vb = lds_ld<u16x4>(nbase + S::VN_OFF);
 
-    // Table reads for both operands are issued up front, so that their
-    // latency overlaps the score products and the softmax.
     // K operand: lane (token j, dims slice g4), k-step s holds dims 8s..8s+7
     // of the slice as 4 code pairs.
     uint32_t ka[2][KS][4];
@@ -847,12 +840,30 @@ void partial_kernel(DecodeArgs a) {
         });
       });
     }
+    // The value operand (the lane's value codes from the stage, their pair
+    // interleave and table reads): built here, so that its table reads
+    // overlap the score products and the softmax, or, in the four-wave
+    // layout, after the softmax, where its registers are free again (the
+    // other waves of the SIMD cover the reads' latency).
+    uint32_t vbw[NB][4];
+    auto build_v = [&] {
+    // the 8 tokens of this lane in the operand/result layouts: 4*g4 + r of each tile
+    const uint32_t vbase = cur + v_off;
+    uint32_t vch[8][VX];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      uint32_t w[VW];
+#pragma unroll
+      for (int i = 0; i < VW; ++i)                           // may read one dword past the row: still in LDS
+        w[i] = lds_ld<uint32_t>(vbase + (16 * (r >> 2) + (r & 3)) * S::RS + 4 * i);
+#pragma unroll
+      for (int i = 0; i < VX; ++i) vch[r][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], vbs & 31);
+    }
     // V operand: column block nb holds dims (D/16) * n + nb of lane column
     // n = j; dword p is the pair of tokens (2p, 2p+1) of the lane's 8
     // (code_a | code_b << BITS).  Per group of 8 column blocks the two tokens'
     // fields are interleaved first (SWAR): X[g][p][parity] holds the pair
     // indices of the group's dims of that parity at 2*BITS-bit strides.
-    uint32_t vbw[NB][4];
     {
       constexpr int NGRP = NB / 8;
       constexpr uint32_t M = (1u << BITS) - 1u;
@@ -884,6 +895,9 @@ void partial_kernel(DecodeArgs a) {
         for (int p = 0; p < 4; ++p) vbw[nb][p] = pair(X[nbv / 8][p][nbv & 1], std::integral_constant<int, sh>{});
       });
     }
+
+    };
+    if constexpr (!kLateV) build_v();
 
     // scores for both tiles
     floatx4 S2[2];
@@ -983,6 +997,10 @@ void partial_kernel(DecodeArgs a) {
       pw[2 + q2] = lo_lane ? lw : got;     // tile 1: a lo lane's own, a hi lane's from its partner
     }
     const half8 P = as_half8(pw[0], pw[1], pw[2], pw[3]);
+    if constexpr (kLateV) {
+      __builtin_amdgcn_sched_barrier(0);     // nothing of the value operand moves above this point
+      build_v();
+    }
 
     // values
 #pragma unroll
