@@ -843,8 +843,8 @@ void partial_kernel(DecodeArgs a) {
     // The value operand (the lane's value codes from the stage, their pair
     // interleave and table reads): built here, so that its table reads
     // overlap the score products and the softmax, or, in the four-wave
-    // layout, after the softmax, where its registers are free again (the
-    // other waves of the SIMD cover the reads' latency).
+    // layout, after the softmax, in the registers the key operand has freed
+    // (the other three waves of the SIMD cover the reads' latency).
     uint32_t vbw[NB][4];
     auto build_v = [&] {
     // the 8 tokens of this lane in the operand/result layouts: 4*g4 + r of each tile
