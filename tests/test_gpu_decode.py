@@ -206,6 +206,36 @@ def test_decode_fp32_io_sweep(d, bits, variant, group):
     assert np.all(arg[1] == 0)
 
 
+# head_dim 128 at 2 and 3 bits runs four workgroups per CU, with the value
+# operand built after the softmax: every group size of that layout
+FOUR_WAVE = [(bits, group, (O.FULL, O.FAST, O.PLANAR)[(bits + group) % 3]) for bits in (2, 3) for group in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("bits,group,variant", FOUR_WAVE)
+def test_decode_four_wave_layout(bits, group, variant):
+    """The four-workgroup kernels (head_dim 128, 2 and 3 bits) at every group
+    size: fp32 queries and outputs at max-abs 1e-5 with the oracle's argmax,
+    on a ragged batch whose longest sequence is cut into many wave shares
+    (an empty sequence, one token, 651 and 3000 tokens)."""
+    d, hkv = 128, 2
+    hq = group * hkv
+    rng = np.random.default_rng(2000 + 10 * bits + group)
+    cap, lens = 3000, [0, 1, 651, 3000]
+    batch = len(lens)
+    cfg, quats = make_config(d, bits, variant, hkv)
+    k = (rng.standard_normal((batch, cap, hkv, d)) * 2).astype(np.float16)
+    v = (rng.standard_normal((batch, cap, hkv, d)) * 2).astype(np.float16)
+    q = rng.standard_normal((batch, hq, d)).astype(np.float32)
+    kc = quantize_rows(cfg, k)
+    vc = quantize_rows(cfg, v)
+    got, lse, arg = run_decode(cfg, q, kc, vc, lens, max(lens), q_f16=False)
+    ref, rlse, rarg = oracle_decode(q, k, v, quats, cfg, lens, host_cache(kc), host_cache(vc))
+    check_outputs(f"four-wave d=128 b={bits} G={group} v={variant}", got, lse, arg, ref, rlse, rarg, 1e-5,
+                  check_arg=True)
+    assert np.all(got[0] == 0) and np.all(arg[0] == -1)
+    assert np.all(arg[1] == 0)
+
+
 def test_argmax_ties_lowest_position():
     """Exact score ties (identical K rows) resolve to the lowest position
     wherever the tied tokens meet in the kernel: in one tile on the two halves
