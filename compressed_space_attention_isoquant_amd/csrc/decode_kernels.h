@@ -881,11 +881,13 @@ void partial_kernel(DecodeArgs a) {
             ca = __builtin_amdgcn_alignbit(vch[2 * p][wd + 1], vch[2 * p][wd], off);
             cb = __builtin_amdgcn_alignbit(vch[2 * p + 1][wd + 1], vch[2 * p + 1][wd], off);
           }
-          // bit-field inserts (one v_bfi_b32 each): the fields of ca under
-          // ME, those of cb shifted into the gaps; only the group's 8 * BITS
-          // bits from bit VS are read afterwards
-          X[gi][p][0] = (ca & ME) | ((cb << BITS) & ~ME);
-          X[gi][p][1] = ((ca >> BITS) & ME) | (cb & ~ME);
+          // bitwise selects (one v_bitop3_b32 each, truth table 0xCA = S0 ?
+          // S1 : S2): the fields of ca under ME, those of cb shifted into
+          // the gaps; only the group's 8 * BITS bits from bit VS are read
+          // afterwards.  (Written as and/or, one of the two comes out as two
+          // instructions once the compiler folds the later table masks.)
+          X[gi][p][0] = __builtin_amdgcn_bitop3_b32(ME, ca, cb << BITS, 0xCA);
+          X[gi][p][1] = __builtin_amdgcn_bitop3_b32(ME, ca >> BITS, cb, 0xCA);
         }
       });
       static_for<NB>([&](auto nb) {
