@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.POINTER(IQCacheC), ctypes.POINTER(IQCacheC), P, i64,
                                                   ctypes.c_float, P, i32, P, P, P]
         L.iq_decode_attention_noalloc.restype = ctypes.c_int
+        L.iq_probe_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+        L.iq_probe_stream_read.restype = ctypes.c_int
         L.iq_status_string.argtypes = [ctypes.c_int]
         L.iq_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -317,3 +319,11 @@ def iq_decode_attention_noalloc(cfg: Config, q, k: PackedCache, v: PackedCache, 
                                              ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_len), int(max_kv_len),
                                              float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse),
                                              _ptr(argmax), _stream(stream)))
+
+
+def iq_probe_stream_read(buf, sink, stream=None) -> None:
+    """Measurement helper (include/iq_probe.h): reads the device tensor
+    ``buf`` (16-byte aligned, size a multiple of 16 bytes) once; ``sink`` is a
+    device tensor of at least 4 bytes."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().iq_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libiq.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "decode_128.hip", "decode_256.hip", "decode_512.hip",
+SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "decode_128.hip", "decode_256.hip", "decode_512.hip", "probe.hip",
            "noalloc.hip"]
 
 # Matrix-core accumulators kept in the unified VGPR file (no AGPR copies around

@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every symbol include/iq.h declares, and
+"""The C-ABI library loads, exports every symbol the headers under include/ declare, and
 validates arguments on the host before anything is enqueued (CPU only: no
 compute is launched here)."""
 
@@ -16,7 +16,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "iq.h")).read()
+    """Every function the headers under include/ declare."""
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(iq_[a-z_]+)\s*\(", text)))
 
@@ -26,7 +28,8 @@ def test_every_declared_symbol_is_exported():
     assert set(names) >= {"iq_quantize_append", "iq_dequantize", "iq_decode_attention",
                           "iq_decode_workspace_bytes", "iq_status_string", "iq_codebook",
                           "iq_decode_attention_partial", "iq_decode_attention_merge",
-                          "iq_quantize_append_rope", "iq_decode_attention_rope", "iq_quantize_append_many"}
+                          "iq_quantize_append_rope", "iq_decode_attention_rope", "iq_quantize_append_many",
+                          "iq_probe_stream_read"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -331,3 +334,15 @@ def test_append_many_validation():
     assert call(base, xs=(0x2000, 0, 0x2200)) == -1
     assert call(base, cap=2) == -1                              # n_new above a capacity
     assert call(base[:2] + [cfg(d=96)]) == -2
+
+
+def test_probe_validation():
+    """The read-bandwidth probe rejects bad arguments on the host, before any
+    GPU call (the pointers below are never dereferenced)."""
+    L = B.lib()
+    S = ctypes.c_size_t
+    assert L.iq_probe_stream_read(None, S(1024), ctypes.c_void_p(4096), None) == -1
+    assert L.iq_probe_stream_read(ctypes.c_void_p(4096), S(1024), None, None) == -1
+    assert L.iq_probe_stream_read(ctypes.c_void_p(4096), S(0), ctypes.c_void_p(4096), None) == -1
+    assert L.iq_probe_stream_read(ctypes.c_void_p(4096), S(1000), ctypes.c_void_p(4096), None) == -1
+    assert L.iq_probe_stream_read(ctypes.c_void_p(4100), S(1024), ctypes.c_void_p(4096), None) == -3
