@@ -11,8 +11,9 @@ query head over the packed caches.  100 steps are timed by default.
 Prints one JSON line: value = packed-KV (+ q, o) bytes the steps' attention
 reads and writes per second of step time (GB/s); the dominant kernel's
 roofline (its algorithmic bytes per launch over its average launch time,
-measured with HIP events on its stream); the FP64 oracle timed on the host as
-a baseline; and, as labelled extras, the batched decode-with-append workload
+measured with HIP events on its stream, also as a fraction of the read rate
+the GPU reaches for a plain stream, measured in the same run); the FP64
+oracle timed on the host as a baseline; and, as labelled extras, the batched decode-with-append workload
 (64 ragged sequences up to 32K, 16/8 heads, d=256, 3-bit Fast) with its own
 roofline and oracle baseline, stage-1 quantize / dequantize rates over the
 whole d x bits x variant x dtype sweep on 2^20 unit vectors (with the
