@@ -248,7 +248,8 @@ constexpr int ilog2() {
 
 // LDS layout: workgroups per CU (each holds one wave per SIMD) and stages
 // per wave.  Four workgroups per CU at head_dim 128 without RoPE rows where
-// each keeps 2 stages per wave next to its table (these kernels fit 128
+// each keeps at least 2 stages per wave next to its table (2 at 3 bits, 3 at
+// 2 bits, whose table is smaller; these kernels fit 128
 // registers once the value operand is built after the softmax, and the
 // fourth wave per SIMD fills VALU issue slots the other three leave: 6%
 // faster than three waves with 3 stages); else three where each can keep 3
